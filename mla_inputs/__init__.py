@@ -1,0 +1,288 @@
+"""Seeded synthetic workloads for MLA absorbed decode.
+
+This module only *makes inputs*: shapes, random draws, storage encodings
+(bf16 round-to-nearest-even, OCP E4M3FN with a per-token scale), the paged
+block pool with its page table, and NaN poison in memory that no output may
+read.  It performs none of the attention arithmetic, so both the CPU oracle
+and the HIP path can use it without sharing any of the method.
+
+Shapes follow the DeepSeek-V2 explainer (deepforge "DeepSeek-V2", section 1,
+"Store a latent, rebuild the keys and values"): per token per layer the cache
+holds a 512-wide latent c_t plus a 64-wide decoupled RoPE key k^R_t; heads are
+128 wide.  The five workloads below are the synthetic configurations the build
+is measured on; their value distributions are stated in each docstring field.
+
+Storage formats (all little-endian, row-major):
+
+* ``f32``  : latent pool  float32 [num_blocks][block][576]  (c | k^R interleaved)
+* ``bf16`` : latent pool  uint16  [num_blocks][block][576]  (bf16 bit patterns)
+* ``fp8``  : c8  uint8 [num_blocks][block][512] (E4M3FN codes),
+             kR  uint16 [num_blocks][block][64] (bf16), scale float32 [num_blocks][block]
+
+Draw order for a seed (numpy ``default_rng(seed)``): lengths (ragged only),
+block permutation (paged only), c, k^R, q_nope, q_rope, W_UK, W_UV.  c and
+k^R are drawn for every pool row (spare blocks and page tails included) and
+then overwritten with NaN where no sequence owns the row.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+D_HEAD = 128
+BLOCK = 64
+ROW = D_LATENT + D_ROPE  # 576 numbers per token per layer
+
+BF16_NAN = np.uint16(0x7FC0)
+E4M3_NAN = np.uint8(0x7F)
+E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    q_per_seq: int
+    heads: int
+    cache_dtype: str                 # "f32" | "bf16" | "fp8"
+    seq_len: Optional[int] = None    # uniform context length
+    len_range: Optional[Tuple[int, int]] = None  # inclusive uniform draw
+    paged: bool = False              # permuted shared block pool
+    spare_blocks: int = 0            # NaN-poisoned blocks no sequence owns
+    num_splits: int = 1              # KV splits the workload prescribes (0 = launcher's choice)
+    seed: int = 0
+    weight_std: float = 1.0 / math.sqrt(D_LATENT)
+
+    @property
+    def q_dtype(self) -> str:
+        return "f32" if self.cache_dtype == "f32" else "bf16"
+
+    @property
+    def w_dtype(self) -> str:
+        return "f32" if self.cache_dtype == "f32" else "bf16"
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five measured configurations.  Seeds are 1000 + position.
+WORKLOADS = {
+    # fp32 everywhere; B=1, H=16, T=1024, contiguous.
+    "fp32_b1_h16_t1k": Workload("fp32_b1_h16_t1k", batch=1, q_per_seq=1, heads=16,
+                                cache_dtype="f32", seq_len=1024, seed=1000),
+    # DeepSeek-V2 head shape, bf16 cache/q/weights; B=32, T=4096, contiguous.
+    "bf16_b32_h128_t4k": Workload("bf16_b32_h128_t4k", batch=32, q_per_seq=1, heads=128,
+                                  cache_dtype="bf16", seq_len=4096, num_splits=0, seed=1001),
+    # Paged ragged batch: B=64, lengths ~ U[512, 16384], permuted shared pool.
+    "bf16_paged_b64_ragged": Workload("bf16_paged_b64_ragged", batch=64, q_per_seq=1, heads=128,
+                                      cache_dtype="bf16", len_range=(512, 16384), paged=True,
+                                      spare_blocks=64, num_splits=0, seed=1002),
+    # Long context: B=1, T=131072 split into 64 chunks, paged permuted.
+    "bf16_long_t128k_s64": Workload("bf16_long_t128k_s64", batch=1, q_per_seq=1, heads=128,
+                                    cache_dtype="bf16", seq_len=131072, paged=True,
+                                    spare_blocks=64, num_splits=64, seed=1003),
+    # fp8 E4M3 latent + fp32 per-token scale, bf16 k^R; B=128, T=8192, 2 causal query tokens.
+    "fp8_b128_t8k_sq2": Workload("fp8_b128_t8k_sq2", batch=128, q_per_seq=2, heads=128,
+                                 cache_dtype="fp8", seq_len=8192, paged=True,
+                                 spare_blocks=64, num_splits=0, seed=1004),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+HEADLINE = "bf16_b32_h128_t4k"
+
+
+def small_variants():
+    """Reduced copies of each workload that the fp64 oracle finishes in
+    seconds: several 64-token pages, ragged tails, every dtype and S_q."""
+    w = WORKLOADS
+    return {
+        "fp32_b1_h16_t1k": w["fp32_b1_h16_t1k"],
+        "bf16_small_contig": w["bf16_b32_h128_t4k"].scaled(
+            name="bf16_small_contig", batch=3, seq_len=300, num_splits=1, seed=2001),
+        "bf16_small_paged": w["bf16_paged_b64_ragged"].scaled(
+            name="bf16_small_paged", batch=5, len_range=(1, 700), spare_blocks=5,
+            num_splits=1, seed=2002),
+        "bf16_small_split": w["bf16_long_t128k_s64"].scaled(
+            name="bf16_small_split", seq_len=2500, spare_blocks=3, num_splits=7, seed=2003),
+        "fp8_small_sq2": w["fp8_b128_t8k_sq2"].scaled(
+            name="fp8_small_sq2", batch=3, len_range=(2, 333), spare_blocks=2,
+            num_splits=1, seed=2004),
+    }
+
+
+# ----------------------------------------------------------------------------
+# storage encodings
+# ----------------------------------------------------------------------------
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns the
+    16-bit patterns.  Inputs here are finite draws, so no NaN handling."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _e4m3_positive_table() -> np.ndarray:
+    """Values of the 127 finite non-negative OCP E4M3FN codes 0x00..0x7E,
+    from the format's definition: bias 7, 3 mantissa bits, subnormals at
+    exponent field 0, code 0x7F is NaN, no infinities."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals, dtype=np.float64)
+
+
+_E4M3_POS = _e4m3_positive_table()
+# midpoints of neighbouring codes have at most 5 significant bits: exact in float32
+_E4M3_MID = ((_E4M3_POS[:-1] + _E4M3_POS[1:]) / 2.0).astype(np.float32)
+
+
+def e4m3_codes(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+    """Encode finite float32 values as OCP E4M3FN bytes, round to nearest with
+    ties to the even code, saturating at +-448.  Works in chunks so very large
+    caches do not need 64-bit temporaries of their full size."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    n_mid = _E4M3_MID.size
+    for lo in range(0, flat.size, chunk):
+        v = flat[lo: lo + chunk]
+        a = np.minimum(np.abs(v), np.float32(E4M3_MAX))
+        idx = np.searchsorted(_E4M3_MID, a, side="left")
+        hit = np.minimum(idx, n_mid - 1)
+        tie = (idx < n_mid) & (a == _E4M3_MID[hit])
+        idx = np.where(tie & (idx % 2 == 1), idx + 1, idx).astype(np.uint8)
+        out[lo: lo + chunk] = np.where(np.signbit(v), idx | np.uint8(0x80), idx)
+    return out.reshape(x.shape)
+
+
+# ----------------------------------------------------------------------------
+# generation
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Inputs:
+    wl: Workload
+    seq_lens: np.ndarray          # int32 [B]   cached tokens incl. the S_q query tokens
+    block_table: np.ndarray       # int32 [B][max_blocks]
+    num_blocks: int
+    # cache storage (see module docstring)
+    latent: np.ndarray            # f32/bf16: pool [nb][64][576]; fp8: c8 [nb][64][512]
+    rope: Optional[np.ndarray]    # fp8 only: bf16 [nb][64][64]; else None (interleaved)
+    scale: Optional[np.ndarray]   # fp8 only: float32 [nb][64]
+    q_nope: np.ndarray            # [B*S_q][H][128]   f32 or bf16 bits
+    q_rope: np.ndarray            # [B*S_q][H][64]
+    w_uk: np.ndarray              # [H][128][512]
+    w_uv: np.ndarray              # [H][128][512]
+    softmax_scale: float
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def kv_tokens(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum())
+
+
+def _encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def draw_lengths(wl: Workload, rng: np.random.Generator) -> np.ndarray:
+    if wl.len_range is not None:
+        lo, hi = wl.len_range
+        lens = rng.integers(lo, hi + 1, size=wl.batch)
+    else:
+        lens = np.full(wl.batch, wl.seq_len)
+    if (lens < wl.q_per_seq).any():
+        raise ValueError("every sequence must hold at least its query tokens")
+    return lens.astype(np.int32)
+
+
+def generate(wl: Workload, seed: Optional[int] = None, poison: bool = True) -> Inputs:
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
+    lens = draw_lengths(wl, rng)
+    pages = (lens.astype(np.int64) + BLOCK - 1) // BLOCK
+    max_blocks = int(pages.max())
+    used = int(pages.sum())
+    nb = used + wl.spare_blocks
+    if wl.paged:
+        perm = rng.permutation(nb).astype(np.int32)
+    else:
+        perm = np.arange(nb, dtype=np.int32)
+    table = np.zeros((B, max_blocks), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, : pages[b]] = perm[off: off + pages[b]]
+        # entries past the sequence's last page name a poisoned spare block
+        # (or, without spares, the sequence's first block): no kernel may read them
+        table[b, pages[b]:] = perm[used] if wl.spare_blocks > 0 else perm[off]
+        off += pages[b]
+    owned = np.zeros((nb, BLOCK), dtype=bool)
+    for b in range(B):
+        for j in range(pages[b]):
+            rows = min(BLOCK, int(lens[b]) - j * BLOCK)
+            owned[table[b, j], :rows] = True
+
+    c = rng.standard_normal((nb, BLOCK, D_LATENT), dtype=np.float32)
+    kr = rng.standard_normal((nb, BLOCK, D_ROPE), dtype=np.float32)
+    q_nope = rng.standard_normal((B * Sq, H, D_HEAD), dtype=np.float32)
+    q_rope = rng.standard_normal((B * Sq, H, D_ROPE), dtype=np.float32)
+    w_uk = rng.standard_normal((H, D_HEAD, D_LATENT), dtype=np.float32) * np.float32(wl.weight_std)
+    w_uv = rng.standard_normal((H, D_HEAD, D_LATENT), dtype=np.float32) * np.float32(wl.weight_std)
+
+    scale = None
+    rope = None
+    if wl.cache_dtype == "fp8":
+        amax = np.abs(c).max(axis=2)
+        scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        safe = np.where(scale > 0, scale, np.float32(1.0))
+        latent = e4m3_codes(c / safe[..., None])
+        rope = bf16_bits(kr)
+        if poison:
+            latent[~owned] = E4M3_NAN
+            rope[~owned] = BF16_NAN
+            scale[~owned] = np.float32("nan")
+    else:
+        pool = np.concatenate([c, kr], axis=2)
+        latent = _encode(pool, wl.cache_dtype)
+        if poison:
+            latent[~owned] = np.float32("nan") if wl.cache_dtype == "f32" else BF16_NAN
+    del c, kr
+    return Inputs(
+        wl=wl, seq_lens=lens, block_table=table, num_blocks=nb,
+        latent=latent, rope=rope, scale=scale,
+        q_nope=_encode(q_nope, wl.q_dtype), q_rope=_encode(q_rope, wl.q_dtype),
+        w_uk=_encode(w_uk, wl.w_dtype), w_uv=_encode(w_uv, wl.w_dtype),
+        softmax_scale=1.0 / math.sqrt(D_HEAD + D_ROPE),
+    )
+
+
+def depaged(inp: Inputs) -> Inputs:
+    """Same logical cache, rewritten as a contiguous pool with an identity
+    page table (sequence b owns blocks b*max_blocks ...).  Used to check that
+    paging changes no output bit."""
+    B, mb = inp.block_table.shape
+    src = inp.block_table.reshape(-1)
+    table = np.arange(B * mb, dtype=np.int32).reshape(B, mb)
+    latent = np.ascontiguousarray(inp.latent[src])
+    rope = None if inp.rope is None else np.ascontiguousarray(inp.rope[src])
+    scale = None if inp.scale is None else np.ascontiguousarray(inp.scale[src])
+    return dataclasses.replace(inp, block_table=table, num_blocks=B * mb,
+                               latent=latent, rope=rope, scale=scale)
+
+
+def cache_bytes_per_token(cache_dtype: str) -> int:
+    """Bytes of one cached token as stored: 576 numbers (+ a 4-byte scale for fp8)."""
+    return {"f32": ROW * 4, "bf16": ROW * 2, "fp8": D_LATENT + 4 + D_ROPE * 2}[cache_dtype]

@@ -1,0 +1,325 @@
+"""Plain, slow, fp64 reference for MLA decode -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this module.  It shares no code with the HIP
+path and imports nothing from it.
+
+Sources (the pages this follows; the short names are used below):
+
+* [DF-bottleneck]  deepforge.srivtx.xyz "DeepSeek-V2: A Strong, Economical, and
+  Efficient Mixture-of-Experts Language Model", section 1 "Theory from first
+  principles", part "The bottleneck at inference time": decode compares the new
+  token's query with the keys of all earlier tokens and mixes their values; an
+  MHA cache entry is one key and one value of width d_head per head per layer.
+* [DF-latent]      same page, section 1, part "Store a latent, rebuild the keys
+  and values" and its formula box "MLA: compress once, reconstruct in
+  attention": the cache holds c_t (512 wide) and one 64-wide decoupled RoPE
+  key per token per layer; keys and values are k = W_UK c and v = W_UV c, and
+  because these maps are linear W_UK can be folded into the query side and
+  W_UV into the output side ("absorption").
+* [DF-snippet]     same page, section 1, the two cache-size helpers and the
+  ratio they print for 128 heads x 128, 60 layers, 8192 context, 2 bytes.
+* [CA-takeaways]   crackai.dev "DeepSeek-V2" card, "Key Takeaways for
+  Interviews": MHA caches 2 x n_heads x d_head, GQA 2 x n_groups x d_head, MLA
+  d_latent plus the small RoPE part, per token per layer.
+
+What the pages leave open (read plainly, listed with reasons in the design
+notes of the repository): the softmax scale is 1/sqrt(d_head + d_rope); one
+k^R row per token is shared by all heads while q_rope is per head; inputs are
+already RoPE-rotated; W_UK and W_UV are stored per head as [d_head][d_latent]
+so that k = W_UK c; with S_q query tokens per sequence, query i sees the first
+len - (S_q - 1 - i) cached tokens (its own included).
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+facts fixed outside this file -- numbers the pages print, closed forms, a
+library attention routine, brute force in exact arithmetic, and planted
+mistakes that must be caught.  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+D_HEAD = 128
+
+__all__ = [
+    "decode_bf16", "decode_e4m3", "decode_f32",
+    "gather_sequence", "reconstruct_keys", "reconstruct_values", "query_vector",
+    "visible_tokens", "scores", "softmax_lse", "mix_values",
+    "explicit_decode", "absorbed_decode", "split_ranges", "split_partials",
+    "combine_partials", "cache_numbers_per_token_layer", "cache_bytes",
+    "default_softmax_scale",
+]
+
+
+# ----------------------------------------------------------------------------
+# storage decoding (exact in fp64)
+# ----------------------------------------------------------------------------
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64.  A bf16 value is the upper half of a
+    float32, so shifting the 16 bits up and reinterpreting is exact."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def decode_f32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN bytes -> float64, from the format definition: sign bit 7,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+    subnormals m * 2^-9; 0x7F / 0xFF are NaN; there are no infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 0xF) & (c & 0x7 == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def _decoder(kind: str):
+    return {"f32": decode_f32, "bf16": decode_bf16}[kind]
+
+
+# ----------------------------------------------------------------------------
+# the cached sequence
+# ----------------------------------------------------------------------------
+
+def gather_sequence(inp, b: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Logical cache of sequence b as (C [len][512], KR [len][64]) in fp64.
+
+    Token t lives in row t mod P of physical block block_table[b][t div P]
+    (P = 64).  Only the c_t latent and the k^R_t key are cached [DF-latent]."""
+    n = int(inp.seq_lens[b])
+    P = inp.latent.shape[1]
+    t = np.arange(n)
+    blocks = inp.block_table[b][t // P]
+    rows = t % P
+    kind = inp.wl.cache_dtype
+    if kind == "fp8":
+        C = decode_e4m3(inp.latent[blocks, rows]) * inp.scale[blocks, rows].astype(np.float64)[:, None]
+        KR = decode_bf16(inp.rope[blocks, rows])
+    else:
+        full = _decoder(kind)(inp.latent[blocks, rows])
+        C, KR = full[:, :D_LATENT], full[:, D_LATENT:D_LATENT + D_ROPE]
+    return C, KR
+
+
+def reconstruct_keys(C: np.ndarray, KR: np.ndarray, w_uk_h: np.ndarray) -> np.ndarray:
+    """Per-head keys k_t = [W_UK c_t ; k^R_t]  ([DF-latent]: k = W_UK c, plus
+    the decoupled RoPE key, shared by all heads).  W_UK is [d_head][d_latent]."""
+    return np.concatenate([C @ w_uk_h.T, KR], axis=1)
+
+
+def reconstruct_values(C: np.ndarray, w_uv_h: np.ndarray) -> np.ndarray:
+    """Per-head values v_t = W_UV c_t  ([DF-latent])."""
+    return C @ w_uv_h.T
+
+
+def query_vector(q_nope: np.ndarray, q_rope: np.ndarray) -> np.ndarray:
+    """The 192-wide query [q_nope ; q_rope] matching the key layout."""
+    return np.concatenate([q_nope, q_rope])
+
+
+def visible_tokens(seq_len: int, q_per_seq: int, i: int) -> int:
+    """Query i of the S_q newest tokens sees every earlier token and itself
+    ([DF-bottleneck]); the S_q query tokens are the last ones counted in len."""
+    return max(0, int(seq_len) - (q_per_seq - 1 - i))
+
+
+def scores(K: np.ndarray, q: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """s_t = (k_t . q) * scale."""
+    return (K @ q) * softmax_scale
+
+
+def softmax_lse(s: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Textbook softmax with the max subtracted; also ln(sum exp s)."""
+    if s.size == 0:
+        return s.copy(), -math.inf
+    m = s.max()
+    e = np.exp(s - m)
+    z = e.sum()
+    return e / z, float(m + math.log(z))
+
+
+def mix_values(p: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """o = sum_t p_t v_t  ([DF-bottleneck]: mix the values)."""
+    if p.size == 0:
+        return np.zeros(V.shape[1])
+    return p @ V
+
+
+def default_softmax_scale() -> float:
+    return 1.0 / math.sqrt(D_HEAD + D_ROPE)
+
+
+def _weights(inp):
+    d = _decoder(inp.wl.w_dtype)
+    return d, d
+
+
+def _selection(inp, select: Optional[Iterable[Tuple[int, int, int]]]):
+    """{b: {h: [i...]}} for the requested (b, i, h) rows, default all."""
+    B, Sq, H = inp.wl.batch, inp.wl.q_per_seq, inp.wl.heads
+    want = {}
+    if select is None:
+        for b in range(B):
+            want[b] = {h: list(range(Sq)) for h in range(H)}
+    else:
+        for b, i, h in select:
+            want.setdefault(int(b), {}).setdefault(int(h), []).append(int(i))
+    return want
+
+
+def explicit_decode(inp, select=None, softmax_scale: Optional[float] = None):
+    """The definition: rebuild every head's keys and values from the latent
+    cache and run softmax attention ([DF-latent], [DF-bottleneck]).
+
+    Returns (o [B*S_q][H][128], lse [B*S_q][H]) in fp64; rows that were not
+    selected are NaN."""
+    wl = inp.wl
+    B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
+    scale = inp.softmax_scale if softmax_scale is None else softmax_scale
+    dq = _decoder(wl.q_dtype)
+    dw = _decoder(wl.w_dtype)
+    o = np.full((B * Sq, H, D_HEAD), np.nan)
+    lse = np.full((B * Sq, H), np.nan)
+    for b, heads in _selection(inp, select).items():
+        C, KR = gather_sequence(inp, b)
+        for h, rows in heads.items():
+            K = reconstruct_keys(C, KR, dw(inp.w_uk[h]))
+            V = reconstruct_values(C, dw(inp.w_uv[h]))
+            for i in rows:
+                r = b * Sq + i
+                n = visible_tokens(inp.seq_lens[b], Sq, i)
+                q = query_vector(dq(inp.q_nope[r, h]), dq(inp.q_rope[r, h]))
+                p, l = softmax_lse(scores(K[:n], q, scale))
+                o[r, h] = mix_values(p, V[:n])
+                lse[r, h] = l
+    return o, lse
+
+
+def absorbed_decode(inp, select=None, softmax_scale: Optional[float] = None):
+    """The absorbed form, written separately ([DF-latent] "absorption"):
+    q_lat = W_UK^T q_nope, s_t = (q_lat . c_t + q_rope . k^R_t) * scale,
+    o_lat = sum_t p_t c_t, o = W_UV o_lat.
+
+    Returns (q_lat, o_lat, lse, o), fp64, NaN for unselected rows."""
+    wl = inp.wl
+    B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
+    scale = inp.softmax_scale if softmax_scale is None else softmax_scale
+    dq = _decoder(wl.q_dtype)
+    dw = _decoder(wl.w_dtype)
+    q_lat = np.full((B * Sq, H, D_LATENT), np.nan)
+    o_lat = np.full((B * Sq, H, D_LATENT), np.nan)
+    o = np.full((B * Sq, H, D_HEAD), np.nan)
+    lse = np.full((B * Sq, H), np.nan)
+    for b, heads in _selection(inp, select).items():
+        C, KR = gather_sequence(inp, b)
+        for h, rows in heads.items():
+            w_uk, w_uv = dw(inp.w_uk[h]), dw(inp.w_uv[h])
+            for i in rows:
+                r = b * Sq + i
+                n = visible_tokens(inp.seq_lens[b], Sq, i)
+                ql = w_uk.T @ dq(inp.q_nope[r, h])
+                s = (C[:n] @ ql + KR[:n] @ dq(inp.q_rope[r, h])) * scale
+                p, l = softmax_lse(s)
+                ol = mix_values(p, C[:n])
+                q_lat[r, h], o_lat[r, h], lse[r, h] = ql, ol, l
+                o[r, h] = w_uv @ ol
+    return q_lat, o_lat, lse, o
+
+
+# ----------------------------------------------------------------------------
+# split-KV and its log-sum-exp merge
+# ----------------------------------------------------------------------------
+
+def split_ranges(seq_len: int, num_splits: int, block: int = 64):
+    """Cut a sequence's pages into num_splits page-aligned chunks of
+    ceil(pages / num_splits) pages each; trailing chunks may be empty."""
+    pages = -(-int(seq_len) // block)
+    per = -(-pages // num_splits) if pages else 0
+    out = []
+    for s in range(num_splits):
+        lo = min(s * per * block, seq_len)
+        hi = min((s + 1) * per * block, seq_len)
+        out.append((lo, hi))
+    return out
+
+
+def split_partials(inp, num_splits: int, select=None, softmax_scale=None):
+    """Per chunk: normalised latent output and log-sum-exp over that chunk's
+    visible tokens; an empty chunk gives zeros and -inf.
+
+    Returns (o_part [B][ns][S_q][H][512], lse_part [B][ns][S_q][H])."""
+    wl = inp.wl
+    B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
+    scale = inp.softmax_scale if softmax_scale is None else softmax_scale
+    dq = _decoder(wl.q_dtype)
+    dw = _decoder(wl.w_dtype)
+    o_part = np.full((B, num_splits, Sq, H, D_LATENT), np.nan)
+    lse_part = np.full((B, num_splits, Sq, H), np.nan)
+    for b, heads in _selection(inp, select).items():
+        C, KR = gather_sequence(inp, b)
+        ranges = split_ranges(inp.seq_lens[b], num_splits, inp.latent.shape[1])
+        for h, rows in heads.items():
+            w_uk = dw(inp.w_uk[h])
+            for i in rows:
+                r = b * Sq + i
+                n = visible_tokens(inp.seq_lens[b], Sq, i)
+                ql = w_uk.T @ dq(inp.q_nope[r, h])
+                s_all = (C[:n] @ ql + KR[:n] @ dq(inp.q_rope[r, h])) * scale
+                for sidx, (lo, hi) in enumerate(ranges):
+                    hi = min(hi, n)
+                    lo = min(lo, hi)
+                    p, l = softmax_lse(s_all[lo:hi])
+                    o_part[b, sidx, i, h] = mix_values(p, C[lo:hi])
+                    lse_part[b, sidx, i, h] = l
+    return o_part, lse_part
+
+
+def combine_partials(o_part: np.ndarray, lse_part: np.ndarray):
+    """Merge chunk results: lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.
+    Chunks with lse = -inf carry weight 0; if every chunk is empty the result
+    is o = 0, lse = -inf.  The split axis is axis 1 of o_part [B][ns][...][d]."""
+    o_part = np.asarray(o_part, dtype=np.float64)
+    lse_part = np.asarray(lse_part, dtype=np.float64)
+    m = lse_part.max(axis=1, keepdims=True)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_part), np.exp(lse_part - m_safe), 0.0)
+    z = w.sum(axis=1, keepdims=True)
+    lse = np.where(finite, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)[:, 0]
+    wn = np.where(z > 0, w / np.where(z > 0, z, 1.0), 0.0)
+    o = (wn[..., None] * np.where(wn[..., None] > 0, o_part, 0.0)).sum(axis=1)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# cache accounting ([DF-bottleneck], [DF-snippet], [CA-takeaways])
+# ----------------------------------------------------------------------------
+
+def cache_numbers_per_token_layer(scheme: str, *, heads: int = 0, d_head: int = 0,
+                                  groups: float = 0, d_latent: int = 0, d_rope: int = 0) -> float:
+    """Numbers cached per token per layer.  MHA: a key and a value of width
+    d_head for each head; GQA: the same per group; MLA: the latent plus the
+    decoupled RoPE key."""
+    if scheme == "mha":
+        return 2 * heads * d_head
+    if scheme == "gqa":
+        return 2 * groups * d_head
+    if scheme == "mla":
+        return d_latent + d_rope
+    raise ValueError(scheme)
+
+
+def cache_bytes(numbers_per_token_layer: float, layers: int, context: int, bytes_per: int = 2):
+    """Whole-cache bytes for one sequence."""
+    return numbers_per_token_layer * layers * context * bytes_per

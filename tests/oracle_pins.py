@@ -1,0 +1,331 @@
+"""Pin checks for the fp64 oracle.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with
+something fixed outside it: a number the pages print, a closed form, a
+library attention routine, brute force in exact arithmetic, or an invariant
+the method guarantees.  ``test_oracle_pins.py`` runs them on the oracle as it
+is; ``test_oracle_mutants.py`` plants plausible mistakes in the oracle and
+requires at least one check to fail for each.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DL, DR, DH = 512, 64, 128
+
+
+def tiny_inputs(lens, heads=2, q_per_seq=1, seed=0, integer=False, block=64,
+                permute=True, scale=None):
+    """fp32-stored inputs of arbitrary small shape, built directly (no HIP
+    code, no generator): random or small-integer values, an optionally
+    permuted block pool, NaN in every row no sequence owns."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    B = lens.size
+    pages = [max(1, -(-int(n) // block)) for n in lens]
+    nb = sum(pages) + 1
+    order = rng.permutation(nb) if permute else np.arange(nb)
+    mb = max(pages)
+    table = np.zeros((B, mb), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :pages[b]] = order[off:off + pages[b]]
+        table[b, pages[b]:] = order[-1]
+        off += pages[b]
+    draw = (lambda *s: rng.integers(-3, 4, size=s).astype(np.float32)) if integer else \
+           (lambda *s: rng.standard_normal(s).astype(np.float32))
+    latent = draw(nb, block, DL + DR)
+    owned = np.zeros((nb, block), dtype=bool)
+    for b in range(B):
+        for t in range(int(lens[b])):
+            owned[table[b, t // block], t % block] = True
+    latent[~owned] = np.nan
+    wscale = 1.0 if integer else 1.0 / math.sqrt(DL)
+    wl = SimpleNamespace(batch=B, q_per_seq=q_per_seq, heads=heads, cache_dtype="f32",
+                         q_dtype="f32", w_dtype="f32")
+    return SimpleNamespace(
+        wl=wl, seq_lens=lens, block_table=table, num_blocks=nb, latent=latent,
+        rope=None, scale=None,
+        q_nope=draw(B * q_per_seq, heads, DH), q_rope=draw(B * q_per_seq, heads, DR),
+        w_uk=(draw(heads, DH, DL) * np.float32(wscale)).astype(np.float32),
+        w_uv=(draw(heads, DH, DL) * np.float32(wscale)).astype(np.float32),
+        softmax_scale=(1.0 / math.sqrt(DH + DR)) if scale is None else scale,
+    )
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel()))
+
+
+# ----------------------------------------------------------------------------
+# numbers the pages print
+# ----------------------------------------------------------------------------
+
+def check_cache_arithmetic():
+    g = json.load(open(os.path.join(GOLDEN, "cache_arithmetic.json")))
+    e = g["mha_numbers_per_token_60L_128H_128d"]
+    per_layer = O.cache_numbers_per_token_layer("mha", heads=e["inputs"]["heads"],
+                                                d_head=e["inputs"]["d_head"])
+    total = per_layer * e["inputs"]["layers"]
+    assert f"{total / 1e6:.2f}M" == e["value_printed"], total
+    e = g["mla_numbers_per_token_layer"]
+    assert O.cache_numbers_per_token_layer("mla", **e["inputs"]) == e["value_printed"]
+    e = g["mha_numbers_per_token_layer_128H_128d"]
+    assert O.cache_numbers_per_token_layer("mha", **e["inputs"]) == e["value_printed"]
+    e = g["gqa_equivalent_groups"]
+    mla = O.cache_numbers_per_token_layer("mla", d_latent=512, d_rope=64)
+    assert O.cache_numbers_per_token_layer("gqa", groups=e["value_printed"],
+                                           d_head=e["inputs"]["d_head"]) == mla
+    e = g["dense_over_mla_bytes_integer_ratio"]
+    i = e["inputs"]
+    dense = O.cache_bytes(O.cache_numbers_per_token_layer("mha", heads=i["heads"], d_head=i["d_head"]),
+                          i["layers"], i["context"], i["bytes_per"])
+    mla = O.cache_bytes(O.cache_numbers_per_token_layer("mla", d_latent=i["d_latent"], d_rope=i["d_rope"]),
+                        i["layers"], i["context"], i["bytes_per"])
+    assert int(dense) // int(mla) == e["value_printed"]
+
+
+# ----------------------------------------------------------------------------
+# storage decoding vs the library's own casts
+# ----------------------------------------------------------------------------
+
+def check_decode_tables():
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+# ----------------------------------------------------------------------------
+# softmax
+# ----------------------------------------------------------------------------
+
+def check_softmax():
+    rng = np.random.default_rng(1)
+    for n in (1, 2, 7, 1000):
+        s = rng.standard_normal(n) * 5
+        p, lse = O.softmax_lse(s)
+        assert abs(p.sum() - 1.0) <= 1e-12
+        assert (p >= 0).all()
+        p2, lse2 = O.softmax_lse(s + 123.25)
+        assert np.max(np.abs(p2 - p)) <= 1e-12
+        assert abs((lse2 - 123.25) - lse) <= 1e-9
+        assert abs(lse - math.log(math.fsum(math.exp(x) for x in s))) <= 1e-9
+    p, lse = O.softmax_lse(np.array([0.0, math.log(3.0)]))
+    assert abs(p[0] - 0.25) <= 1e-15 and abs(p[1] - 0.75) <= 1e-15
+    assert abs(lse - math.log(4.0)) <= 1e-15
+
+
+# ----------------------------------------------------------------------------
+# reduction to a library attention routine
+# ----------------------------------------------------------------------------
+
+def check_textbook_reduction():
+    """With W_UK = [I_128 | 0] the reconstructed key of token t is
+    [c_t[:128] ; k^R_t]; MLA decode is then ordinary single-query softmax
+    attention, which torch's scaled_dot_product_attention computes (CPU, fp64)."""
+    import torch
+    import torch.nn.functional as F
+    inp = tiny_inputs([37, 130], heads=3, seed=5)
+    wuk = np.zeros((DH, DL), dtype=np.float32)
+    wuk[:, :DH] = np.eye(DH, dtype=np.float32)
+    inp.w_uk = np.stack([wuk] * 3)
+    o, lse = O.explicit_decode(inp)
+    q_lat, o_lat, lse_a, o_a = O.absorbed_decode(inp)
+    for b in range(2):
+        n = int(inp.seq_lens[b])
+        t = np.arange(n)
+        rows = inp.latent[inp.block_table[b][t // 64], t % 64].astype(np.float64)
+        for h in range(3):
+            k = np.concatenate([rows[:, :DH], rows[:, DL:]], axis=1)
+            v = rows[:, :DL] @ inp.w_uv[h].astype(np.float64).T
+            q = np.concatenate([inp.q_nope[b, h], inp.q_rope[b, h]]).astype(np.float64)
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(q)[None, None, None], torch.from_numpy(k)[None, None],
+                torch.from_numpy(v)[None, None], scale=1.0 / math.sqrt(192)).numpy()[0, 0, 0]
+            assert np.max(np.abs(o[b, h] - ref)) <= 1e-12 * max(1.0, np.abs(ref).max())
+            assert np.max(np.abs(o_a[b, h] - ref)) <= 1e-12 * max(1.0, np.abs(ref).max())
+            s = (k @ q) / math.sqrt(192)
+            ref_lse = float(torch.logsumexp(torch.from_numpy(s), 0))
+            assert abs(lse[b, h] - ref_lse) <= 1e-12 and abs(lse_a[b, h] - ref_lse) <= 1e-12
+
+
+# ----------------------------------------------------------------------------
+# closed forms and special cases
+# ----------------------------------------------------------------------------
+
+def check_closed_forms():
+    # one cached token: softmax weight 1, o = W_UV c_0, lse = s_0
+    inp = tiny_inputs([1], heads=2, seed=2)
+    o, lse = O.explicit_decode(inp)
+    blk = inp.block_table[0, 0]
+    c0 = inp.latent[blk, 0].astype(np.float64)
+    for h in range(2):
+        assert np.max(np.abs(o[0, h] - inp.w_uv[h].astype(np.float64) @ c0[:DL])) <= 1e-12
+        k = np.concatenate([inp.w_uk[h].astype(np.float64) @ c0[:DL], c0[DL:]])
+        q = np.concatenate([inp.q_nope[0, h], inp.q_rope[0, h]]).astype(np.float64)
+        assert abs(lse[0, h] - (k @ q) / math.sqrt(192)) <= 1e-12
+    # zero query: uniform weights, o = W_UV mean(c), lse = ln(len)
+    inp = tiny_inputs([150], heads=2, seed=3)
+    inp.q_nope[:] = 0
+    inp.q_rope[:] = 0
+    o, lse = O.explicit_decode(inp)
+    t = np.arange(150)
+    C = inp.latent[inp.block_table[0][t // 64], t % 64, :DL].astype(np.float64)
+    for h in range(2):
+        assert np.max(np.abs(o[0, h] - inp.w_uv[h].astype(np.float64) @ C.mean(axis=0))) <= 1e-12
+        assert abs(lse[0, h] - math.log(150)) <= 1e-12
+    # two tokens: p_0 = 1 / (1 + exp(s_1 - s_0))
+    inp = tiny_inputs([2], heads=1, seed=4)
+    o, lse = O.explicit_decode(inp)
+    rows = inp.latent[inp.block_table[0, 0], :2].astype(np.float64)
+    wuk, wuv = inp.w_uk[0].astype(np.float64), inp.w_uv[0].astype(np.float64)
+    q = np.concatenate([inp.q_nope[0, 0], inp.q_rope[0, 0]]).astype(np.float64)
+    s = [np.concatenate([wuk @ r[:DL], r[DL:]]) @ q / math.sqrt(192) for r in rows]
+    p0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+    ref = p0 * (wuv @ rows[0, :DL]) + (1 - p0) * (wuv @ rows[1, :DL])
+    assert np.max(np.abs(o[0, 0] - ref)) <= 1e-12
+    # a token whose key dominates every other one takes all the weight
+    inp = tiny_inputs([90], heads=1, seed=6)
+    n = 90
+    t = np.arange(n)
+    blocks, rows_ = inp.block_table[0][t // 64], t % 64
+    j = 41
+    ql = inp.w_uk[0].astype(np.float64).T @ inp.q_nope[0, 0].astype(np.float64)
+    inp.latent[blocks[j], rows_[j], :DL] = (60.0 * ql / np.linalg.norm(ql)).astype(np.float32)
+    o, _ = O.explicit_decode(inp)
+    cj = inp.latent[blocks[j], rows_[j], :DL].astype(np.float64)
+    assert rel_l2(o[0, 0], inp.w_uv[0].astype(np.float64) @ cj) <= 1e-6
+
+
+def check_brute_force_exact():
+    """Small-integer inputs, every step written out with Python integers and
+    math.fsum / math.exp, no numpy: scores are exact integers times the scale."""
+    inp = tiny_inputs([3, 5], heads=2, q_per_seq=2, seed=7, integer=True)
+    o, lse = O.explicit_decode(inp)
+    Sq = 2
+    for b in range(2):
+        n_all = int(inp.seq_lens[b])
+        toks = []
+        for t in range(n_all):
+            blk = int(inp.block_table[b][t // 64])
+            toks.append([int(x) for x in inp.latent[blk, t % 64]])
+        for h in range(2):
+            wuk = [[int(x) for x in row] for row in inp.w_uk[h]]
+            wuv = [[int(x) for x in row] for row in inp.w_uv[h]]
+            keys = [[sum(wuk[d][k] * c[k] for k in range(DL)) for d in range(DH)] + c[DL:] for c in toks]
+            vals = [[sum(wuv[d][k] * c[k] for k in range(DL)) for d in range(DH)] for c in toks]
+            for i in range(Sq):
+                r = b * Sq + i
+                q = [int(x) for x in inp.q_nope[r, h]] + [int(x) for x in inp.q_rope[r, h]]
+                n = n_all - (Sq - 1 - i)
+                dots = [sum(kk * qq for kk, qq in zip(keys[t], q)) for t in range(n)]
+                sc = 1.0 / math.sqrt(192)
+                sf = [float(d) * sc for d in dots]
+                m = max(sf)
+                e = [math.exp(x - m) for x in sf]
+                z = math.fsum(e)
+                ref_o = [math.fsum(e[t] * vals[t][d] for t in range(n)) / z for d in range(DH)]
+                ref_lse = m + math.log(z)
+                scale_o = max(1.0, max(abs(x) for x in ref_o))
+                assert max(abs(a - c) for a, c in zip(o[r, h], ref_o)) <= 1e-12 * scale_o
+                assert abs(lse[r, h] - ref_lse) <= 1e-12 * max(1.0, abs(ref_lse))
+
+
+# ----------------------------------------------------------------------------
+# invariants the method guarantees
+# ----------------------------------------------------------------------------
+
+def check_absorbed_equals_explicit(inp, select=None, tol=1e-12):
+    """Absorption is exact algebra ([DF-latent]): folding W_UK into the query
+    and W_UV into the output changes nothing but rounding."""
+    o, lse = O.explicit_decode(inp, select)
+    _, _, lse_a, o_a = O.absorbed_decode(inp, select)
+    m = ~np.isnan(lse)
+    assert rel_l2(o_a[m], o[m]) <= tol, rel_l2(o_a[m], o[m])
+    assert np.max(np.abs(lse_a[m] - lse[m])) <= tol * max(1.0, np.abs(lse[m]).max())
+
+
+def check_paging_invariance():
+    inp = tiny_inputs([70, 200, 5], heads=2, seed=8, permute=True)
+    flat = tiny_inputs([70, 200, 5], heads=2, seed=8, permute=True)
+    # rebuild `flat` as the same logical cache in an identity-ordered pool
+    B, mb = inp.block_table.shape
+    src = inp.block_table.reshape(-1)
+    flat.latent = np.ascontiguousarray(inp.latent[src])
+    flat.block_table = np.arange(B * mb, dtype=np.int32).reshape(B, mb)
+    a = O.explicit_decode(inp)
+    b = O.explicit_decode(flat)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def check_causal_two_tokens():
+    """With two query tokens, the older one sees one token fewer: it equals a
+    single-query decode over the first len-1 tokens."""
+    two = tiny_inputs([66, 131], heads=2, q_per_seq=2, seed=9)
+    o2, l2 = O.explicit_decode(two)
+    one = tiny_inputs([65, 130], heads=2, q_per_seq=1, seed=9)
+    one.latent, one.block_table = two.latent, two.block_table
+    one.w_uk, one.w_uv = two.w_uk, two.w_uv
+    one.q_nope = np.ascontiguousarray(two.q_nope[0::2])
+    one.q_rope = np.ascontiguousarray(two.q_rope[0::2])
+    o1, l1 = O.explicit_decode(one)
+    assert np.array_equal(o2[0::2], o1) and np.array_equal(l2[0::2], l1)
+    # and the newer one sees the whole sequence
+    full = tiny_inputs([66, 131], heads=2, q_per_seq=1, seed=9)
+    full.latent, full.block_table = two.latent, two.block_table
+    full.w_uk, full.w_uv = two.w_uk, two.w_uv
+    full.q_nope = np.ascontiguousarray(two.q_nope[1::2])
+    full.q_rope = np.ascontiguousarray(two.q_rope[1::2])
+    of, lf = O.explicit_decode(full)
+    assert np.array_equal(o2[1::2], of) and np.array_equal(l2[1::2], lf)
+
+
+def check_split_combine():
+    """Any page-aligned partition of the tokens, merged by log-sum-exp, equals
+    the unsplit latent output (empty chunks included)."""
+    inp = tiny_inputs([1, 64, 65, 300], heads=2, q_per_seq=2, seed=10)
+    _, o_lat, lse, _ = O.absorbed_decode(inp)
+    B, Sq, H = 4, 2, 2
+    for ns in (1, 2, 3, 7):
+        op, lp = O.split_partials(inp, ns)
+        o, l = O.combine_partials(op, lp)
+        o = o.reshape(B * Sq, H, DL)
+        l = l.reshape(B * Sq, H)
+        assert np.max(np.abs(o - o_lat)) <= 1e-12
+        # a query that sees no token (len 1, older of two queries) has lse -inf
+        assert np.array_equal(np.isneginf(l), np.isneginf(lse))
+        fin = np.isfinite(lse)
+        assert np.max(np.abs(l[fin] - lse[fin])) <= 1e-12
+    # a chunking that cannot be page-aligned differently: each chunk alone
+    assert O.split_ranges(300, 7) == [(0, 64), (64, 128), (128, 192), (192, 256),
+                                      (256, 300), (300, 300), (300, 300)]
+    assert O.split_ranges(300, 2) == [(0, 192), (192, 300)]
+    # all-empty merge
+    o, l = O.combine_partials(np.zeros((1, 3, 4)), np.full((1, 3), -np.inf))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+ALL_CHECKS = [check_cache_arithmetic, check_decode_tables, check_softmax,
+              check_textbook_reduction, check_closed_forms, check_brute_force_exact,
+              check_paging_invariance, check_causal_two_tokens, check_split_combine]

@@ -1,0 +1,156 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and require that the
+pin checks catch each one.  This shows the pins constrain every step: a
+dropped term, a wrong scale, an off-by-one mask, a wrong index or operand."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mla_oracle as M
+from oracle_pins import ALL_CHECKS
+
+_orig = {name: getattr(M, name) for name in dir(M) if callable(getattr(M, name))}
+
+
+def _keys_without_rope(C, KR, w):
+    return np.concatenate([C @ w.T, np.zeros_like(KR)], axis=1)
+
+
+def _keys_transposed_weight(C, KR, w):
+    # uses W_UK's first 128 latent columns as if it were [d_latent][d_head]
+    return np.concatenate([C @ w.T[:, ::-1], KR], axis=1)
+
+
+def _values_skip_projection(C, w):
+    return C[:, :w.shape[0]]
+
+
+def _scores_wrong_scale(K, q, s):
+    return (K @ q) / math.sqrt(128)
+
+
+def _scores_sign(K, q, s):
+    return -(K @ q) * s
+
+
+def _visible_excludes_self(n, sq, i):
+    return max(0, int(n) - (sq - i))
+
+
+def _visible_ignores_causal(n, sq, i):
+    return int(n)
+
+
+def _gather_ignores_table(inp, b):
+    n = int(inp.seq_lens[b])
+    t = np.arange(n)
+    start = int(inp.block_table[b][0])
+    blocks = start + t // 64
+    full = M.decode_f32(inp.latent[blocks % inp.latent.shape[0], t % 64])
+    return full[:, :512], full[:, 512:]
+
+
+def _gather_wrong_row(inp, b):
+    n = int(inp.seq_lens[b])
+    t = np.arange(n)
+    blocks = inp.block_table[b][t // 64]
+    full = M.decode_f32(inp.latent[blocks, (63 - t % 64) % 64])
+    return full[:, :512], full[:, 512:]
+
+
+def _softmax_no_norm(s):
+    if s.size == 0:
+        return s.copy(), -math.inf
+    m = s.max()
+    e = np.exp(s - m)
+    return e, float(m + math.log(e.sum()))
+
+
+def _softmax_lse_missing_max(s):
+    if s.size == 0:
+        return s.copy(), -math.inf
+    m = s.max()
+    e = np.exp(s - m)
+    return e / e.sum(), float(math.log(e.sum()))
+
+
+def _mix_reversed(p, V):
+    return p[::-1] @ V if p.size else np.zeros(V.shape[1])
+
+
+def _query_swapped(qn, qr):
+    return np.concatenate([qr, qn])
+
+
+def _e4m3_bias8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8) * np.exp2(e - 8.0))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def _e4m3_no_subnormal(codes):
+    out = _orig["decode_e4m3"](codes)
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.where((c & 0x78) == 0, 0.0 * out, out)
+
+
+def _bf16_truncated_mantissa(bits):
+    u = (np.asarray(bits, dtype=np.uint16) & np.uint16(0xFFFE)).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _combine_no_max_weight(o_part, lse_part):
+    w = np.where(np.isfinite(lse_part), 1.0, 0.0)
+    z = w.sum(axis=1, keepdims=True)
+    wn = np.where(z > 0, w / np.where(z > 0, z, 1), 0)
+    lse = np.log(np.exp(np.where(np.isfinite(lse_part), lse_part, -np.inf)).sum(axis=1))
+    return (wn[..., None] * np.nan_to_num(o_part)).sum(axis=1), lse
+
+
+def _split_token_equal(seq_len, ns, block=64):
+    per = -(-int(seq_len) // ns)
+    return [(min(s * per, seq_len), min((s + 1) * per, seq_len)) for s in range(ns)]
+
+
+def _cache_mha_one_vector(scheme, **kw):
+    if scheme == "mha":
+        return kw["heads"] * kw["d_head"]
+    return _orig["cache_numbers_per_token_layer"](scheme, **kw)
+
+
+MUTANTS = {
+    "reconstruct_keys": [_keys_without_rope, _keys_transposed_weight],
+    "reconstruct_values": [_values_skip_projection],
+    "scores": [_scores_wrong_scale, _scores_sign],
+    "visible_tokens": [_visible_excludes_self, _visible_ignores_causal],
+    "gather_sequence": [_gather_ignores_table, _gather_wrong_row],
+    "softmax_lse": [_softmax_no_norm, _softmax_lse_missing_max],
+    "mix_values": [_mix_reversed],
+    "query_vector": [_query_swapped],
+    "decode_e4m3": [_e4m3_bias8, _e4m3_no_subnormal],
+    "decode_bf16": [_bf16_truncated_mantissa],
+    "combine_partials": [_combine_no_max_weight],
+    "split_ranges": [_split_token_equal],
+    "cache_numbers_per_token_layer": [_cache_mha_one_vector],
+}
+
+CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]
+
+
+@pytest.mark.parametrize("name,mutant", CASES, ids=[f.__name__ for _, f in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(M, name, mutant)
+    monkeypatch.setattr(oracle, name, mutant, raising=False)
+    caught = []
+    for check in ALL_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(check.__name__)
+    assert caught, f"planted mistake {mutant.__name__} in {name} went unnoticed"
