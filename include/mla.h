@@ -1,0 +1,179 @@
+/*
+ * mla.h -- C ABI of the MLA absorbed-decode library for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  DeepSeek-V2 Multi-head Latent Attention caches, per token
+ * per layer, a 512-wide latent c_t and one 64-wide decoupled RoPE key k^R_t
+ * (deepforge.srivtx.xyz "DeepSeek-V2", section 1, "Store a latent, rebuild the
+ * keys and values" and the formula box "MLA: compress once, reconstruct in
+ * attention").  Keys and values are k = W_UK c and v = W_UV c per head; since
+ * both maps are linear, W_UK is folded into the query and W_UV into the output
+ * ("absorption", same passage), so decode attention runs on the cache itself:
+ *
+ *   q_lat[h]  = W_UK[h]^T q_nope[h]                          (mla_absorb_q)
+ *   s_t[h]    = (q_lat[h] . c_t + q_rope[h] . k^R_t) * scale  (mla_decode)
+ *   p[h]      = softmax_t(s[h]),  o_lat[h] = sum_t p_t[h] c_t
+ *   o_lat     = log-sum-exp merge of per-chunk results          (mla_split_combine)
+ *   o[h]      = W_UV[h] o_lat[h]                               (mla_out_uv)
+ *
+ * Decode compares the newest token's query with the keys of every earlier
+ * token and mixes their values (same page, section 1, "The bottleneck at
+ * inference time"); with S_q query tokens per sequence, query i (0-based,
+ * oldest first) sees the first len - (S_q - 1 - i) cached tokens.
+ *
+ * Conventions for every entry point.
+ *  - Every array argument is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees, copies to the host or synchronizes.  Struct
+ *    arguments (mla_dims, mla_paged_kv) are HOST pointers read during the call.
+ *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream).  Calls return as soon as the work is enqueued.
+ *  - Arrays are dense row-major unless a stride says otherwise; strides are
+ *    in elements.  bf16 is stored as its 16-bit pattern, E4M3 as OCP E4M3FN
+ *    bytes (the gfx950 fp8 format, max 448).
+ *  - Arguments are validated on the host before any launch; an invalid call
+ *    returns a negative mla_status and enqueues nothing.  Device-side data
+ *    (block_table, seq_lens) is trusted: entries must name blocks below
+ *    num_blocks and lengths must fit max_blocks_per_seq * block_size.
+ *  - Supported sizes: d_latent = 512, d_rope = 64, d_head = 128,
+ *    block_size = 64, 1 <= q_per_seq <= 2; anything else is MLA_ERR_SHAPE.
+ *  - Thread-safe: the library holds no mutable global state.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_dtype {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2 /* OCP E4M3FN, one fp32 scale per cached token */
+} mla_dtype;
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,   /* a required pointer is NULL                         */
+  MLA_ERR_SHAPE = -2,  /* a size is out of range or unsupported              */
+  MLA_ERR_DTYPE = -3,  /* an unsupported dtype or dtype combination          */
+  MLA_ERR_ALIGN = -4,  /* a pointer or stride breaks the 16-byte alignment   */
+  MLA_ERR_SPLITS = -5, /* num_splits < 1 or > MLA_MAX_SPLITS                 */
+  MLA_ERR_LAUNCH = -6, /* the HIP runtime refused the launch                 */
+  MLA_ERR_DEVICE = -7  /* no usable gfx950 device is current                 */
+} mla_status;
+
+#define MLA_MAX_SPLITS 1024
+
+/* Static description of one decode batch. */
+typedef struct mla_dims {
+  int32_t batch;       /* B: sequences                                       */
+  int32_t q_per_seq;   /* S_q: query tokens per sequence (1 or 2)            */
+  int32_t heads;       /* H: attention heads (1..1024)                       */
+  int32_t d_latent;    /* 512                                                */
+  int32_t d_rope;      /* 64                                                 */
+  int32_t d_head;      /* 128                                                */
+  float softmax_scale; /* multiplies q.k; DeepSeek-V2 head shape: 1/sqrt(192) */
+} mla_dims;
+
+/* Paged latent cache.  Token t of sequence b is row (t mod block_size) of
+ * physical block block_table[b * max_blocks_per_seq + t / block_size].
+ *
+ *   latent row:  latent + block * latent_block_stride + row * latent_row_stride
+ *                (d_latent values of latent_dtype)
+ *   rope row:    rope   + block * rope_block_stride   + row * rope_row_stride
+ *                (d_rope values of rope_dtype)
+ *   fp8 scale:   scale[block * scale_block_stride + row]  (fp32; fp8 only)
+ *
+ * The 576-wide interleaved layout [c | k^R] is rope = latent + 512 with both
+ * row strides 576 and both block strides 64 * 576.  Supported combinations:
+ *   latent F32  + rope F32                  (use with F32 queries)
+ *   latent BF16 + rope BF16                 (use with BF16 queries)
+ *   latent FP8_E4M3 + scale + rope BF16     (use with BF16 queries)
+ * Rows at or past a sequence's length may hold anything, NaN included: no
+ * output depends on them. */
+typedef struct mla_paged_kv {
+  const void* latent;
+  int32_t latent_dtype;
+  int64_t latent_block_stride;
+  int64_t latent_row_stride;
+  const void* rope;
+  int32_t rope_dtype;
+  int64_t rope_block_stride;
+  int64_t rope_row_stride;
+  const float* scale; /* FP8_E4M3 latent only, else NULL */
+  int64_t scale_block_stride;
+  int32_t block_size;         /* 64 */
+  int32_t num_blocks;         /* physical blocks in the pool */
+  int32_t max_blocks_per_seq; /* row length of block_table */
+  const int32_t* block_table; /* [batch][max_blocks_per_seq] int32 */
+  const int32_t* seq_lens;    /* [batch] int32, cached tokens incl. the S_q query tokens */
+} mla_paged_kv;
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_str(int status);
+
+/* MLA_ABI_VERSION of the built library. */
+int mla_abi_version(void);
+
+/* Query absorption (formula box "MLA: compress once, reconstruct in attention":
+ * k = W_UK c, folded into the query side):
+ *   q_lat[r][h][c] = sum_d w_uk[h][d][c] * q_nope[r][h][d],   r < batch*q_per_seq.
+ * q_nope: [batch*q_per_seq][heads][d_head], in_dtype (F32 or BF16)
+ * w_uk:   [heads][d_head][d_latent], in_dtype
+ * q_lat:  [batch*q_per_seq][heads][d_latent], q_lat_dtype (F32, or BF16
+ *         rounded to nearest-even from the fp32 sum)
+ * Products are exact, sums are fp32. */
+int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int32_t in_dtype,
+                 void* q_lat, int32_t q_lat_dtype, void* stream);
+
+/* Decode attention over the paged latent cache (same page, section 1, "The
+ * bottleneck at inference time" and "Store a latent, rebuild the keys and
+ * values"):
+ *   s_t = (q_lat . c_t + q_rope . k^R_t) * softmax_scale,  t visible to the query,
+ *   o_lat = sum_t softmax(s)_t c_t,   lse = ln sum_t exp(s_t).
+ * q_lat:  [batch*q_per_seq][heads][d_latent], q_dtype
+ * q_rope: [batch*q_per_seq][heads][d_rope],   q_dtype (F32 with an F32 cache, else BF16)
+ * num_splits == 1: o = o_lat [batch*q_per_seq][heads][d_latent], lse [batch*q_per_seq][heads].
+ * num_splits  > 1: each sequence's pages are cut into num_splits page-aligned
+ *   chunks of ceil(pages / num_splits) pages; chunk s writes its own
+ *   normalised result: o = [batch][num_splits][q_per_seq][heads][d_latent],
+ *   lse = [batch][num_splits][q_per_seq][heads]; merge with mla_split_combine.
+ * A query (or chunk) that sees no token writes o = 0 and lse = -inf.
+ * Arithmetic: bf16/fp8 caches use bf16 matrix cores with fp32 accumulation
+ * (E4M3 codes are exact in bf16; the per-token scale is applied in fp32);
+ * the F32 cache is computed in fp32 throughout. */
+int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int32_t q_dtype,
+               const mla_paged_kv* kv, int32_t num_splits, float* o, float* lse, void* stream);
+
+/* Log-sum-exp merge of mla_decode's per-chunk results:
+ *   lse = ln sum_s exp(lse_s),   o_lat = sum_s exp(lse_s - lse) o_s.
+ * Chunks with lse_s = -inf carry weight 0; if all do, o_lat = 0 and lse = -inf.
+ * o_part: [batch][num_splits][q_per_seq][heads][d_latent], lse_part: [batch][num_splits][q_per_seq][heads]
+ * o_lat:  [batch*q_per_seq][heads][d_latent];  lse: same layout as mla_decode's, or NULL. */
+int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_part,
+                      const float* lse_part, float* o_lat, float* lse, void* stream);
+
+/* Output absorption (W_UV folded into the output side, same formula box):
+ *   out[r][h][d] = sum_c w_uv[h][d][c] * o_lat[r][h][c].
+ * o_lat: [batch*q_per_seq][heads][d_latent] fp32
+ * w_uv:  [heads][d_head][d_latent], w_dtype (F32 or BF16)
+ * out:   [batch*q_per_seq][heads][d_head] fp32
+ * With BF16 weights the fp32 o_lat is split into two bf16 terms (hi + lo), so
+ * the result carries fp32-level accuracy at matrix-core speed. */
+int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32_t w_dtype,
+               float* out, void* stream);
+
+/* A launch-shape helper: the num_splits mla_decode should use so that the
+ * device's compute units are filled, given the longest sequence length the
+ * caller expects.  Writes 1 when one chunk per sequence already fills the
+ * device.  Host-only; reads the current device's compute-unit count. */
+int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,188 @@
+"""Python binding of libmla.so, the C-ABI MLA absorbed-decode library for
+MI355X (gfx950).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C entry point of the same name and raises on a
+non-zero status.  All arithmetic runs in the library's HIP kernels; PyTorch
+provides device memory and streams.  The library must have been built
+(``python -m mla_latent_kv_17_amd.build``); importing fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+MLA_OK = 0
+MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_ALIGN = -1, -2, -3, -4
+MLA_ERR_SPLITS, MLA_ERR_LAUNCH, MLA_ERR_DEVICE = -5, -6, -7
+MLA_MAX_SPLITS = 1024
+D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
+
+# the C entry points this binding exposes (also checked by the tests)
+EXPORTS = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_decode",
+           "mla_split_combine", "mla_out_uv", "mla_decode_num_splits"]
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_per_seq", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class MlaPagedKV(ctypes.Structure):
+    _fields_ = [("latent", ctypes.c_void_p), ("latent_dtype", ctypes.c_int32),
+                ("latent_block_stride", ctypes.c_int64), ("latent_row_stride", ctypes.c_int64),
+                ("rope", ctypes.c_void_p), ("rope_dtype", ctypes.c_int32),
+                ("rope_block_stride", ctypes.c_int64), ("rope_row_stride", ctypes.c_int64),
+                ("scale", ctypes.c_void_p), ("scale_block_stride", ctypes.c_int64),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+def _hip_runtimes():
+    try:
+        maps = open("/proc/self/maps").read().splitlines()
+    except OSError:
+        return set()
+    return {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mla_latent_kv_17_amd.build`")
+    # torch brings its own HIP runtime; load it first so that libmla.so binds to
+    # the same runtime (same soname) instead of a second copy whose streams and
+    # allocations would be foreign to torch's.
+    import torch  # noqa: F401
+    torch.cuda.is_available  # the HIP runtime is loaded with torch's extension
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped ({sorted(runtimes)}); import torch before loading "
+                          f"{LIB_PATH} by any other route")
+    vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    dp, kvp = ctypes.POINTER(MlaDims), ctypes.POINTER(MlaPagedKV)
+    sig = {
+        "mla_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "mla_abi_version": ([], ctypes.c_int),
+        "mla_absorb_q": ([dp, vp, vp, i32, vp, i32, vp], ctypes.c_int),
+        "mla_decode": ([dp, vp, vp, i32, kvp, i32, f32p, f32p, vp], ctypes.c_int),
+        "mla_split_combine": ([dp, i32, f32p, f32p, f32p, f32p, vp], ctypes.c_int),
+        "mla_out_uv": ([dp, f32p, vp, i32, f32p, vp], ctypes.c_int),
+        "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def status_str(status: int) -> str:
+    return _lib.mla_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.mla_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != MLA_OK:
+        raise MlaError(fn, status)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16,
+            torch.float8_e4m3fn: MLA_FP8_E4M3, torch.uint8: MLA_FP8_E4M3}[t.dtype]
+
+
+def make_dims(batch: int, q_per_seq: int, heads: int, softmax_scale: Optional[float] = None) -> MlaDims:
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D_HEAD + D_ROPE)
+    return MlaDims(batch, q_per_seq, heads, D_LATENT, D_ROPE, D_HEAD, softmax_scale)
+
+
+class PagedCache:
+    """Describes a paged latent cache held in torch device tensors.
+
+    ``latent``: [num_blocks][64][576] (f32/bf16, c | k^R interleaved) when
+    ``rope`` is None; else the fp8 codes [num_blocks][64][512] with
+    ``rope`` bf16 [num_blocks][64][64] and ``scale`` fp32 [num_blocks][64].
+    ``block_table`` int32 [B][max_blocks], ``seq_lens`` int32 [B]."""
+
+    def __init__(self, latent, block_table, seq_lens, rope=None, scale=None):
+        self.latent, self.rope, self.scale = latent, rope, scale
+        self.block_table, self.seq_lens = block_table, seq_lens
+        nb = latent.shape[0]
+        if rope is None:
+            ld = _dtype_code(latent)
+            row = latent.shape[2]
+            self.kv = MlaPagedKV(latent.data_ptr(), ld, BLOCK * row, row,
+                                 latent.data_ptr() + D_LATENT * latent.element_size(), ld, BLOCK * row, row,
+                                 None, 0, BLOCK, nb, block_table.shape[1],
+                                 block_table.data_ptr(), seq_lens.data_ptr())
+        else:
+            self.kv = MlaPagedKV(latent.data_ptr(), MLA_FP8_E4M3, BLOCK * D_LATENT, D_LATENT,
+                                 rope.data_ptr(), _dtype_code(rope), BLOCK * D_ROPE, D_ROPE,
+                                 _ptr(scale), BLOCK, BLOCK, nb, block_table.shape[1],
+                                 block_table.data_ptr(), seq_lens.data_ptr())
+
+
+def mla_absorb_q(dims: MlaDims, q_nope, w_uk, q_lat, stream=None):
+    """q_lat[r][h][:] = W_UK[h]^T q_nope[r][h][:]."""
+    _check("mla_absorb_q", _lib.mla_absorb_q(ctypes.byref(dims), _ptr(q_nope), _ptr(w_uk), _dtype_code(q_nope),
+                                             _ptr(q_lat), _dtype_code(q_lat), _stream(stream)))
+
+
+def mla_decode(dims: MlaDims, q_lat, q_rope, cache: PagedCache, num_splits: int, o, lse, stream=None):
+    """Decode attention over the paged latent cache; o/lse are o_lat/lse
+    (num_splits == 1) or the per-chunk partials (num_splits > 1)."""
+    _check("mla_decode", _lib.mla_decode(ctypes.byref(dims), _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat),
+                                         ctypes.byref(cache.kv), int(num_splits), _ptr(o), _ptr(lse),
+                                         _stream(stream)))
+
+
+def mla_split_combine(dims: MlaDims, num_splits: int, o_part, lse_part, o_lat, lse=None, stream=None):
+    _check("mla_split_combine", _lib.mla_split_combine(ctypes.byref(dims), int(num_splits), _ptr(o_part),
+                                                       _ptr(lse_part), _ptr(o_lat), _ptr(lse), _stream(stream)))
+
+
+def mla_out_uv(dims: MlaDims, o_lat, w_uv, out, stream=None):
+    """out[r][h][:] = W_UV[h] o_lat[r][h][:]."""
+    _check("mla_out_uv", _lib.mla_out_uv(ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _dtype_code(w_uv),
+                                         _ptr(out), _stream(stream)))
+
+
+def mla_decode_num_splits(dims: MlaDims, max_seq_len: int) -> int:
+    out = ctypes.c_int32(0)
+    _check("mla_decode_num_splits", _lib.mla_decode_num_splits(ctypes.byref(dims), int(max_seq_len),
+                                                               ctypes.byref(out)))
+    return int(out.value)

@@ -1,0 +1,233 @@
+// Host entry points of the C ABI declared in include/mla.h: argument
+// validation (before any launch), kernel selection and launch on the
+// caller's stream.  The library allocates nothing and keeps no state.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "mla.h"
+#include "mla_kernels.h"
+
+namespace {
+
+constexpr int kDL = 512, kDR = 64, kDH = 128, kBlock = 64;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_size(int32_t dt) {
+  switch (dt) {
+    case MLA_F32: return 4;
+    case MLA_BF16: return 2;
+    case MLA_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+int check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->batch < 0 || d->heads < 1 || d->heads > 1024 || d->q_per_seq < 1 || d->q_per_seq > 2)
+    return MLA_ERR_SHAPE;
+  if (d->d_latent != kDL || d->d_rope != kDR || d->d_head != kDH) return MLA_ERR_SHAPE;
+  if (!isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+  // row counts must fit 32-bit index arithmetic in the kernels
+  if ((int64_t)d->batch * d->q_per_seq * d->heads > (1 << 24)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+// Launch through hipLaunchKernel so the status returned is this launch's own
+// (hipGetLastError would also report errors left by unrelated earlier calls).
+// With MLA_VERBOSE set in the environment a refused launch prints the HIP error.
+template <typename Args>
+int launch(const char* name, const void* kernel, dim3 grid, dim3 block, const Args& a, hipStream_t s) {
+  void* argv[] = {(void*)&a};
+  const hipError_t e = hipLaunchKernel(kernel, grid, block, argv, 0, s);
+  if (e == hipSuccess) return MLA_OK;
+  if (getenv("MLA_VERBOSE"))
+    fprintf(stderr, "mla: launch of %s (grid %u,%u,%u block %u) failed: %s\n", name, grid.x, grid.y, grid.z,
+            block.x, hipGetErrorString(e));
+  return MLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is out of range or unsupported";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unsupported dtype or dtype combination";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: a pointer or stride is not 16-byte aligned";
+    case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_splits out of range";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: the HIP runtime refused the launch";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable device";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int32_t in_dtype,
+                 void* q_lat, int32_t q_lat_dtype, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;
+  if ((in_dtype != MLA_F32 && in_dtype != MLA_BF16) || (q_lat_dtype != MLA_F32 && q_lat_dtype != MLA_BF16))
+    return MLA_ERR_DTYPE;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat)) return MLA_ERR_ALIGN;
+  const int rows = dims->batch * dims->q_per_seq;
+  if (rows == 0) return MLA_OK;
+  mla::AbsorbArgs a{q_nope, w_uk, q_lat, rows, dims->heads};
+  hipStream_t s = (hipStream_t)stream;
+  if (in_dtype == MLA_BF16) {
+    dim3 grid(dims->heads, kDL / 64);
+    if (q_lat_dtype == MLA_BF16)
+      st = launch("mla::absorb_q_mfma<true>", (const void*)mla::absorb_q_mfma<true>, grid, dim3(256), a, s);
+    else
+      st = launch("mla::absorb_q_mfma<false>", (const void*)mla::absorb_q_mfma<false>, grid, dim3(256), a, s);
+  } else {
+    dim3 grid(dims->heads, kDL / 256, rows);
+    if (rows > 65535) return MLA_ERR_SHAPE;
+    if (q_lat_dtype == MLA_BF16)
+      st = launch("mla::absorb_q_f32<true>", (const void*)mla::absorb_q_f32<true>, grid, dim3(256), a, s);
+    else
+      st = launch("mla::absorb_q_f32<false>", (const void*)mla::absorb_q_f32<false>, grid, dim3(256), a, s);
+  }
+  return st;
+}
+
+int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int32_t q_dtype,
+               const mla_paged_kv* kv, int32_t num_splits, float* o, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!kv || !q_lat || !q_rope || !o || !lse) return MLA_ERR_NULL;
+  if (!kv->latent || !kv->rope || !kv->block_table || !kv->seq_lens) return MLA_ERR_NULL;
+  if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
+  if (kv->block_size != kBlock || kv->num_blocks < 1 || kv->max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  const int32_t ld = kv->latent_dtype, rd = kv->rope_dtype;
+  int fmt;  // 0 = f32, 1 = bf16, 2 = fp8
+  if (q_dtype == MLA_F32 && ld == MLA_F32 && rd == MLA_F32) fmt = 0;
+  else if (q_dtype == MLA_BF16 && ld == MLA_BF16 && rd == MLA_BF16) fmt = 1;
+  else if (q_dtype == MLA_BF16 && ld == MLA_FP8_E4M3 && rd == MLA_BF16) fmt = 2;
+  else return MLA_ERR_DTYPE;
+  if (fmt == 2 && !kv->scale) return MLA_ERR_NULL;
+  if (fmt != 2 && kv->scale) return MLA_ERR_DTYPE;
+  if (kv->latent_row_stride < kDL || kv->rope_row_stride < kDR || kv->latent_block_stride < 0 ||
+      kv->rope_block_stride < 0 || (fmt == 2 && kv->scale_block_stride < kBlock))
+    return MLA_ERR_SHAPE;
+  const int64_t les = elem_size(ld), res = elem_size(rd);
+  const int64_t lat_rs = kv->latent_row_stride * les, lat_bs = kv->latent_block_stride * les;
+  const int64_t rope_rs = kv->rope_row_stride * res, rope_bs = kv->rope_block_stride * res;
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(o) || !aligned16(kv->latent) ||
+      !aligned16(kv->rope) || (lat_rs & 15) || (lat_bs & 15) || (rope_rs & 15) || (rope_bs & 15) ||
+      (fmt == 2 && ((uintptr_t)kv->scale & 3)))
+    return MLA_ERR_ALIGN;
+  const int rows = dims->q_per_seq * dims->heads;
+  if (dims->batch == 0) return MLA_OK;
+  const int64_t units = (int64_t)dims->batch * num_splits;
+  if (units > (1 << 24)) return MLA_ERR_SHAPE;
+
+  mla::DecodeArgs a;
+  a.q_lat = (const uint16_t*)q_lat;
+  a.q_rope = (const uint16_t*)q_rope;
+  a.latent = (const uint8_t*)kv->latent;
+  a.rope = (const uint8_t*)kv->rope;
+  a.kv_scale_bytes = (const uint8_t*)kv->scale;
+  a.lat_bs = lat_bs;
+  a.lat_rs = lat_rs;
+  a.rope_bs = rope_bs;
+  a.rope_rs = rope_rs;
+  a.scale_bs = (int64_t)kv->scale_block_stride * 4;
+  a.block_table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.batch = dims->batch;
+  a.sq = dims->q_per_seq;
+  a.heads = dims->heads;
+  a.rows = rows;
+  a.row_blocks = (rows + mla::kDecodeRowsPerWg - 1) / mla::kDecodeRowsPerWg;
+  a.num_splits = num_splits;
+  a.units = (int)units;
+  a.max_blocks = kv->max_blocks_per_seq;
+  a.softmax_scale = dims->softmax_scale;
+  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == 1) {
+    const int64_t padded = (units + 7) / 8 * 8;
+    const int64_t grid = padded * a.row_blocks;
+    if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
+    st = launch("mla::decode_mfma_bf16", (const void*)mla::decode_mfma_bf16, dim3((unsigned)grid), dim3(256), a, s);
+  } else {
+    const int64_t grid = units * rows;
+    if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
+    if (fmt == 0)
+      st = launch("mla::decode_scalar<0>", (const void*)mla::decode_scalar<0>, dim3((unsigned)grid), dim3(256), a, s);
+    else
+      st = launch("mla::decode_scalar<2>", (const void*)mla::decode_scalar<2>, dim3((unsigned)grid), dim3(256), a, s);
+  }
+  return st;
+}
+
+int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
+                      float* o_lat, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!o_part || !lse_part || !o_lat) return MLA_ERR_NULL;
+  if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
+  if (!aligned16(o_part) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
+  const int rows = dims->q_per_seq * dims->heads;
+  const int64_t grid = (int64_t)dims->batch * rows;
+  if (grid == 0) return MLA_OK;
+  mla::CombineArgs a{o_part, lse_part, o_lat, lse, dims->batch, num_splits, rows};
+  st = launch("mla::split_combine", (const void*)mla::split_combine, dim3((unsigned)grid), dim3(128), a, (hipStream_t)stream);
+  return st;
+}
+
+int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32_t w_dtype, float* out,
+               void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (w_dtype != MLA_F32 && w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  const int rows = dims->batch * dims->q_per_seq;
+  if (rows == 0) return MLA_OK;
+  mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads};
+  hipStream_t s = (hipStream_t)stream;
+  if (w_dtype == MLA_BF16) {
+    st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3(dims->heads, kDH / 64), dim3(256), a, s);
+  } else {
+    if (rows > 65535) return MLA_ERR_SHAPE;
+    st = launch("mla::out_uv_f32", (const void*)mla::out_uv_f32, dim3(dims->heads, rows), dim3(128), a, s);
+  }
+  return st;
+}
+
+int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!num_splits) return MLA_ERR_NULL;
+  if (max_seq_len < 0) return MLA_ERR_SHAPE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return MLA_ERR_DEVICE;
+  const int rows = dims->q_per_seq * dims->heads;
+  const int64_t per_split = (int64_t)(dims->batch > 0 ? dims->batch : 1) *
+                            ((rows + mla::kDecodeRowsPerWg - 1) / mla::kDecodeRowsPerWg);
+  const int pages = (max_seq_len + kBlock - 1) / kBlock;
+  int64_t ns = (cus + per_split - 1) / per_split;
+  // keep at least 4 pages (256 tokens) per chunk so each workgroup streams enough
+  const int64_t max_ns = pages / 4 > 0 ? pages / 4 : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns > MLA_MAX_SPLITS) ns = MLA_MAX_SPLITS;
+  if (ns < 1) ns = 1;
+  *num_splits = (int32_t)ns;
+  return MLA_OK;
+}
+
+}  // extern "C"

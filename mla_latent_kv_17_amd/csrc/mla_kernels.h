@@ -1,0 +1,59 @@
+// Kernel argument blocks and kernel declarations shared by the host entry
+// points and the kernel sources.  Strides inside these blocks are in BYTES.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeArgs {
+  const uint16_t* q_lat;   // [B*S_q][H][512]  bf16 bits (fp32 for the f32 path)
+  const uint16_t* q_rope;  // [B*S_q][H][64]
+  const uint8_t* latent;   // cache latent rows
+  const uint8_t* rope;     // cache RoPE-key rows
+  const uint8_t* kv_scale_bytes;  // fp8 per-token scales (fp32)
+  int64_t lat_bs, lat_rs, rope_bs, rope_rs, scale_bs;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* o;    // o_lat [slot][rows][512], slot = b * num_splits + split
+  float* lse;  // [slot][rows]
+  int batch, sq, heads, rows, row_blocks, num_splits, units, max_blocks;
+  float softmax_scale, scale_log2;
+};
+
+__global__ void decode_mfma_bf16(const DecodeArgs a);
+constexpr int kDecodeRowsPerWg = 64;
+template <int kFmt>
+__global__ void decode_scalar(const DecodeArgs a);
+
+struct AbsorbArgs {
+  const void* q_nope;  // [R][H][128]
+  const void* w;       // [H][128][512]
+  void* q_lat;         // [R][H][512]
+  int rows, heads;     // rows = B * S_q
+};
+template <bool kOutBf16>
+__global__ void absorb_q_mfma(const AbsorbArgs a);   // bf16 inputs
+template <bool kOutBf16>
+__global__ void absorb_q_f32(const AbsorbArgs a);    // fp32 inputs
+
+struct CombineArgs {
+  const float* o_part;    // [B][ns][S_q][H][512]
+  const float* lse_part;  // [B][ns][S_q][H]
+  float* o_lat;           // [B*S_q][H][512]
+  float* lse;             // [B*S_q][H] or null
+  int batch, num_splits, rows;  // rows = S_q * H
+};
+__global__ void split_combine(const CombineArgs a);
+
+struct OutUvArgs {
+  const float* o_lat;  // [R][H][512]
+  const void* w;       // [H][128][512]
+  float* out;          // [R][H][128]
+  int rows, heads;
+};
+__global__ void out_uv_mfma(const OutUvArgs a);  // bf16 weights, hi/lo split of o_lat
+__global__ void out_uv_f32(const OutUvArgs a);   // fp32 weights
+
+}  // namespace mla

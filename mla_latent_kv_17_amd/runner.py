@@ -1,0 +1,112 @@
+"""Drive the four library calls for one decode step on torch device tensors.
+
+    absorb:  q_lat = W_UK^T q_nope              (mla_absorb_q)
+    decode:  o_lat, lse over the paged cache     (mla_decode)
+    merge:   log-sum-exp merge of KV chunks      (mla_split_combine, num_splits > 1)
+    output:  o = W_UV o_lat                      (mla_out_uv)
+
+Host-side plumbing only: uploads arrays, allocates outputs and the split-KV
+workspace with torch, and calls the binding.  Inputs are any object with the
+fields of a generated workload (numpy arrays in storage format).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (PagedCache, make_dims, mla_absorb_q, mla_decode, mla_decode_num_splits,
+               mla_out_uv, mla_split_combine)
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _dev(x: np.ndarray, kind: str, device):
+    """Upload a storage-format numpy array (bf16 as uint16 bits, fp8 as uint8)."""
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if kind == "bf16":
+        t = t.view(torch.int16).view(torch.bfloat16)
+    elif kind == "fp8":
+        t = t.view(torch.uint8)
+    return t.to(device)
+
+
+class DeviceInputs:
+    def __init__(self, inp, device="cuda"):
+        wl = inp.wl
+        self.wl = wl
+        self.batch, self.q_per_seq, self.heads = wl.batch, wl.q_per_seq, wl.heads
+        self.softmax_scale = inp.softmax_scale
+        self.seq_lens_host = np.asarray(inp.seq_lens)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(inp.block_table)).to(device)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(inp.seq_lens)).to(device)
+        if wl.cache_dtype == "fp8":
+            latent = _dev(inp.latent, "fp8", device)
+            rope = _dev(inp.rope, "bf16", device)
+            scale = torch.from_numpy(np.ascontiguousarray(inp.scale)).to(device)
+            self.cache = PagedCache(latent, self.block_table, self.seq_lens, rope=rope, scale=scale)
+        else:
+            latent = _dev(inp.latent, wl.cache_dtype, device)
+            self.cache = PagedCache(latent, self.block_table, self.seq_lens)
+        self.q_nope = _dev(inp.q_nope, wl.q_dtype, device)
+        self.q_rope = _dev(inp.q_rope, wl.q_dtype, device)
+        self.w_uk = _dev(inp.w_uk, wl.w_dtype, device)
+        self.w_uv = _dev(inp.w_uv, wl.w_dtype, device)
+        self.q_dtype = _TORCH[wl.q_dtype]
+        self.dims = make_dims(self.batch, self.q_per_seq, self.heads, self.softmax_scale)
+
+    @property
+    def cache_bytes(self) -> int:
+        c = self.cache
+        n = c.latent.numel() * c.latent.element_size()
+        if c.rope is not None:
+            n += c.rope.numel() * c.rope.element_size() + c.scale.numel() * 4
+        return n
+
+
+class DecodeStep:
+    """Owns the outputs and the split workspace of one decode step."""
+
+    def __init__(self, dev: DeviceInputs, num_splits: int = 0):
+        self.dev = dev
+        if num_splits <= 0:
+            num_splits = mla_decode_num_splits(dev.dims, int(dev.seq_lens_host.max(initial=0)))
+        self.num_splits = num_splits
+        R = dev.batch * dev.q_per_seq
+        H = dev.heads
+        device = dev.q_nope.device
+        self.q_lat = torch.empty((R, H, 512), dtype=dev.q_dtype, device=device)
+        self.o_lat = torch.empty((R, H, 512), dtype=torch.float32, device=device)
+        self.lse = torch.empty((R, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((R, H, 128), dtype=torch.float32, device=device)
+        if num_splits > 1:
+            self.o_part = torch.empty((dev.batch, num_splits, dev.q_per_seq, H, 512), dtype=torch.float32,
+                                      device=device)
+            self.lse_part = torch.empty((dev.batch, num_splits, dev.q_per_seq, H), dtype=torch.float32,
+                                        device=device)
+        else:
+            self.o_part = self.lse_part = None
+
+    def absorb(self, stream=None):
+        mla_absorb_q(self.dev.dims, self.dev.q_nope, self.dev.w_uk, self.q_lat, stream)
+
+    def decode(self, stream=None):
+        d = self.dev
+        if self.num_splits > 1:
+            mla_decode(d.dims, self.q_lat, d.q_rope, d.cache, self.num_splits, self.o_part, self.lse_part, stream)
+        else:
+            mla_decode(d.dims, self.q_lat, d.q_rope, d.cache, 1, self.o_lat, self.lse, stream)
+
+    def combine(self, stream=None):
+        if self.num_splits > 1:
+            mla_split_combine(self.dev.dims, self.num_splits, self.o_part, self.lse_part, self.o_lat, self.lse,
+                              stream)
+
+    def project(self, stream=None):
+        mla_out_uv(self.dev.dims, self.o_lat, self.dev.w_uv, self.out, stream)
+
+    def run(self, stream=None):
+        self.absorb(stream)
+        self.decode(stream)
+        self.combine(stream)
+        self.project(stream)
+        return self.out

@@ -8,3 +8,14 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+
+
+def _ensure_built():
+    """Build the HIP library in-tree when nothing is built yet."""
+    lib = os.path.join(ROOT, "mla_latent_kv_17_amd", "libmla.so")
+    if not os.path.exists(lib):
+        from mla_latent_kv_17_amd.build import build
+        build()
+
+
+_ensure_built()

@@ -1,0 +1,85 @@
+"""The C-ABI library loads and exports what include/mla.h declares, and host
+validation rejects bad calls with the documented status before any launch
+(no GPU needed: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_17_amd as M
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mla.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    syms = declared_symbols()
+    assert len(syms) == 7, syms
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(M.EXPORTS) == syms
+
+
+def test_version_and_status_strings():
+    assert M.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert M.status_str(code).startswith("MLA_")
+    assert "UNKNOWN" in M.status_str(-99)
+
+
+def _call_decode(dims, kv, ns=1, q=0x1000, qr=0x2000, o=0x3000, lse=0x4000, qdt=M.MLA_BF16):
+    return M._lib.mla_decode(ctypes.byref(dims), q, qr, qdt, ctypes.byref(kv) if kv is not None else None,
+                             ns, o, lse, None)
+
+
+def _kv(latent=0x10000, rope=0x10000 + 1024, ldt=M.MLA_BF16, rdt=M.MLA_BF16, scale=None, bs=64):
+    return M.MlaPagedKV(latent, ldt, 64 * 576, 576, rope, rdt, 64 * 576, 576, scale, 64 if scale else 0,
+                        bs, 10, 4, 0x20000, 0x30000)
+
+
+def test_decode_validation():
+    d = M.make_dims(2, 1, 128)
+    assert _call_decode(d, None) == M.MLA_ERR_NULL
+    assert _call_decode(d, _kv(), q=0) == M.MLA_ERR_NULL
+    assert _call_decode(d, _kv(), ns=0) == M.MLA_ERR_SPLITS
+    assert _call_decode(d, _kv(), ns=M.MLA_MAX_SPLITS + 1) == M.MLA_ERR_SPLITS
+    assert _call_decode(d, _kv(bs=32)) == M.MLA_ERR_SHAPE
+    assert _call_decode(d, _kv(), qdt=M.MLA_F32) == M.MLA_ERR_DTYPE
+    assert _call_decode(d, _kv(ldt=M.MLA_FP8_E4M3)) == M.MLA_ERR_NULL           # fp8 needs a scale
+    assert _call_decode(d, _kv(scale=0x50000)) == M.MLA_ERR_DTYPE               # scale only with fp8
+    assert _call_decode(d, _kv(latent=0x10008)) == M.MLA_ERR_ALIGN
+    assert _call_decode(d, _kv(), q=0x1004) == M.MLA_ERR_ALIGN
+    bad = M.make_dims(2, 3, 128)
+    assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
+    bad = M.MlaDims(2, 1, 128, 256, 64, 128, 0.1)
+    assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
+    bad = M.MlaDims(2, 1, 128, 512, 64, 128, float("nan"))
+    assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
+    bad = M.make_dims(2, 1, 0)
+    assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
+    # batch 0: nothing to do, nothing launched
+    assert _call_decode(M.make_dims(0, 1, 128), _kv()) == M.MLA_OK
+
+
+def test_other_entry_points_validation():
+    d = M.make_dims(2, 1, 128)
+    L = M._lib
+    assert L.mla_absorb_q(ctypes.byref(d), None, 0x1000, M.MLA_BF16, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_NULL
+    assert L.mla_absorb_q(ctypes.byref(d), 0x1000, 0x1000, M.MLA_FP8_E4M3, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_DTYPE
+    assert L.mla_absorb_q(ctypes.byref(d), 0x1002, 0x1000, M.MLA_BF16, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_ALIGN
+    assert L.mla_absorb_q(None, 0x1000, 0x1000, M.MLA_BF16, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_NULL
+    assert L.mla_split_combine(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, None, None) == M.MLA_ERR_SPLITS
+    assert L.mla_split_combine(ctypes.byref(d), 4, None, 0x2000, 0x3000, None, None) == M.MLA_ERR_NULL
+    assert L.mla_split_combine(ctypes.byref(d), 4, 0x1004, 0x2000, 0x3000, None, None) == M.MLA_ERR_ALIGN
+    assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_FP8_E4M3, 0x3000, None) == M.MLA_ERR_DTYPE
+    assert L.mla_out_uv(ctypes.byref(d), None, 0x2000, M.MLA_BF16, 0x3000, None) == M.MLA_ERR_NULL
+    out = ctypes.c_int32(0)
+    assert L.mla_decode_num_splits(ctypes.byref(d), 100, None) == M.MLA_ERR_NULL
+    assert L.mla_decode_num_splits(ctypes.byref(d), -1, ctypes.byref(out)) == M.MLA_ERR_SHAPE
