@@ -1,0 +1,200 @@
+"""Benchmark: MLA absorbed decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole decode path for one batch: mla_absorb_q, mla_decode,
+mla_split_combine (when the context is split) and mla_out_uv, on the
+synthetic workload B=32, H=128, T=4096, bf16 cache/queries/weights
+(d_latent 512, d_rope 64, d_head 128), inputs resident in HBM.
+
+Before every timed step an untimed read of a 1 GiB buffer evicts the 256 MB
+Infinity Cache and the L2s, so the step streams its cache and weights from
+HBM as it would with other layers' data in between.  HIP events on the
+stream the library launches on (torch's current stream) time each step and
+each decode launch.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s
+METRIC = "MLA decode KV-tokens/s + achieved TB/s & TFLOP/s vs roofline (H=128,B=32,T=4K)"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_bf16_b32_h128_t4k_counters.json")
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "mla_device.h", "mla_kernels.h"):
+        h.update(open(os.path.join(ROOT, "mla_latent_kv_17_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None when the decode kernel source changed since they were taken."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("decode_source_hash") != decode_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the fp64 oracle (explicit K/V reconstruction) on the first
+    (sequence, head) rows of the same workload until `budget_s` elapses."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    wl = inp.wl
+    done = []
+    t0 = time.perf_counter()
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            O.explicit_decode(inp, select=[(b, i, h) for i in range(wl.q_per_seq)])
+            done.append((b, h))
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    # a (sequence, head) row covers len_b KV tokens for one of H heads
+    kv_equiv = sum(int(inp.seq_lens[b]) for b, _ in done) / wl.heads
+    return {"value": kv_equiv / el, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} (sequence, head) rows of {wl.name} ({wl.batch * wl.heads} in a step), "
+                      f"explicit fp64 K/V reconstruction, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_b32_h128_t4k")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(batch sharding needs no exchange and is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mla_inputs as MI
+    from mla_latent_kv_17_amd.runner import DecodeStep, DeviceInputs
+
+    wl = MI.WORKLOADS[args.workload]
+    print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
+    inp = MI.generate(wl)
+    dev = DeviceInputs(inp)
+    step = DecodeStep(dev, args.num_splits if args.num_splits > 0 else wl.num_splits)
+    kv_tokens = int(inp.seq_lens.astype(np.int64).sum())
+    rows = wl.q_per_seq * wl.heads
+    per_tok = MI.cache_bytes_per_token(wl.cache_dtype)
+    cache_bytes = kv_tokens * per_tok
+    # score (2*576) + value (2*512) flops per (query row, visible token)
+    pairs = sum(max(0, int(L) - (wl.q_per_seq - 1 - i)) for L in inp.seq_lens for i in range(wl.q_per_seq))
+    decode_flops = pairs * wl.heads * 2 * (576 + 512)
+    proj_flops = 2 * (wl.batch * wl.q_per_seq) * wl.heads * 2 * 128 * 512
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush.fill_(1.0)
+
+    def do_flush():
+        torch.sum(flush)
+
+    for _ in range(args.warmup):
+        do_flush()
+        step.run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        do_flush()
+        e0, e1, e2, e3 = ev[i]
+        e0.record()
+        step.absorb()
+        e1.record()
+        step.decode()
+        e2.record()
+        step.combine()
+        step.project()
+        e3.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    # warm (no eviction between steps): context only, never the headline
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    for _ in range(K):
+        step.run()
+    w1.record()
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+
+    ms_per_step = float(step_ms.mean())
+    dec_avg = float(dec_ms.mean())
+    achieved = cache_bytes / (dec_avg * 1e-3)
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": kv_tokens / (ms_per_step * 1e-3),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.cache_dtype != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) cache and queries, weights N(0, std 1/sqrt(512)))",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": int(inp.seq_lens.max()),
+                   "q_per_seq": wl.q_per_seq, "heads": wl.heads, "d_latent": 512, "d_rope": 64, "d_head": 128,
+                   "block_size": 64, "cache_dtype": wl.cache_dtype, "num_splits": step.num_splits,
+                   "steps_timed": "absorb_q + decode + split_combine + out_uv, caches evicted before each"},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": traffic,
+                     "kernel": "decode_mfma_bf16", "launch_ms": dec_avg,
+                     "algorithmic_bytes": cache_bytes},
+        "decode_tflops": decode_flops / (dec_avg * 1e-3) / 1e12,
+        "decode_mfma_frac": decode_flops / (dec_avg * 1e-3) / MFMA_BF16_PEAK,
+        "kv_tokens_per_step": kv_tokens,
+        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "decode_ms_p10_p50_p90": [float(np.percentile(dec_ms, q)) for q in (10, 50, 90)],
+        "step_tflops": (decode_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
+        "warm_ms_per_step": warm_ms,
+        "wall_s_timed_loop_incl_eviction": wall,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"]["cpu"] = platform.processor() or platform.machine()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

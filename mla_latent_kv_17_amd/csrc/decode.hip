@@ -27,6 +27,8 @@
 //        element is read from LDS once per workgroup for this product.
 //  * decode_scalar (fp32 cache, and any dtype as a plain second path):
 //    one workgroup per (sequence, chunk, query row), fp32 VALU.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -60,15 +62,56 @@ __device__ __forceinline__ int rope_off(int r, int q) { return kLatBytes + (r * 
 
 __device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) { return (uint32_t)(size_t)p; }
 
-// Wave-wide HBM -> LDS copy of `bytes` (16 or 4) per lane: lane i's data
-// lands at lds_base + bytes * i.  Issued through asm so the compiler does not
-// turn every later LDS read into a wait for all outstanding copies;
-// completion is tracked with explicit s_waitcnt vmcnt.
+// Wave-wide HBM -> LDS copy of 16 bytes per lane: lane i's data lands at
+// lds_base + 16 * i (the base travels in M0, which is saved and restored so
+// the compiler's own use of M0 is untouched; one wait state separates the M0
+// write from the load that reads it).  Issued through asm so that the
+// compiler does not turn later LDS reads into waits for every outstanding
+// copy; completion is tracked with explicit s_waitcnt vmcnt.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "s"(lds_base) : "memory", "m0");
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" :: "v"(src), "s"(lds_base) : "memory", "m0");
+
+// Same copy with a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
+// byte offset (no per-lane address arithmetic).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  // readfirstlane returns int: widen each half through uint32_t (a sign
+  // extension of the low half would overwrite the high half of the address)
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  base = (const void*)(((uint64_t)hi << 32) | (uint64_t)lo);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+// A wait the compiler sees (it updates its own counter model): all vector
+// memory loads issued so far have completed.
+__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scalar (constant address space) load of a wave-uniform int: tracked by
+// lgkmcnt, so it never waits on the outstanding HBM -> LDS copies.
+__device__ __forceinline__ int load_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
 template <int N>
@@ -111,9 +154,9 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
 }  // namespace
 
 // bf16 cache.  Workgroup = 4 waves = one (sequence, KV chunk, block of 64
-// query rows).  The context is walked in 64-token steps (two 32-token tiles).
-// Wave w: score rows 32*(w&1) .. +31 over the step's token half (w>>1), and
-// value columns 128*w .. +127 for all 64 rows.
+// query rows).  The context is walked in 64-token steps (two 32-token tiles
+// = one cache page).  Wave w: score rows 32*(w&1) .. +31 over the step's token
+// half (w>>1), and value columns 128*w .. +127 for all 64 rows.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_mfma_bf16(const DecodeArgs a) {
   constexpr int kBuf = 4;                       // tile ring = 2 steps
@@ -121,16 +164,15 @@ decode_mfma_bf16(const DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kBuf * kTileBytes + kPBytes + 1024];
   MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)&smem[0];
   MLA_LDS uint8_t* const pl = tiles + kBuf * kTileBytes;
-  MLA_LDS float* const mx_lds = (MLA_LDS float*)(pl + kPBytes);   // [2 halves][64 rows]
-  MLA_LDS float* const m_lds = mx_lds + 128;                       // [64]
-  MLA_LDS float* const l_lds = m_lds + 64;                         // [64]
-  MLA_LDS int* const ovf_lds = (MLA_LDS int*)(l_lds + 64);         // [4]
+  MLA_LDS float* const xm = (MLA_LDS float*)(pl + kPBytes);   // [2 halves][64 rows] maxima
+  MLA_LDS float* const xl = xm + 128;                         // [64] row sums
+  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 64);            // [4] overflow flags
 
   Work wk;
   if (!decode_work(a, wk)) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int g = lane >> 5;      // k-half of an MFMA operand
   const int n32 = lane & 31;
@@ -141,6 +183,52 @@ decode_mfma_bf16(const DecodeArgs a) {
   const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
   const int ntiles = wk.ntiles;
   const int nsteps = (ntiles + 1) >> 1;
+  const uint32_t tiles_lds = lds_addr(tiles);
+
+  // ---- HBM -> LDS copies of one 32-token tile: 9 instructions per wave.
+  // A step's two tiles are the halves of one 64-token page, so one block id
+  // serves both; ids are fetched a step ahead with scalar loads.
+  const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
+  auto page_block = [&](int st) -> int {
+    return 2 * st < ntiles ? load_uniform(a.block_table, bt_row + (wk.tok0 >> 6) + st) : 0;
+  };
+  // RoPE part: rows wave*8 + lane/8, 8 chunks each (lane part of the address)
+  const int rope_r = wave * 8 + (lane >> 3);
+  const uint32_t rope_lane = (uint32_t)((lane >> 3) * a.rope_rs) + ((((lane & 7) ^ s8(rope_r))) << 4);
+  auto issue_tile = [&](int t, int blk) {
+    const int tt = wk.tok0 + t * kTileTok;
+    const int r0 = (tt & 63) + wave * 8;
+    const uint32_t tl = tiles_lds + (t % kBuf) * kTileBytes;
+    const uint8_t* rp = a.latent + blk * a.lat_bs + (int64_t)r0 * a.lat_rs;
+    const uint8_t* rr = a.rope + blk * a.rope_bs + (int64_t)r0 * a.rope_rs;
+    const int valid_rows = wk.len - tt - wave * 8;  // rows j < valid_rows hold tokens
+    if (valid_rows >= 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sw = ((j & 3) << 2) | ((2 * wave + (j >> 2)) & 3);  // s16(wave*8 + j)
+        dma16s(rp + (int64_t)j * a.lat_rs, (uint32_t)(lane ^ sw) << 4, tl + (wave * 8 + j) * 1024);
+      }
+      dma16s(rr, rope_lane, tl + kLatBytes + wave * 1024);
+    } else {  // last page of the sequence: rows past its length read zeros
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sw = ((j & 3) << 2) | ((2 * wave + (j >> 2)) & 3);
+        if (j < valid_rows)
+          dma16s(rp + (int64_t)j * a.lat_rs, (uint32_t)(lane ^ sw) << 4, tl + (wave * 8 + j) * 1024);
+        else
+          dma16s(g_zero_row, (uint32_t)lane << 4, tl + (wave * 8 + j) * 1024);
+      }
+      const uint8_t* src = (lane >> 3) < valid_rows ? rr + rope_lane : (const uint8_t*)g_zero_row + (lane << 4);
+      dma16(src, tl + kLatBytes + wave * 1024);
+    }
+  };
+  auto issue_step = [&](int st, int blk) {
+    if (2 * st < ntiles) issue_tile(2 * st, blk);
+    if (2 * st + 1 < ntiles) issue_tile(2 * st + 1, blk);
+  };
+
+  // first pass: the copies of step 0 overlap the query loads
+  issue_step(0, page_block(0));
 
   // ---- queries of rows row_base + 32*rg + n32: B operand of the score product
   const int qrow = row_base + rg * 32 + n32;
@@ -157,189 +245,187 @@ decode_mfma_bf16(const DecodeArgs a) {
     if (!qvalid)
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) qf[kb] = as_bf16x8(u32x4{0, 0, 0, 0});
+    // the query loads (and the step-0 copies) complete here, where the
+    // compiler sees it, so it never waits on later copies when Q is used
+    wait_all_vmem();
   }
-  // a row's query sees tokens < nvis; the chunk ends at tok1
+  // a row's query sees tokens < its horizon; the chunk ends at tok1
   const int qi = qvalid ? qrow / a.heads : 0;
   const int hi_tok = min(wk.tok1, qvalid ? wk.len - (a.sq - 1 - qi) : 0);
   const int hi_min = min(wk.tok1, wk.len - (a.sq - 1));
 
-  // ---- HBM -> LDS copies of one 32-token tile: 9 instructions per wave
-  const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
-  auto issue_tile = [&](int t) {
-    const int tt = wk.tok0 + t * kTileTok;
-    const int blk = a.block_table[bt_row + (tt >> 6)];
-    const int r0 = tt & 63;
-    MLA_LDS uint8_t* tb = tiles + (t % kBuf) * kTileBytes;
-    const uint8_t* lat_blk = a.latent + blk * a.lat_bs + r0 * a.lat_rs;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = wave * 8 + j;
-      const uint8_t* src = (tt + r < wk.len) ? lat_blk + r * a.lat_rs + ((lane ^ s16(r)) << 4)
-                                             : (const uint8_t*)g_zero_row + (lane << 4);
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(tb + r * 1024)));
-    }
-    const int r = wave * 8 + (lane >> 3);
-    const int q = (lane & 7) ^ s8(r);
-    const uint8_t* src = (tt + r < wk.len) ? a.rope + blk * a.rope_bs + (r0 + r) * a.rope_rs + (q << 4)
-                                           : (const uint8_t*)g_zero_row + (lane << 4);
-    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(tb + kLatBytes + wave * 1024)));
-  };
-  auto issue_step = [&](int st) {
-    if (2 * st < ntiles) issue_tile(2 * st);
-    if (2 * st + 1 < ntiles) issue_tile(2 * st + 1);
-  };
-
-  // ---- accumulators.  A row's reference max m_ref is fixed at its first
-  // finite step maximum, so P and O never need rescaling; if a later score
-  // exceeds it by more than 2^kRefSlack the whole chunk is recomputed with the
-  // raised reference (exact either way, and never taken unless the scores of
-  // one row span more than 44 nats).
-  f32x16 oacc[4][2];
-  float m_ref = -__builtin_inff();   // this lane's score row (log2 domain)
-  float l_part = 0.f;                // this lane's share of the row sum
-
-  const int lat_rbase = n32 * 1024;
-  const int lat_x = (16 * g) ^ (16 * s16(n32));
-  const int rope_rbase = kLatBytes + n32 * 128;
-  const int rope_x = (16 * g) ^ (16 * s8(n32));
+  // ---- per-lane LDS offsets (the tile buffer adds a constant)
+  // score operand: latent row n32, chunk 2kb+g; RoPE row n32, chunk 2(kb-32)+g
+  const uint32_t c1_lat = n32 * 1024 + th * kTileBytes;
+  const uint32_t lat_x = (16 * g) ^ (16 * s16(n32));
+  const uint32_t c1_rope = kLatBytes + n32 * 128 + th * kTileBytes;
+  const uint32_t rope_x = (16 * g) ^ (16 * s8(n32));
+  // value operand (transposing reads): token row 16hb + 8j2 + 4g + i/4, columns
+  // 128*wave + 32*mt + 16*(lane/16 % 2) + 4*(i%4), i = lane % 16
   const int i16 = lane & 15;
   const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
-  const int vbyte = (i16 & 1) * 8;
+  uint32_t voff[2][4];
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2) {
+    const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + wave * 256 + (((4 * mt) ^ vy ^ sw) << 4) + (i16 & 1) * 8;
+  }
 
-  for (;;) {  // a pass over the chunk; repeated only after a reference overflow
+  // ---- accumulators.  A row's reference max m_ref is fixed at its first
+  // finite step maximum, so P and O never need rescaling.  If a later score
+  // exceeds it by more than 2^kRefSlack the pass is finished (its values are
+  // discarded) and repeated with the row's chunk maximum as the reference:
+  // exact either way, and never taken unless the scores of one row span more
+  // than 44 nats.
+  f32x16 oacc[4][2];
+  float m_ref = -__builtin_inff();   // this lane's score row (log2 domain)
+  float m_hi = -__builtin_inff();    // largest step maximum seen this pass
+  float l_part = 0.f;                // this lane's share of the row sum
+  bool ovf = false;
+
+  auto run_step = [&](int st, int& blk_next, bool set_ref, auto parc) {
+    constexpr int par = decltype(parc)::value;  // st & 1: which half of the tile ring
+    // tiles of step st-1 are free (barrier 2 of the previous step): prefetch step st+1
+    if (st + 1 < nsteps) issue_step(st + 1, blk_next);
+    blk_next = page_block(st + 2);
+    const bool own_valid = 2 * st + th < ntiles;
+    const bool second_valid = 2 * st + 1 < ntiles;
+    const int tt = wk.tok0 + (2 * st + th) * kTileTok;
+
+    // ---- scores S^T[token][row] for this wave's token half, K = 576
+    float p[16];
+    if (own_valid) {
+      const MLA_LDS uint8_t* tb = tiles + 2 * par * kTileBytes;
+      auto ldA = [&](int kb) -> bf16x8 {
+        if (kb < 32)
+          return *(const MLA_LDS bf16x8*)(tb + c1_lat + (kb >> 3) * 256 + (((kb & 7) * 32) ^ lat_x));
+        return *(const MLA_LDS bf16x8*)(tb + c1_rope + (((kb - 32) * 32) ^ rope_x));
+      };
+      constexpr int kDepth = 8;
+      f32x16 sacc = f32x16{};
+      bf16x8 ar[kDepth];
+#pragma unroll
+      for (int kb = 0; kb < kDepth; ++kb) ar[kb] = ldA(kb);
+#pragma unroll
+      for (int kb = 0; kb < 36; ++kb) {
+        sacc = mfma32x32x16(ar[kb % kDepth], qf[kb], sacc);
+        if (kb + kDepth < 36) ar[kb % kDepth] = ldA(kb + kDepth);
+        sched_fence();
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = sacc[r] * a.scale_log2;
+      if (tt + kTileTok > hi_min) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tt + (r >> 2) * 8 + 4 * g + (r & 3);
+          if (tok >= hi_tok) p[r] = -__builtin_inff();
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = -__builtin_inff();
+    }
+    // value operand of the first 16-token block: issued now, used after barrier 1
+    auto ldV = [&](int kb, bf16x8 (&av)[4]) {
+      const MLA_LDS uint8_t* vt = tiles + (2 * par + (kb >> 1)) * kTileBytes + (kb & 1) * 16 * 1024;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
+        const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
+        av[mt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+    };
+    bf16x8 av[4];
+    ldV(0, av);
+
+    float mx = p[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, p[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (set_ref) {
+      // first step of the first pass (workgroup-uniform): the two token halves
+      // agree on each row's reference.  A row left at -inf here sees no token
+      // of this chunk at all (a row's visible tokens are a prefix of it).
+      if (lane < 32) xm[th * 64 + rg * 32 + lane] = mx;
+      wg_barrier();
+      mx = fmaxf(mx, xm[(th ^ 1) * 64 + rg * 32 + n32]);
+      m_ref = mx;
+    }
+    m_hi = fmaxf(m_hi, mx);
+    if (mx > m_ref + kRefSlack) ovf = true;
+    const float mu = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = exp2f(p[r] - mu);
+      l_part += p[r];
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const u32x4 pk = {pack_bf16x2(p[8 * hb + 0], p[8 * hb + 1]), pack_bf16x2(p[8 * hb + 2], p[8 * hb + 3]),
+                        pack_bf16x2(p[8 * hb + 4], p[8 * hb + 5]), pack_bf16x2(p[8 * hb + 6], p[8 * hb + 7])};
+      *(MLA_LDS u32x4*)(pl + ((rg * 4 + 2 * th + hb) * 64 + lane) * 16) = pk;
+    }
+    wg_barrier();  // ---- barrier 1: P visible
+
+    // ---- values: O^T[columns 128w..][64 rows] += C^T[.., 64 tokens] P^T
+    const int nkb = second_valid ? 4 : 2;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb >= nkb) break;
+      const bf16x8 b0 = *(const MLA_LDS bf16x8*)(pl + ((0 * 4 + kb) * 64 + lane) * 16);
+      const bf16x8 b1 = *(const MLA_LDS bf16x8*)(pl + ((1 * 4 + kb) * 64 + lane) * 16);
+      bf16x8 an[4];
+      if (kb + 1 < nkb) ldV(kb + 1, an);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        oacc[mt][0] = mfma32x32x16(av[mt], b0, oacc[mt][0]);
+        oacc[mt][1] = mfma32x32x16(av[mt], b1, oacc[mt][1]);
+      }
+      sched_fence();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) av[mt] = an[mt];
+    }
+    // ---- barrier 2: P may be overwritten, step st's tiles are free, step st+1 resident
+    wait_vmcnt<0>();
+    wg_barrier();
+  };
+
+  for (bool first = true;; first = false) {  // one pass; repeated only after an overflow
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) oacc[i][j] = f32x16{};
     l_part = 0.f;
-    if (tid < 4) ovf_lds[tid] = 0;
-    issue_step(0);
+    ovf = false;
+    if (!first) issue_step(0, page_block(0));
     wait_vmcnt<0>();
     wg_barrier();
 
-    bool restart = false;
-    for (int st = 0; st < nsteps; ++st) {
-      // tiles of step st-1 are free (barrier 2 of the previous step): prefetch step st+1
-      if (st + 1 < nsteps) issue_step(st + 1);
-      const int t_own = 2 * st + th;
-      const bool own_valid = t_own < ntiles;
-      const bool second_valid = 2 * st + 1 < ntiles;
-      const MLA_LDS uint8_t* tb = tiles + (t_own % kBuf) * kTileBytes;
-      const int tt = wk.tok0 + t_own * kTileTok;
-
-      // ---- scores S^T[token][row] for this wave's token half, K = 576
-      float p[16];
-      if (own_valid) {
-        auto ldA = [&](int kb) -> bf16x8 {
-          if (kb < 32) return *(const MLA_LDS bf16x8*)(tb + lat_rbase + (kb >> 3) * 256 + (((kb & 7) * 32) ^ lat_x));
-          return *(const MLA_LDS bf16x8*)(tb + rope_rbase + (((kb - 32) * 32) ^ rope_x));
-        };
-        f32x16 sacc = f32x16{};
-        bf16x8 ar[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ar[kb] = ldA(kb);
-#pragma unroll
-        for (int kb = 0; kb < 36; ++kb) {
-          sacc = mfma32x32x16(ar[kb & 3], qf[kb], sacc);
-          if (kb + 4 < 36) ar[kb & 3] = ldA(kb + 4);
-          sched_fence();
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = sacc[r] * a.scale_log2;
-        if (tt + kTileTok > hi_min) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tok = tt + (r >> 2) * 8 + 4 * g + (r & 3);
-            if (tok >= hi_tok) p[r] = -__builtin_inff();
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = -__builtin_inff();
-      }
-      float mx = p[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, p[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (lane < 32) mx_lds[th * 64 + rg * 32 + lane] = mx;
-      wg_barrier();  // ---- barrier 0: both token halves' maxima visible
-
-      mx = fmaxf(mx, mx_lds[(th ^ 1) * 64 + rg * 32 + n32]);
-      bool ovf = false;
-      if (m_ref == -__builtin_inff()) {
-        m_ref = mx;  // first visible tokens of this row: O and l are still 0
-      } else if (mx > m_ref + kRefSlack) {
-        ovf = true;
-        m_ref = mx;  // raised reference for the repeated pass
-      }
-      const float mu = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(p[r] - mu);
-        l_part += p[r];
-      }
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const u32x4 pk = {pack_bf16x2(p[8 * hb + 0], p[8 * hb + 1]), pack_bf16x2(p[8 * hb + 2], p[8 * hb + 3]),
-                          pack_bf16x2(p[8 * hb + 4], p[8 * hb + 5]), pack_bf16x2(p[8 * hb + 6], p[8 * hb + 7])};
-        *(MLA_LDS u32x4*)(pl + ((rg * 4 + 2 * th + hb) * 64 + lane) * 16) = pk;
-      }
-      if (__builtin_amdgcn_ballot_w64(ovf) && lane == 0) ovf_lds[wave] = 1;
-      wg_barrier();  // ---- barrier 1: P and overflow flags visible
-      if (ovf_lds[0] | ovf_lds[1] | ovf_lds[2] | ovf_lds[3]) {
-        restart = true;
-        break;
-      }
-
-      // ---- values: O^T[columns 128w..][64 rows] += C^T[.., 64 tokens] P^T
-      {
-        const int nkb = second_valid ? 4 : 2;
-        auto ldV = [&](int kb, int mt) -> bf16x8 {
-          const MLA_LDS uint8_t* vt = tiles + ((2 * st + (kb >> 1)) % kBuf) * kTileBytes;
-          const int hb = kb & 1;
-          u32x2 v[2];
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2) {
-            const int row = 16 * hb + 8 * j2 + 4 * g + (i16 >> 2);
-            const int off = row * 1024 + wave * 256 + (((4 * mt + vy) ^ s16(row)) << 4) + vbyte;
-            v[j2] = lds_read_tr16_b64(vt + off);
-          }
-          return as_bf16x8(u32x4{v[0][0], v[0][1], v[1][0], v[1][1]});
-        };
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          if (kb >= nkb) break;
-          const bf16x8 b0 = *(const MLA_LDS bf16x8*)(pl + ((0 * 4 + kb) * 64 + lane) * 16);
-          const bf16x8 b1 = *(const MLA_LDS bf16x8*)(pl + ((1 * 4 + kb) * 64 + lane) * 16);
-          bf16x8 av = ldV(kb, 0);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            bf16x8 anext = av;
-            if (mt + 1 < 4) anext = ldV(kb, mt + 1);
-            oacc[mt][0] = mfma32x32x16(av, b0, oacc[mt][0]);
-            oacc[mt][1] = mfma32x32x16(av, b1, oacc[mt][1]);
-            av = anext;
-            sched_fence();
-          }
-        }
-      }
-      // ---- barrier 2: P may be overwritten, step st's tiles are free, step st+1 resident
-      wait_vmcnt<0>();
-      wg_barrier();
+    int blk_next = page_block(1);
+    for (int st = 0; st < nsteps; st += 2) {
+      run_step(st, blk_next, first && st == 0, std::integral_constant<int, 0>{});
+      if (st + 1 < nsteps) run_step(st + 1, blk_next, false, std::integral_constant<int, 1>{});
     }
-    if (!restart) break;
-    wait_vmcnt<0>();  // drain the prefetch of the abandoned pass
+    // ---- did any row overflow its reference?  (its pair partner may not know)
+    if (lane < 32) xm[th * 64 + rg * 32 + lane] = m_hi;
+    if (lane == 0) xf[wave] = __builtin_amdgcn_ballot_w64(ovf) != 0;
+    wg_barrier();
+    const bool again = xf[0] | xf[1] | xf[2] | xf[3];
+    if (!again) break;
+    m_ref = fmaxf(m_hi, xm[(th ^ 1) * 64 + rg * 32 + n32]);  // the row's chunk maximum
+    m_hi = -__builtin_inff();
     wg_barrier();
   }
 
   // ---- epilogue: complete row sums (two lane halves x two token halves)
   const float l_half = l_part + __shfl_xor(l_part, 32, 64);
-  if (lane < 32) mx_lds[th * 64 + rg * 32 + lane] = l_half;
+  if (lane < 32) xm[th * 64 + rg * 32 + lane] = l_half;
   wg_barrier();
   if (lane < 32 && th == 0) {
-    const float lt = l_half + mx_lds[64 + rg * 32 + lane];
-    l_lds[rg * 32 + lane] = lt;
-    m_lds[rg * 32 + lane] = m_ref;
+    const float lt = l_half + xm[64 + rg * 32 + lane];
+    xl[rg * 32 + lane] = lt;
     if (qvalid) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -__builtin_inff();
   }
   wg_barrier();
@@ -347,7 +433,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int row = row_base + nt * 32 + n32;
-    const float lt = l_lds[nt * 32 + n32];
+    const float lt = xl[nt * 32 + n32];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float* orow = obase + (int64_t)row * 512 + wave * 128;
 #pragma unroll
