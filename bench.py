@@ -90,6 +90,7 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="also time steps without cache eviction")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -146,14 +147,17 @@ def main():
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
 
-    # warm (no eviction between steps): context only, never the headline
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record()
-    for _ in range(K):
-        step.run()
-    w1.record()
-    torch.cuda.synchronize()
-    warm_ms = w0.elapsed_time(w1) / K
+    # warm (no eviction between steps): context only, never the headline; off by
+    # default so that every decode launch of a default run is a cold one
+    warm_ms = None
+    if args.warm:
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for _ in range(K):
+            step.run()
+        w1.record()
+        torch.cuda.synchronize()
+        warm_ms = w0.elapsed_time(w1) / K
 
     ms_per_step = float(step_ms.mean())
     dec_avg = float(dec_ms.mean())

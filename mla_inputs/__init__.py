@@ -57,6 +57,7 @@ class Workload:
     num_splits: int = 1              # KV splits the workload prescribes (0 = launcher's choice)
     seed: int = 0
     weight_std: float = 1.0 / math.sqrt(D_LATENT)
+    lens: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths (edge cases)
 
     @property
     def q_dtype(self) -> str:
@@ -118,12 +119,20 @@ def small_variants():
 # storage encodings
 # ----------------------------------------------------------------------------
 
-def bf16_bits(x: np.ndarray) -> np.ndarray:
+def bf16_bits(x: np.ndarray, chunk: int = 1 << 22) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns the
-    16-bit patterns.  Inputs here are finite draws, so no NaN handling."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)
+    16-bit patterns.  Inputs here are finite draws, so no NaN handling.
+    Works in chunks so the 32-bit temporaries stay small."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).reshape(-1)
+    out = np.empty(u.shape, dtype=np.uint16)
+    for lo in range(0, u.size, chunk):
+        v = u[lo: lo + chunk]
+        r = (v >> np.uint32(16)) & np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += v
+        r >>= np.uint32(16)
+        out[lo: lo + chunk] = r
+    return out.reshape(np.shape(x))
 
 
 def _e4m3_positive_table() -> np.ndarray:
@@ -142,22 +151,43 @@ _E4M3_POS = _e4m3_positive_table()
 _E4M3_MID = ((_E4M3_POS[:-1] + _E4M3_POS[1:]) / 2.0).astype(np.float32)
 
 
-def e4m3_codes(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+def e4m3_codes_by_table(x: np.ndarray) -> np.ndarray:
+    """Encode finite float32 values as OCP E4M3FN bytes by search among the
+    127 finite code values: nearest, ties to the even code, saturating at
+    +-448.  Slow; kept as the definition the fast encoder is checked against."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    v = x.reshape(-1)
+    n_mid = _E4M3_MID.size
+    a = np.minimum(np.abs(v), np.float32(E4M3_MAX))
+    idx = np.searchsorted(_E4M3_MID, a, side="left")
+    hit = np.minimum(idx, n_mid - 1)
+    tie = (idx < n_mid) & (a == _E4M3_MID[hit])
+    idx = np.where(tie & (idx % 2 == 1), idx + 1, idx).astype(np.uint8)
+    return np.where(np.signbit(v), idx | np.uint8(0x80), idx).reshape(x.shape)
+
+
+def e4m3_codes(x: np.ndarray, chunk: int = 1 << 22) -> np.ndarray:
     """Encode finite float32 values as OCP E4M3FN bytes, round to nearest with
-    ties to the even code, saturating at +-448.  Works in chunks so very large
-    caches do not need 64-bit temporaries of their full size."""
+    ties to the even code, saturating at +-448.  Normal range: the float32
+    pattern rounded to 3 mantissa bits (nearest-even on the bits, a carry
+    moves into the exponent as it should) and re-biased from 127 to 7;
+    below 2^-6 the code is the nearest-even multiple of 2^-9.  Identical to
+    ``e4m3_codes_by_table``; works in chunks."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     flat = x.reshape(-1)
     out = np.empty(flat.shape, dtype=np.uint8)
-    n_mid = _E4M3_MID.size
     for lo in range(0, flat.size, chunk):
         v = flat[lo: lo + chunk]
         a = np.minimum(np.abs(v), np.float32(E4M3_MAX))
-        idx = np.searchsorted(_E4M3_MID, a, side="left")
-        hit = np.minimum(idx, n_mid - 1)
-        tie = (idx < n_mid) & (a == _E4M3_MID[hit])
-        idx = np.where(tie & (idx % 2 == 1), idx + 1, idx).astype(np.uint8)
-        out[lo: lo + chunk] = np.where(np.signbit(v), idx | np.uint8(0x80), idx)
+        u = a.view(np.uint32)
+        r = (u >> np.uint32(20)) & np.uint32(1)
+        r += np.uint32(0x7FFFF)
+        r += u
+        r >>= np.uint32(20)
+        normal = a >= np.float32(2.0 ** -6)
+        code = np.where(normal, r.astype(np.int64) - (120 << 3),
+                        np.rint(a * np.float32(512.0)).astype(np.int64)).astype(np.uint8)
+        out[lo: lo + chunk] = np.where(np.signbit(v), code | np.uint8(0x80), code)
     return out.reshape(x.shape)
 
 
@@ -199,13 +229,19 @@ def _encode(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def draw_lengths(wl: Workload, rng: np.random.Generator) -> np.ndarray:
-    if wl.len_range is not None:
+    """Per-sequence cached-token counts.  A length below q_per_seq is legal:
+    the queries that see no token give o = 0 and lse = -inf."""
+    if wl.lens is not None:
+        lens = np.asarray(wl.lens)
+        if lens.size != wl.batch:
+            raise ValueError("lens must give one length per sequence")
+    elif wl.len_range is not None:
         lo, hi = wl.len_range
         lens = rng.integers(lo, hi + 1, size=wl.batch)
     else:
         lens = np.full(wl.batch, wl.seq_len)
-    if (lens < wl.q_per_seq).any():
-        raise ValueError("every sequence must hold at least its query tokens")
+    if (lens < 0).any():
+        raise ValueError("negative sequence length")
     return lens.astype(np.int32)
 
 
@@ -214,9 +250,11 @@ def generate(wl: Workload, seed: Optional[int] = None, poison: bool = True) -> I
     B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
     lens = draw_lengths(wl, rng)
     pages = (lens.astype(np.int64) + BLOCK - 1) // BLOCK
-    max_blocks = int(pages.max())
+    max_blocks = max(1, int(pages.max(initial=0)))
     used = int(pages.sum())
     nb = used + wl.spare_blocks
+    if (pages == 0).any() and wl.spare_blocks < 1:
+        raise ValueError("an empty sequence needs a spare block for its page-table row")
     if wl.paged:
         perm = rng.permutation(nb).astype(np.int32)
     else:
@@ -235,31 +273,47 @@ def generate(wl: Workload, seed: Optional[int] = None, poison: bool = True) -> I
             rows = min(BLOCK, int(lens[b]) - j * BLOCK)
             owned[table[b, j], :rows] = True
 
-    c = rng.standard_normal((nb, BLOCK, D_LATENT), dtype=np.float32)
-    kr = rng.standard_normal((nb, BLOCK, D_ROPE), dtype=np.float32)
+    # Draw order: every block's c, then every block's k^R, then q_nope, q_rope,
+    # W_UK, W_UV.  The cache is drawn and encoded a few blocks at a time (the
+    # generator's stream does not depend on how a draw is cut into calls).
+    step = max(1, (1 << 22) // (BLOCK * D_LATENT))
+    scale = None
+    rope = None
+    if wl.cache_dtype == "fp8":
+        latent = np.empty((nb, BLOCK, D_LATENT), dtype=np.uint8)
+        scale = np.empty((nb, BLOCK), dtype=np.float32)
+        for lo in range(0, nb, step):
+            n = min(step, nb - lo)
+            c = rng.standard_normal((n, BLOCK, D_LATENT), dtype=np.float32)
+            sc = (np.abs(c).max(axis=2) / np.float32(E4M3_MAX)).astype(np.float32)
+            safe = np.where(sc > 0, sc, np.float32(1.0))
+            latent[lo: lo + n] = e4m3_codes(c / safe[..., None])
+            scale[lo: lo + n] = sc
+        rope = np.empty((nb, BLOCK, D_ROPE), dtype=np.uint16)
+        for lo in range(0, nb, step):
+            n = min(step, nb - lo)
+            rope[lo: lo + n] = bf16_bits(rng.standard_normal((n, BLOCK, D_ROPE), dtype=np.float32))
+    else:
+        latent = np.empty((nb, BLOCK, ROW), dtype=np.float32 if wl.cache_dtype == "f32" else np.uint16)
+        for lo in range(0, nb, step):
+            n = min(step, nb - lo)
+            latent[lo: lo + n, :, :D_LATENT] = _encode(
+                rng.standard_normal((n, BLOCK, D_LATENT), dtype=np.float32), wl.cache_dtype)
+        for lo in range(0, nb, step):
+            n = min(step, nb - lo)
+            latent[lo: lo + n, :, D_LATENT:] = _encode(
+                rng.standard_normal((n, BLOCK, D_ROPE), dtype=np.float32), wl.cache_dtype)
     q_nope = rng.standard_normal((B * Sq, H, D_HEAD), dtype=np.float32)
     q_rope = rng.standard_normal((B * Sq, H, D_ROPE), dtype=np.float32)
     w_uk = rng.standard_normal((H, D_HEAD, D_LATENT), dtype=np.float32) * np.float32(wl.weight_std)
     w_uv = rng.standard_normal((H, D_HEAD, D_LATENT), dtype=np.float32) * np.float32(wl.weight_std)
-
-    scale = None
-    rope = None
-    if wl.cache_dtype == "fp8":
-        amax = np.abs(c).max(axis=2)
-        scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-        safe = np.where(scale > 0, scale, np.float32(1.0))
-        latent = e4m3_codes(c / safe[..., None])
-        rope = bf16_bits(kr)
-        if poison:
+    if poison:
+        if wl.cache_dtype == "fp8":
             latent[~owned] = E4M3_NAN
             rope[~owned] = BF16_NAN
             scale[~owned] = np.float32("nan")
-    else:
-        pool = np.concatenate([c, kr], axis=2)
-        latent = _encode(pool, wl.cache_dtype)
-        if poison:
+        else:
             latent[~owned] = np.float32("nan") if wl.cache_dtype == "f32" else BF16_NAN
-    del c, kr
     return Inputs(
         wl=wl, seq_lens=lens, block_table=table, num_blocks=nb,
         latent=latent, rope=rope, scale=scale,

@@ -83,7 +83,7 @@ int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int
   mla::AbsorbArgs a{q_nope, w_uk, q_lat, rows, dims->heads};
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == MLA_BF16) {
-    dim3 grid(dims->heads, kDL / 64);
+    dim3 grid(dims->heads * 2);  // (head, half of d_latent)
     if (q_lat_dtype == MLA_BF16)
       st = launch("mla::absorb_q_mfma<true>", (const void*)mla::absorb_q_mfma<true>, grid, dim3(256), a, s);
     else
@@ -183,7 +183,8 @@ int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_p
   const int64_t grid = (int64_t)dims->batch * rows;
   if (grid == 0) return MLA_OK;
   mla::CombineArgs a{o_part, lse_part, o_lat, lse, dims->batch, num_splits, rows};
-  st = launch("mla::split_combine", (const void*)mla::split_combine, dim3((unsigned)grid), dim3(128), a, (hipStream_t)stream);
+  st = launch("mla::split_combine", (const void*)mla::split_combine, dim3((unsigned)((grid + 1) / 2)), dim3(256), a,
+              (hipStream_t)stream);
   return st;
 }
 
@@ -199,7 +200,7 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
   mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
-    st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3(dims->heads, kDH / 64), dim3(256), a, s);
+    st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3(dims->heads * (kDH / 64)), dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;
     st = launch("mla::out_uv_f32", (const void*)mla::out_uv_f32, dim3(dims->heads, rows), dim3(128), a, s);

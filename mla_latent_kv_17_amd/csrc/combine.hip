@@ -6,46 +6,56 @@
 // inference time": attention over all earlier tokens).  Chunks that saw no
 // token carry lse_s = -inf and weight 0.
 //
-// One workgroup per query row, 128 threads x 4 columns; the ns partial rows
-// are read once, coalesced.
+// 128 threads x 4 columns per query row, two rows per workgroup.  Up to
+// kBatch chunks are handled per round with every load (log-sum-exps and
+// partial rows) issued before any arithmetic, so a round costs one memory
+// latency; the running merge across rounds is the same log-sum-exp update.
 #include "mla_device.h"
 #include "mla_kernels.h"
 
 namespace mla {
 
-__global__ void __launch_bounds__(128) split_combine(const CombineArgs a) {
-  __shared__ float wsh[1024];
-  const int gr = blockIdx.x;
+__global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
+  constexpr int kBatch = 8;
+  const int gr = blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (gr >= a.batch * a.rows) return;
   const int b = gr / a.rows, row = gr - b * a.rows;
   const int ns = a.num_splits;
+  const int c = (threadIdx.x & 127) * 4;
   const float* lp = a.lse_part + (int64_t)b * ns * a.rows + row;
-  // max and normaliser over the chunks (every thread computes them; ns is small)
-  float m = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, lp[(int64_t)s * a.rows]);
-  float z = 0.f;
-  if (m != -__builtin_inff()) {
-    for (int s = threadIdx.x; s < ns; s += 128) {
-      const float ls = lp[(int64_t)s * a.rows];
-      const float e = ls == -__builtin_inff() ? 0.f : expf(ls - m);
-      wsh[s] = e;
+  const float* op = a.o_part + ((int64_t)b * ns * a.rows + row) * 512 + c;
+  const int64_t ostride = (int64_t)a.rows * 512;
+  float m = -__builtin_inff(), z = 0.f;  // running maximum and sum of exp(lse_s - m)
+  f32x4 acc = f32x4{};                   // running sum of exp(lse_s - m) o_s
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    float ls[kBatch];
+    f32x4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = s0 + j < ns;
+      ls[j] = in ? lp[(int64_t)(s0 + j) * a.rows] : -__builtin_inff();
+      v[j] = in ? *(const f32x4*)(op + (s0 + j) * ostride) : f32x4{};
     }
-    __syncthreads();
-    for (int s = 0; s < ns; ++s) z += wsh[s];
-  }
-  const int c = threadIdx.x * 4;
-  f32x4 acc = f32x4{};
-  if (z > 0.f) {
-    const float inv = 1.f / z;
-    const float* op = a.o_part + ((int64_t)b * ns * a.rows + row) * 512 + c;
-    for (int s = 0; s < ns; ++s) {
-      const float ws = wsh[s] * inv;
-      if (ws == 0.f) continue;
-      const f32x4 v = *(const f32x4*)(op + (int64_t)s * a.rows * 512);
-      acc += ws * v;
+    float mb = m;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ls[j]);
+    if (mb == -__builtin_inff()) continue;  // no chunk so far saw a token
+    const float alpha = m == -__builtin_inff() ? 0.f : expf(m - mb);
+    z *= alpha;
+    acc *= alpha;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (ls[j] == -__builtin_inff()) continue;  // an empty chunk has weight 0
+      const float e = expf(ls[j] - mb);
+      z += e;
+      acc += e * v[j];
     }
+    m = mb;
   }
-  *(f32x4*)(a.o_lat + ((int64_t)b * a.rows + row) * 512 + c) = acc;
-  if (a.lse && threadIdx.x == 0) a.lse[(int64_t)b * a.rows + row] = z > 0.f ? m + logf(z) : -__builtin_inff();
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  *(f32x4*)(a.o_lat + ((int64_t)b * a.rows + row) * 512 + c) = acc * inv;
+  if (a.lse && (threadIdx.x & 127) == 0)
+    a.lse[(int64_t)b * a.rows + row] = z > 0.f ? m + logf(z) : -__builtin_inff();
 }
 
 }  // namespace mla

@@ -410,7 +410,10 @@ decode_mfma_bf16(const DecodeArgs a) {
     }
     // ---- did any row overflow its reference?  (its pair partner may not know)
     if (lane < 32) xm[th * 64 + rg * 32 + lane] = m_hi;
-    if (lane == 0) xf[wave] = __builtin_amdgcn_ballot_w64(ovf) != 0;
+    // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
+    // would see lane 0's row alone)
+    const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
+    if (lane == 0) xf[wave] = wave_ovf;
     wg_barrier();
     const bool again = xf[0] | xf[1] | xf[2] | xf[3];
     if (!again) break;

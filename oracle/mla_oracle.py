@@ -52,7 +52,7 @@ __all__ = [
     "visible_tokens", "scores", "softmax_lse", "mix_values",
     "explicit_decode", "absorbed_decode", "split_ranges", "split_partials",
     "combine_partials", "cache_numbers_per_token_layer", "cache_bytes",
-    "default_softmax_scale",
+    "default_softmax_scale", "absorb_queries", "project_output",
 ]
 
 
@@ -235,6 +235,30 @@ def absorbed_decode(inp, select=None, softmax_scale: Optional[float] = None):
                 q_lat[r, h], o_lat[r, h], lse[r, h] = ql, ol, l
                 o[r, h] = w_uv @ ol
     return q_lat, o_lat, lse, o
+
+
+def absorb_queries(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """Query-side absorption ([DF-latent]): q_lat[r][h] = W_UK[h]^T q_nope[r][h],
+    so that q_lat . c_t equals q_nope . (W_UK c_t), the score against the
+    rebuilt key.  q_nope [R][H][128], w_uk [H][128][512], fp64 -> [R][H][512]."""
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    out = np.empty((q_nope.shape[0], q_nope.shape[1], w_uk.shape[2]))
+    for h in range(q_nope.shape[1]):
+        out[:, h] = q_nope[:, h] @ w_uk[h]
+    return out
+
+
+def project_output(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Output-side absorption ([DF-latent]): o[r][h] = W_UV[h] o_lat[r][h];
+    for o_lat = sum_t p_t c_t this is sum_t p_t (W_UV c_t), the mix of rebuilt
+    values.  o_lat [R][H][512], w_uv [H][128][512], fp64 -> [R][H][128]."""
+    o_lat = np.asarray(o_lat, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    out = np.empty((o_lat.shape[0], o_lat.shape[1], w_uv.shape[1]))
+    for h in range(o_lat.shape[1]):
+        out[:, h] = o_lat[:, h] @ w_uv[h].T
+    return out
 
 
 # ----------------------------------------------------------------------------

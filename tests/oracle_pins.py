@@ -326,6 +326,37 @@ def check_split_combine():
     assert (o == 0).all() and np.isneginf(l).all()
 
 
+def check_absorb_project_identities():
+    """The two absorbed weight products against the rebuilt keys and values
+    ([DF-latent]): q_lat . c = q_nope . (W_UK c) for every cached row c, and
+    W_UV (sum_t p_t c_t) = sum_t p_t (W_UV c_t), per head; plus exact
+    small-integer brute force for single elements."""
+    inp = tiny_inputs([150], heads=3, seed=11)
+    C, KR = O.gather_sequence(inp, 0)
+    qn = inp.q_nope.astype(np.float64)
+    q_lat = O.absorb_queries(qn, inp.w_uk)
+    rng = np.random.default_rng(12)
+    p = rng.random(C.shape[0])
+    p /= p.sum()
+    o_lat = np.broadcast_to(p @ C, (1, 3, DL))
+    o = O.project_output(o_lat, inp.w_uv)
+    for h in range(3):
+        K = O.reconstruct_keys(C, KR, inp.w_uk[h].astype(np.float64))
+        assert rel_l2(C @ q_lat[0, h], K[:, :DH] @ qn[0, h]) <= 1e-12
+        V = O.reconstruct_values(C, inp.w_uv[h].astype(np.float64))
+        assert rel_l2(o[0, h], p @ V) <= 1e-12
+    # brute force, integers (exact): one element of each product
+    t = tiny_inputs([3], heads=2, seed=13, integer=True)
+    ql = O.absorb_queries(t.q_nope, t.w_uk)
+    for h, c in ((0, 5), (1, 511)):
+        assert ql[0, h, c] == sum(float(t.w_uk[h, d, c]) * float(t.q_nope[0, h, d]) for d in range(DH))
+    x = np.arange(2 * DL, dtype=np.float64).reshape(1, 2, DL) % 7 - 3
+    ob = O.project_output(x, t.w_uv)
+    for h, d in ((0, 0), (1, 127)):
+        assert ob[0, h, d] == sum(float(t.w_uv[h, d, c]) * x[0, h, c] for c in range(DL))
+
+
 ALL_CHECKS = [check_cache_arithmetic, check_decode_tables, check_softmax,
               check_textbook_reduction, check_closed_forms, check_brute_force_exact,
-              check_paging_invariance, check_causal_two_tokens, check_split_combine]
+              check_paging_invariance, check_causal_two_tokens, check_split_combine,
+              check_absorb_project_identities]

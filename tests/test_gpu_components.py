@@ -1,0 +1,107 @@
+"""Each C-ABI entry point on its own against the oracle's definition of that
+step: mla_absorb_q, mla_out_uv and mla_split_combine, at row counts that span
+several 32-row tiles with a ragged tail, and at the largest split count."""
+import math
+
+import numpy as np
+import pytest
+
+import mla_inputs as MI
+import oracle as O
+from parity import check, metrics
+
+pytestmark = pytest.mark.gpu
+
+H = 128
+
+
+def _bf16_tensor(bits, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.int16).view(torch.bfloat16).to(device)
+
+
+def _weights(rng, std=1.0 / math.sqrt(512)):
+    return MI.bf16_bits(rng.standard_normal((H, 128, 512), dtype=np.float32) * np.float32(std))
+
+
+@pytest.mark.parametrize("rows", [1, 37, 256])
+def test_absorb_q_bf16(rows):
+    import torch
+    import mla_latent_kv_17_amd as M
+    print(f"[case] absorb_q bf16 rows={rows}", flush=True)
+    rng = np.random.default_rng(3000 + rows)
+    qn = MI.bf16_bits(rng.standard_normal((rows, H, 128), dtype=np.float32))
+    w = _weights(rng)
+    q_lat = torch.empty((rows, H, 512), dtype=torch.bfloat16, device="cuda")
+    M.mla_absorb_q(M.make_dims(rows, 1, H), _bf16_tensor(qn), _bf16_tensor(w), q_lat)
+    got = q_lat.float().cpu().numpy().astype(np.float64)
+    ref = O.absorb_queries(O.decode_bf16(qn), O.decode_bf16(w))
+    # fp32 sums of exact products, rounded once to bf16 (nearest-even):
+    # within half a bf16 step of the value, plus fp32 summation error
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-6
+    worst = float(np.max(np.abs(got - ref) - bound))
+    print(f"[parity] absorb rows={rows}: max excess over bf16 rounding bound {worst:.3e}", flush=True)
+    assert worst <= 0.0
+
+
+def test_absorb_q_f32_out():
+    import torch
+    import mla_latent_kv_17_amd as M
+    rows = 33
+    rng = np.random.default_rng(3100)
+    qn = MI.bf16_bits(rng.standard_normal((rows, H, 128), dtype=np.float32))
+    w = _weights(rng)
+    q_lat = torch.empty((rows, H, 512), dtype=torch.float32, device="cuda")
+    M.mla_absorb_q(M.make_dims(rows, 1, H), _bf16_tensor(qn), _bf16_tensor(w), q_lat)
+    ref = O.absorb_queries(O.decode_bf16(qn), O.decode_bf16(w))
+    check("absorb f32 out", q_lat.cpu().numpy(), ref, "f32")
+
+
+@pytest.mark.parametrize("rows", [1, 37, 256])
+def test_out_uv_bf16_weights(rows):
+    import torch
+    import mla_latent_kv_17_amd as M
+    print(f"[case] out_uv bf16 rows={rows}", flush=True)
+    rng = np.random.default_rng(3200 + rows)
+    o_lat = rng.standard_normal((rows, H, 512)).astype(np.float32) * np.float32(0.05)
+    w = _weights(rng)
+    out = torch.empty((rows, H, 128), dtype=torch.float32, device="cuda")
+    M.mla_out_uv(M.make_dims(rows, 1, H), torch.from_numpy(o_lat).cuda(), _bf16_tensor(w), out)
+    ref = O.project_output(o_lat, O.decode_bf16(w))
+    # o_lat enters as two bf16 halves (about 16 significant bits): fp32-level
+    check(f"out_uv rows={rows}", out.cpu().numpy(), ref, "f32")
+
+
+def _combine_case(B, ns, Sq, heads, seed):
+    rng = np.random.default_rng(seed)
+    o_part = rng.standard_normal((B, ns, Sq, heads, 512)).astype(np.float32)
+    lse_part = (rng.standard_normal((B, ns, Sq, heads)) * 3.0).astype(np.float32)
+    # empty chunks: lse -inf and garbage partial rows that must get weight 0
+    empty = rng.random((B, ns, Sq, heads)) < 0.3
+    lse_part[empty] = -np.inf
+    o_part[empty] = np.nan
+    # one query row that no chunk saw
+    lse_part[0, :, 0, 0] = -np.inf
+    o_part[0, :, 0, 0] = np.nan
+    return o_part, lse_part
+
+
+@pytest.mark.parametrize("B,ns,Sq,heads", [(3, 5, 2, 128), (2, 64, 1, 128), (1, 1024, 1, 16), (4, 1, 1, 16)])
+def test_split_combine(B, ns, Sq, heads):
+    import torch
+    import mla_latent_kv_17_amd as M
+    print(f"[case] split_combine B={B} ns={ns} Sq={Sq} H={heads}", flush=True)
+    o_part, lse_part = _combine_case(B, ns, Sq, heads, 3300 + ns)
+    o_lat = torch.empty((B * Sq, heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B * Sq, heads), dtype=torch.float32, device="cuda")
+    M.mla_split_combine(M.make_dims(B, Sq, heads), ns, torch.from_numpy(o_part).cuda(),
+                        torch.from_numpy(lse_part).cuda(), o_lat, lse)
+    o_ref, lse_ref = O.combine_partials(o_part, lse_part)
+    got = o_lat.cpu().numpy().reshape(B, Sq, heads, 512)
+    gl = lse.cpu().numpy().reshape(B, Sq, heads)
+    assert np.isfinite(got).all()
+    check(f"combine ns={ns}", got, o_ref, "f32")
+    none = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(gl), none)
+    assert (got[none] == 0).all()
+    assert np.max(np.abs(gl[~none] - lse_ref[~none])) <= 1e-5 * max(1.0, np.abs(lse_ref[~none]).max())

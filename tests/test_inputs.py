@@ -72,6 +72,18 @@ def test_e4m3_rounding_matches_torch():
     assert np.array_equal(MI.e4m3_codes(x), ref)
 
 
+def test_e4m3_fast_encoder_equals_table_search():
+    """Every float32 bit pattern in a dense sweep of [0, 448] (and its
+    negative), the code midpoints and values just beside them: the bit-level
+    encoder and the search over the 127 code values agree."""
+    u = np.arange(0, 0x43E00001, 97, dtype=np.uint32)  # 0 .. 448, every 97th pattern
+    mids = MI._E4M3_MID
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    x = np.concatenate([u.view(np.float32), near, np.float32([0.0, 448.0, 2.0 ** -6, 2.0 ** -9, 2.0 ** -10])])
+    x = np.concatenate([x, -x])
+    assert np.array_equal(MI.e4m3_codes(x), MI.e4m3_codes_by_table(x))
+
+
 def test_fp8_scale_is_row_max_over_448():
     inp = MI.generate(MI.small_variants()["fp8_small_sq2"])
     b0 = inp.block_table[0, 0]

@@ -123,6 +123,22 @@ def _cache_mha_one_vector(scheme, **kw):
     return _orig["cache_numbers_per_token_layer"](scheme, **kw)
 
 
+def _absorb_first_head(q_nope, w_uk):
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    return np.stack([q_nope[:, h] @ np.asarray(w_uk[0], dtype=np.float64) for h in range(q_nope.shape[1])], axis=1)
+
+
+def _project_first_head(o_lat, w_uv):
+    o_lat = np.asarray(o_lat, dtype=np.float64)
+    return np.stack([o_lat[:, h] @ np.asarray(w_uv[0], dtype=np.float64).T for h in range(o_lat.shape[1])], axis=1)
+
+
+def _project_drops_last_column(o_lat, w_uv):
+    o_lat = np.asarray(o_lat, dtype=np.float64)
+    w = np.asarray(w_uv, dtype=np.float64)
+    return np.stack([o_lat[:, h, :-1] @ w[h, :, :-1].T for h in range(o_lat.shape[1])], axis=1)
+
+
 MUTANTS = {
     "reconstruct_keys": [_keys_without_rope, _keys_transposed_weight],
     "reconstruct_values": [_values_skip_projection],
@@ -137,6 +153,8 @@ MUTANTS = {
     "combine_partials": [_combine_no_max_weight],
     "split_ranges": [_split_token_equal],
     "cache_numbers_per_token_layer": [_cache_mha_one_vector],
+    "absorb_queries": [_absorb_first_head],
+    "project_output": [_project_first_head, _project_drops_last_column],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]
