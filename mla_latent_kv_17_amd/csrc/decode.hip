@@ -189,13 +189,28 @@ decode_mfma_bf16(const DecodeArgs a) {
   // A step's two tiles are the halves of one 64-token page, so one block id
   // serves both; ids are fetched a step ahead with scalar loads.
   const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
-  auto page_block = [&](int st) -> int {
+  auto page_block = [&](int st) __attribute__((always_inline)) -> int {
     return 2 * st < ntiles ? load_uniform(a.block_table, bt_row + (wk.tok0 >> 6) + st) : 0;
   };
   // RoPE part: rows wave*8 + lane/8, 8 chunks each (lane part of the address)
   const int rope_r = wave * 8 + (lane >> 3);
   const uint32_t rope_lane = (uint32_t)((lane >> 3) * a.rope_rs) + ((((lane & 7) ^ s8(rope_r))) << 4);
-  auto issue_tile = [&](int t, int blk) {
+  // copy j of a full tile (all 32 rows hold tokens): j < 8 is latent row
+  // wave*8 + j, j == 8 the wave's eight RoPE rows
+  auto tile_chunk = [&](int t, int blk, int j) __attribute__((always_inline)) {
+    const int tt = wk.tok0 + t * kTileTok;
+    const int r0 = (tt & 63) + wave * 8;
+    const uint32_t tl = tiles_lds + (t % kBuf) * kTileBytes;
+    if (j < 8) {
+      const uint8_t* rp = a.latent + blk * a.lat_bs + (int64_t)(r0 + j) * a.lat_rs;
+      const int sw = ((j & 3) << 2) | ((2 * wave + (j >> 2)) & 3);  // s16(wave*8 + j)
+      dma16s(rp, (uint32_t)(lane ^ sw) << 4, tl + (wave * 8 + j) * 1024);
+    } else {
+      const uint8_t* rr = a.rope + blk * a.rope_bs + (int64_t)r0 * a.rope_rs;
+      dma16s(rr, rope_lane, tl + kLatBytes + wave * 1024);
+    }
+  };
+  auto issue_tile = [&](int t, int blk) __attribute__((always_inline)) {
     const int tt = wk.tok0 + t * kTileTok;
     const int r0 = (tt & 63) + wave * 8;
     const uint32_t tl = tiles_lds + (t % kBuf) * kTileBytes;
@@ -204,11 +219,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     const int valid_rows = wk.len - tt - wave * 8;  // rows j < valid_rows hold tokens
     if (valid_rows >= 8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sw = ((j & 3) << 2) | ((2 * wave + (j >> 2)) & 3);  // s16(wave*8 + j)
-        dma16s(rp + (int64_t)j * a.lat_rs, (uint32_t)(lane ^ sw) << 4, tl + (wave * 8 + j) * 1024);
-      }
-      dma16s(rr, rope_lane, tl + kLatBytes + wave * 1024);
+      for (int j = 0; j < 9; ++j) tile_chunk(t, blk, j);
     } else {  // last page of the sequence: rows past its length read zeros
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -222,7 +233,7 @@ decode_mfma_bf16(const DecodeArgs a) {
       dma16(src, tl + kLatBytes + wave * 1024);
     }
   };
-  auto issue_step = [&](int st, int blk) {
+  auto issue_step = [&](int st, int blk) __attribute__((always_inline)) {
     if (2 * st < ntiles) issue_tile(2 * st, blk);
     if (2 * st + 1 < ntiles) issue_tile(2 * st + 1, blk);
   };
@@ -285,10 +296,16 @@ decode_mfma_bf16(const DecodeArgs a) {
   float l_part = 0.f;                // this lane's share of the row sum
   bool ovf = false;
 
-  auto run_step = [&](int st, int& blk_next, bool set_ref, auto parc) {
+  auto run_step = [&](int st, int& blk_next, bool set_ref, auto parc) __attribute__((always_inline)) {
     constexpr int par = decltype(parc)::value;  // st & 1: which half of the tile ring
-    // tiles of step st-1 are free (barrier 2 of the previous step): prefetch step st+1
-    if (st + 1 < nsteps) issue_step(st + 1, blk_next);
+    // tiles of step st-1 are free (barrier 2 of the previous step): prefetch
+    // step st+1.  When both of its tiles are full (every step but a
+    // sequence's last page), the 18 copies are spread over the score
+    // product below, one per two MFMAs, so that the wave never stalls on a
+    // full memory queue with no matrix work in flight.
+    const int blk_cur = blk_next;
+    const bool spread = st + 1 < nsteps && wk.len - (wk.tok0 + (2 * st + 2) * kTileTok) >= 2 * kTileTok;
+    if (st + 1 < nsteps && !spread) issue_step(st + 1, blk_cur);
     blk_next = page_block(st + 2);
     const bool own_valid = 2 * st + th < ntiles;
     const bool second_valid = 2 * st + 1 < ntiles;
@@ -298,7 +315,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     float p[16];
     if (own_valid) {
       const MLA_LDS uint8_t* tb = tiles + 2 * par * kTileBytes;
-      auto ldA = [&](int kb) -> bf16x8 {
+      auto ldA = [&](int kb) __attribute__((always_inline)) -> bf16x8 {
         if (kb < 32)
           return *(const MLA_LDS bf16x8*)(tb + c1_lat + (kb >> 3) * 256 + (((kb & 7) * 32) ^ lat_x));
         return *(const MLA_LDS bf16x8*)(tb + c1_rope + (((kb - 32) * 32) ^ rope_x));
@@ -308,11 +325,21 @@ decode_mfma_bf16(const DecodeArgs a) {
       bf16x8 ar[kDepth];
 #pragma unroll
       for (int kb = 0; kb < kDepth; ++kb) ar[kb] = ldA(kb);
+      if (spread) {
 #pragma unroll
-      for (int kb = 0; kb < 36; ++kb) {
-        sacc = mfma32x32x16(ar[kb % kDepth], qf[kb], sacc);
-        if (kb + kDepth < 36) ar[kb % kDepth] = ldA(kb + kDepth);
-        sched_fence();
+        for (int kb = 0; kb < 36; ++kb) {
+          sacc = mfma32x32x16(ar[kb % kDepth], qf[kb], sacc);
+          if (kb + kDepth < 36) ar[kb % kDepth] = ldA(kb + kDepth);
+          if ((kb & 1) == 0) tile_chunk(2 * st + 2 + (kb >= 18), blk_cur, (kb >> 1) % 9);
+          sched_fence();
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 36; ++kb) {
+          sacc = mfma32x32x16(ar[kb % kDepth], qf[kb], sacc);
+          if (kb + kDepth < 36) ar[kb % kDepth] = ldA(kb + kDepth);
+          sched_fence();
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = sacc[r] * a.scale_log2;
@@ -328,7 +355,7 @@ decode_mfma_bf16(const DecodeArgs a) {
       for (int r = 0; r < 16; ++r) p[r] = -__builtin_inff();
     }
     // value operand of the first 16-token block: issued now, used after barrier 1
-    auto ldV = [&](int kb, bf16x8 (&av)[4]) {
+    auto ldV = [&](int kb, bf16x8 (&av)[4]) __attribute__((always_inline)) {
       const MLA_LDS uint8_t* vt = tiles + (2 * par + (kb >> 1)) * kTileBytes + (kb & 1) * 16 * 1024;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
