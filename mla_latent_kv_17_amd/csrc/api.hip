@@ -160,7 +160,7 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
     const int64_t padded = (units + 7) / 8 * 8;
     const int64_t grid = padded * a.row_blocks;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    st = launch("mla::decode_mfma_bf16", (const void*)mla::decode_mfma_bf16, dim3((unsigned)grid), dim3(256), a, s);
+    st = launch("mla::decode_mfma_bf16", (const void*)mla::decode_mfma_bf16, dim3((unsigned)grid), dim3(512), a, s);
   } else {
     const int64_t grid = units * rows;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;

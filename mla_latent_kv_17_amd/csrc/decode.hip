@@ -104,6 +104,33 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t 
       : "memory");
 }
 
+// Same copy where lane i's byte offset is ((16 i) ^ x16) + row, for
+// wave-uniform x16 and row: the offset is formed inside the asm block, so the
+// compiler keeps one lane register and one base per tile instead of a 64-bit
+// address (and a hoisted offset register) for every copy.
+__device__ __forceinline__ void dma16x(const void* base, uint32_t lane16, uint32_t x16, uint32_t row,
+                                       uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  x16 = __builtin_amdgcn_readfirstlane(x16);
+  row = __builtin_amdgcn_readfirstlane(row);
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  base = (const void*)(((uint64_t)hi << 32) | (uint64_t)lo);
+  uint32_t saved, off;
+  asm volatile(
+      "v_xor_b32 %1, %2, %3\n\t"
+      "v_add_u32 %1, %1, %4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved), "=&v"(off)
+      : "v"(lane16), "s"(x16), "s"(row), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
 // A wait the compiler sees (it updates its own counter model): all vector
 // memory loads issued so far have completed.
 __device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -153,321 +180,374 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
 
 }  // namespace
 
-// bf16 cache.  Workgroup = 4 waves = one (sequence, KV chunk, block of 64
-// query rows).  The context is walked in 64-token steps (two 32-token tiles
-// = one cache page).  Wave w: score rows 32*(w&1) .. +31 over the step's token
-// half (w>>1), and value columns 128*w .. +127 for all 64 rows.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// bf16 cache.  Workgroup = 8 waves (two per SIMD) = one (sequence, KV chunk,
+// block of 64 query rows); the chunk is walked in 32-token tiles (half a
+// cache page).  Two waves per SIMD let one wave's LDS, memory and barrier
+// waits be covered by the other's matrix work.
+//
+// Per tile s, with a ring of four LDS tile buffers (s-1 being read by the
+// value product, s by the score product, s+1 and s+2 in flight):
+//   scores   wave w: S^T[16 tokens (half w&1)][16 rows (quarter w>>1)],
+//            v_mfma_f32_16x16x32_bf16 over K = 576; A = tile rows from LDS,
+//            B = the wave's queries in registers.
+//   softmax  of tile s (log2 domain, fixed per-row reference).
+//   values   of tile s-1: wave w accumulates O^T[latent columns 64w..+63]
+//            [64 rows] += C^T P^T with v_mfma_f32_32x32x16_bf16, C^T read by
+//            the transposing LDS load, P^T from a double-buffered LDS array.
+//   The matrix instructions of the two products, the softmax arithmetic and
+//   the five DMA copies each wave issues for tile s+2 are interleaved in
+//   program order; one barrier per tile (P(s) visible, tile s-1 free, tile
+//   s+1 resident).
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_bf16(const DecodeArgs a) {
-  constexpr int kBuf = 4;                       // tile ring = 2 steps
-  constexpr int kPBytes = 2 * 4 * 64 * 16;      // P^T fragments: 64 rows x 64 tokens
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBuf * kTileBytes + kPBytes + 1024];
+  constexpr int kBuf = 4;                         // tile ring
+  constexpr int kPBytes = 64 * 32 * 2;            // P of one tile: 64 rows x 32 tokens bf16
+  constexpr int kQStride = 73;                    // staged query row: 72 chunks + 1 pad
+  constexpr int kQBase = 2 * kTileBytes;          // queries are staged over tiles 2, 3 (+ P)
+  constexpr int kXOff = kBuf * kTileBytes + 2 * kPBytes;
+  static_assert(kQBase + 64 * kQStride * 16 <= kXOff, "query staging must fit before the exchange area");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280];
   MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)&smem[0];
-  MLA_LDS uint8_t* const pl = tiles + kBuf * kTileBytes;
-  MLA_LDS float* const xm = (MLA_LDS float*)(pl + kPBytes);   // [2 halves][64 rows] maxima
-  MLA_LDS float* const xl = xm + 128;                         // [64] row sums
-  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 64);            // [4] overflow flags
+  MLA_LDS uint8_t* const pbuf = tiles + kBuf * kTileBytes;
+  MLA_LDS float* const xm = (MLA_LDS float*)(tiles + kXOff);  // [2 token halves][64 rows]
+  MLA_LDS float* const xl = xm + 128;                         // [2][64] row sums
+  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 128);           // [8] overflow flags
 
+  // the roles below assume exactly eight waves
+  if (blockDim.x != 512) return;
   Work wk;
   if (!decode_work(a, wk)) return;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, 0..7
   const int lane = tid & 63;
-  const int g = lane >> 5;      // k-half of an MFMA operand
+  const int g = lane >> 5;        // k-half of a 32x32 operand
   const int n32 = lane & 31;
-  const int rg = wave & 1;      // score row group
-  const int th = wave >> 1;     // token half of a step
+  const int q4 = lane >> 4;       // k-quarter of a 16x16 operand / token quad of its result
+  const int i16 = lane & 15;
+  const int th = wave & 1;        // score token half of a tile
+  const int rq = wave >> 1;       // score row quarter of the block
   const int rows = a.rows;
   const int row_base = wk.rb * kRowsPerWg;
   const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
   const int ntiles = wk.ntiles;
-  const int nsteps = (ntiles + 1) >> 1;
   const uint32_t tiles_lds = lds_addr(tiles);
 
-  // ---- HBM -> LDS copies of one 32-token tile: 9 instructions per wave.
-  // A step's two tiles are the halves of one 64-token page, so one block id
-  // serves both; ids are fetched a step ahead with scalar loads.
+  // ---- HBM -> LDS copies of one tile: 5 per wave.  Latent rows 4w .. 4w+3
+  // (one row per copy) and RoPE rows rb .. rb+7, rb = min(8w, 24): a copy
+  // moves eight 128-byte RoPE rows, so four copies would do and waves 4..7
+  // rewrite rows 24..31 with the same bytes (every wave issues five copies).
   const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
-  auto page_block = [&](int st) __attribute__((always_inline)) -> int {
-    return 2 * st < ntiles ? load_uniform(a.block_table, bt_row + (wk.tok0 >> 6) + st) : 0;
+  auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
+    return t < ntiles ? load_uniform(a.block_table, bt_row + ((wk.tok0 + t * kTileTok) >> 6)) : 0;
   };
-  // RoPE part: rows wave*8 + lane/8, 8 chunks each (lane part of the address)
-  const int rope_r = wave * 8 + (lane >> 3);
+  const int rope_base = min(8 * wave, 24);
+  const int rope_r = rope_base + (lane >> 3);
   const uint32_t rope_lane = (uint32_t)((lane >> 3) * a.rope_rs) + ((((lane & 7) ^ s8(rope_r))) << 4);
-  // copy j of a full tile (all 32 rows hold tokens): j < 8 is latent row
-  // wave*8 + j, j == 8 the wave's eight RoPE rows
-  auto tile_chunk = [&](int t, int blk, int j) __attribute__((always_inline)) {
+  const uint32_t lane16 = (uint32_t)lane << 4;
+  struct TileSrc {
+    const uint8_t* lat;   // latent row 4 wave of the tile
+    const uint8_t* rope;  // RoPE row rope_base of the tile
+    uint32_t lds;         // the tile's buffer
+    int vlat, vrope;      // rows (from those firsts) that hold tokens
+  };
+  auto tile_src = [&](int t, int blk) __attribute__((always_inline)) -> TileSrc {
     const int tt = wk.tok0 + t * kTileTok;
-    const int r0 = (tt & 63) + wave * 8;
-    const uint32_t tl = tiles_lds + (t % kBuf) * kTileBytes;
-    if (j < 8) {
-      const uint8_t* rp = a.latent + blk * a.lat_bs + (int64_t)(r0 + j) * a.lat_rs;
-      const int sw = ((j & 3) << 2) | ((2 * wave + (j >> 2)) & 3);  // s16(wave*8 + j)
-      dma16s(rp, (uint32_t)(lane ^ sw) << 4, tl + (wave * 8 + j) * 1024);
+    const int r = tt & 63;
+    const int left = t < ntiles ? wk.len - tt : 0;
+    return TileSrc{a.latent + blk * a.lat_bs + (int64_t)(r + 4 * wave) * a.lat_rs,
+                   a.rope + blk * a.rope_bs + (int64_t)(r + rope_base) * a.rope_rs,
+                   tiles_lds + (uint32_t)((t % kBuf) * kTileBytes), left - 4 * wave, left - rope_base};
+  };
+  // copy j of a tile (j < 4: latent row 4 wave + j; j == 4: RoPE rows).
+  // Rows at or past the sequence's length (all rows, for a tile past the
+  // chunk) read the zero row.  Branch-free: uniform and per-lane selects.
+  auto tile_chunk = [&](const TileSrc& src, int j) __attribute__((always_inline)) {
+    if (j < 4) {
+      const bool v = j < src.vlat;
+      const int sw = (j << 2) | (wave & 3);  // s16(4 wave + j)
+      dma16x(v ? (const void*)src.lat : (const void*)g_zero_row, lane16, v ? (uint32_t)sw << 4 : 0u,
+             v ? (uint32_t)(j * a.lat_rs) : 0u, src.lds + (4 * wave + j) * 1024);
     } else {
-      const uint8_t* rr = a.rope + blk * a.rope_bs + (int64_t)r0 * a.rope_rs;
-      dma16s(rr, rope_lane, tl + kLatBytes + wave * 1024);
+      const bool v = (lane >> 3) < src.vrope;
+      dma16(v ? (const void*)(src.rope + rope_lane) : (const void*)((const uint8_t*)g_zero_row + (lane << 4)),
+            src.lds + kLatBytes + rope_base * 128);
     }
   };
   auto issue_tile = [&](int t, int blk) __attribute__((always_inline)) {
-    const int tt = wk.tok0 + t * kTileTok;
-    const int r0 = (tt & 63) + wave * 8;
-    const uint32_t tl = tiles_lds + (t % kBuf) * kTileBytes;
-    const uint8_t* rp = a.latent + blk * a.lat_bs + (int64_t)r0 * a.lat_rs;
-    const uint8_t* rr = a.rope + blk * a.rope_bs + (int64_t)r0 * a.rope_rs;
-    const int valid_rows = wk.len - tt - wave * 8;  // rows j < valid_rows hold tokens
-    if (valid_rows >= 8) {
+    const TileSrc src = tile_src(t, blk);
 #pragma unroll
-      for (int j = 0; j < 9; ++j) tile_chunk(t, blk, j);
-    } else {  // last page of the sequence: rows past its length read zeros
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sw = ((j & 3) << 2) | ((2 * wave + (j >> 2)) & 3);
-        if (j < valid_rows)
-          dma16s(rp + (int64_t)j * a.lat_rs, (uint32_t)(lane ^ sw) << 4, tl + (wave * 8 + j) * 1024);
-        else
-          dma16s(g_zero_row, (uint32_t)lane << 4, tl + (wave * 8 + j) * 1024);
-      }
-      const uint8_t* src = (lane >> 3) < valid_rows ? rr + rope_lane : (const uint8_t*)g_zero_row + (lane << 4);
-      dma16(src, tl + kLatBytes + wave * 1024);
-    }
-  };
-  auto issue_step = [&](int st, int blk) __attribute__((always_inline)) {
-    if (2 * st < ntiles) issue_tile(2 * st, blk);
-    if (2 * st + 1 < ntiles) issue_tile(2 * st + 1, blk);
+    for (int j = 0; j < 5; ++j) tile_chunk(src, j);
   };
 
-  // first pass: the copies of step 0 overlap the query loads
-  issue_step(0, page_block(0));
+  // ---- this lane's score row: 16 rq + i16
+  const int qrow = row_base + 16 * rq + i16;
+  const int hi_tok = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
 
-  // ---- queries of rows row_base + 32*rg + n32: B operand of the score product
-  const int qrow = row_base + rg * 32 + n32;
-  const bool qvalid = qrow < rows;
-  bf16x8 qf[36];
+  // ---- first pass prologue: stage the block's 64 query rows (q_lat | q_rope,
+  // 72 chunks of 16 bytes each, row stride 73 chunks) over tile buffers 2..3
+  // with DMA, start tiles 0 and 1, then pull the score operand into registers.
   {
-    const int qr = qvalid ? qrow : 0;
-    const uint16_t* ql = a.q_lat + ((int64_t)wk.b * rows + qr) * 512 + 8 * g;
-    const uint16_t* qp = a.q_rope + ((int64_t)wk.b * rows + qr) * 64 + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < 32; ++kb) qf[kb] = as_bf16x8(*(const u32x4*)(ql + kb * 16));
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qf[32 + kb] = as_bf16x8(*(const u32x4*)(qp + kb * 16));
-    if (!qvalid)
-#pragma unroll
-      for (int kb = 0; kb < 36; ++kb) qf[kb] = as_bf16x8(u32x4{0, 0, 0, 0});
-    // the query loads (and the step-0 copies) complete here, where the
-    // compiler sees it, so it never waits on later copies when Q is used
-    wait_all_vmem();
+    const int64_t qbase = (int64_t)wk.b * rows;
+    for (int i = wave; i < (64 * kQStride) / 64; i += 8) {
+      const int sl = i * 64 + lane;
+      const int r = sl / kQStride, c = sl - r * kQStride;
+      const int qr = min(row_base + r, rows - 1);
+      const uint8_t* src = c < 64 ? (const uint8_t*)(a.q_lat + (qbase + qr) * 512 + c * 8)
+                                  : (const uint8_t*)(a.q_rope + (qbase + qr) * 64 + (c < 72 ? c - 64 : 0) * 8);
+      dma16(src, tiles_lds + kQBase + i * 1024);
+    }
   }
-  // a row's query sees tokens < its horizon; the chunk ends at tok1
-  const int qi = qvalid ? qrow / a.heads : 0;
-  const int hi_tok = min(wk.tok1, qvalid ? wk.len - (a.sq - 1 - qi) : 0);
-  const int hi_min = min(wk.tok1, wk.len - (a.sq - 1));
+  const int blk_a = tile_block(0), blk_b = tile_block(1);
+  issue_tile(0, blk_a);
+  issue_tile(1, blk_b);
+  wait_vmcnt<10>();  // the queries (tiles 0 and 1 may still be in flight)
+  wg_barrier();
+  bf16x8 qf[18];  // B operand: row 16 rq + i16, chunk 4 ks + q4
+  {
+    const int r = 16 * rq + i16;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks)
+      qf[ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + 4 * ks + q4) * 16);
+  }
+  wg_barrier();  // every wave holds its queries: tiles 2, 3 and P are free
 
-  // ---- per-lane LDS offsets (the tile buffer adds a constant)
-  // score operand: latent row n32, chunk 2kb+g; RoPE row n32, chunk 2(kb-32)+g
-  const uint32_t c1_lat = n32 * 1024 + th * kTileBytes;
-  const uint32_t lat_x = (16 * g) ^ (16 * s16(n32));
-  const uint32_t c1_rope = kLatBytes + n32 * 128 + th * kTileBytes;
-  const uint32_t rope_x = (16 * g) ^ (16 * s8(n32));
-  // value operand (transposing reads): token row 16hb + 8j2 + 4g + i/4, columns
-  // 128*wave + 32*mt + 16*(lane/16 % 2) + 4*(i%4), i = lane % 16
-  const int i16 = lane & 15;
+  // ---- per-lane LDS offsets
+  // score operand: tile row 16 th + i16, chunk 4 ks + q4 (latent ks < 16, RoPE after)
+  const int tr = 16 * th + i16;
+  uint32_t c1_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c1_off[k] = tr * 1024 + (((4 * k + q4) ^ s16(tr)) << 4);
+  uint32_t c1_rope[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
+  // value operand (transposing reads): token row 16 ks + 8 j2 + 4 g + i16/4 of
+  // the tile, latent columns 64 wave + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
   const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
-  uint32_t voff[2][4];
+  uint32_t voff[2][2];
 #pragma unroll
   for (int j2 = 0; j2 < 2; ++j2) {
     const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + wave * 256 + (((4 * mt) ^ vy ^ sw) << 4) + (i16 & 1) * 8;
+    for (int mt = 0; mt < 2; ++mt)
+      voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + (((8 * wave + 4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
   }
+  // P^T operand of the value product: row R = 32 nt + n32, 16-byte chunk 2 ks + g
+  // holding tokens 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot
+  // 4 R + (chunk ^ (R/4 % 4)) of the tile's P buffer (rows 32.. are 2048 bytes on)
+  uint32_t pread[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
+  // P write of a score lane: row 16 rq + i16, tokens 16 th + 4 q4 + 0..3
+  const int prow = 16 * rq + i16;
+  const uint32_t pwrite = (4 * prow + ((2 * th + (q4 & 1)) ^ ((prow >> 2) & 3))) * 16 + 8 * (q4 >> 1);
 
   // ---- accumulators.  A row's reference max m_ref is fixed at its first
-  // finite step maximum, so P and O never need rescaling.  If a later score
-  // exceeds it by more than 2^kRefSlack the pass is finished (its values are
-  // discarded) and repeated with the row's chunk maximum as the reference:
-  // exact either way, and never taken unless the scores of one row span more
-  // than 44 nats.
-  f32x16 oacc[4][2];
-  float m_ref = -__builtin_inff();   // this lane's score row (log2 domain)
-  float m_hi = -__builtin_inff();    // largest step maximum seen this pass
-  float l_part = 0.f;                // this lane's share of the row sum
-  bool ovf = false;
+  // tile, so P and O never need rescaling.  If a later score exceeds it by
+  // more than 2^kRefSlack the pass is finished (its values are discarded)
+  // and repeated with the row's chunk maximum as the reference: exact either
+  // way, and never taken unless the scores of one row span more than 44 nats.
+  f32x16 oacc[2][2];
+  float m_ref = -__builtin_inff();
+  float m_hi, l_part;
+  bool ovf;
 
-  auto run_step = [&](int st, int& blk_next, bool set_ref, auto parc) __attribute__((always_inline)) {
-    constexpr int par = decltype(parc)::value;  // st & 1: which half of the tile ring
-    // tiles of step st-1 are free (barrier 2 of the previous step): prefetch
-    // step st+1.  When both of its tiles are full (every step but a
-    // sequence's last page), the 18 copies are spread over the score
-    // product below, one per two MFMAs, so that the wave never stalls on a
-    // full memory queue with no matrix work in flight.
-    const int blk_cur = blk_next;
-    const bool spread = st + 1 < nsteps && wk.len - (wk.tok0 + (2 * st + 2) * kTileTok) >= 2 * kTileTok;
-    if (st + 1 < nsteps && !spread) issue_step(st + 1, blk_cur);
-    blk_next = page_block(st + 2);
-    const bool own_valid = 2 * st + th < ntiles;
-    const bool second_valid = 2 * st + 1 < ntiles;
-    const int tt = wk.tok0 + (2 * st + th) * kTileTok;
-
-    // ---- scores S^T[token][row] for this wave's token half, K = 576
-    float p[16];
-    if (own_valid) {
-      const MLA_LDS uint8_t* tb = tiles + 2 * par * kTileBytes;
-      auto ldA = [&](int kb) __attribute__((always_inline)) -> bf16x8 {
-        if (kb < 32)
-          return *(const MLA_LDS bf16x8*)(tb + c1_lat + (kb >> 3) * 256 + (((kb & 7) * 32) ^ lat_x));
-        return *(const MLA_LDS bf16x8*)(tb + c1_rope + (((kb - 32) * 32) ^ rope_x));
-      };
-      constexpr int kDepth = 8;
-      f32x16 sacc = f32x16{};
-      bf16x8 ar[kDepth];
+  // value-product operands of one 16-token half (ks) of tile t
+  auto values_load = [&](int t, int ks, bf16x8 (&av)[2], bf16x8 (&bp)[2]) __attribute__((always_inline)) {
+    const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 1024;
+    const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes + pread[ks];
 #pragma unroll
-      for (int kb = 0; kb < kDepth; ++kb) ar[kb] = ldA(kb);
-      if (spread) {
-#pragma unroll
-        for (int kb = 0; kb < 36; ++kb) {
-          sacc = mfma32x32x16(ar[kb % kDepth], qf[kb], sacc);
-          if (kb + kDepth < 36) ar[kb % kDepth] = ldA(kb + kDepth);
-          if ((kb & 1) == 0) tile_chunk(2 * st + 2 + (kb >= 18), blk_cur, (kb >> 1) % 9);
-          sched_fence();
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 36; ++kb) {
-          sacc = mfma32x32x16(ar[kb % kDepth], qf[kb], sacc);
-          if (kb + kDepth < 36) ar[kb % kDepth] = ldA(kb + kDepth);
-          sched_fence();
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = sacc[r] * a.scale_log2;
-      if (tt + kTileTok > hi_min) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = tt + (r >> 2) * 8 + 4 * g + (r & 3);
-          if (tok >= hi_tok) p[r] = -__builtin_inff();
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = -__builtin_inff();
+    for (int mt = 0; mt < 2; ++mt) {
+      const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
+      const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
+      av[mt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
-    // value operand of the first 16-token block: issued now, used after barrier 1
-    auto ldV = [&](int kb, bf16x8 (&av)[4]) __attribute__((always_inline)) {
-      const MLA_LDS uint8_t* vt = tiles + (2 * par + (kb >> 1)) * kTileBytes + (kb & 1) * 16 * 1024;
+    bp[0] = *(const MLA_LDS bf16x8*)(pb);
+    bp[1] = *(const MLA_LDS bf16x8*)(pb + 2048);
+  };
+  // MFMA i of a half: O^T[cols 32 (i/2)..][rows 32 (i%2)..]
+  auto values_mfma = [&](int i, const bf16x8 (&av)[2], const bf16x8 (&bp)[2]) __attribute__((always_inline)) {
+    oacc[i >> 1][i & 1] = mfma32x32x16(av[i >> 1], bp[i & 1], oacc[i >> 1][i & 1]);
+  };
+  auto values_all = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
-        const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
-        av[mt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-      }
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 av[2], bp[2];
+      values_load(t, ks, av, bp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) values_mfma(i, av, bp);
+    }
+  };
+
+  // scores of tile s: 18 k-steps (16x16x32).  `hook(ks)` runs after k-step ks.
+  auto scores = [&](int s, f32x4& sacc, auto hook) __attribute__((always_inline)) {
+    const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
+    auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
+      if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + c1_off[ks & 3] + (ks >> 2) * 256);
+      return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
     };
-    bf16x8 av[4];
-    ldV(0, av);
-
-    float mx = p[0];
+    constexpr int kDepth = 4;
+    sacc = f32x4{};
+    bf16x8 ar[kDepth];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, p[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (set_ref) {
-      // first step of the first pass (workgroup-uniform): the two token halves
-      // agree on each row's reference.  A row left at -inf here sees no token
-      // of this chunk at all (a row's visible tokens are a prefix of it).
-      if (lane < 32) xm[th * 64 + rg * 32 + lane] = mx;
-      wg_barrier();
-      mx = fmaxf(mx, xm[(th ^ 1) * 64 + rg * 32 + n32]);
-      m_ref = mx;
+    for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      sacc = mfma16x16x32(ar[ks % kDepth], qf[ks], sacc);
+      if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
+      hook(ks);
+      sched_fence();
     }
-    m_hi = fmaxf(m_hi, mx);
-    if (mx > m_ref + kRefSlack) ovf = true;
-    const float mu = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+  };
+
+  // softmax of tile s: lane holds tokens 16 th + 4 q4 + r of row 16 rq + i16
+  float p[4], mx;
+  auto soft_scale = [&](int s, const f32x4& sacc) __attribute__((always_inline)) {
+    const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 4; ++r) {
+      const float x = sacc[r] * a.scale_log2;
+      p[r] = tt + r < hi_tok ? x : -__builtin_inff();
+    }
+    mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+  };
+  auto soft_track = [&]() __attribute__((always_inline)) {
+    m_hi = fmaxf(m_hi, mx);
+    ovf |= mx > m_ref + kRefSlack;
+  };
+  auto soft_exp = [&]() __attribute__((always_inline)) {
+    const float mu = m_ref == -__builtin_inff() ? 0.f : m_ref;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
       p[r] = exp2f(p[r] - mu);
       l_part += p[r];
     }
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const u32x4 pk = {pack_bf16x2(p[8 * hb + 0], p[8 * hb + 1]), pack_bf16x2(p[8 * hb + 2], p[8 * hb + 3]),
-                        pack_bf16x2(p[8 * hb + 4], p[8 * hb + 5]), pack_bf16x2(p[8 * hb + 6], p[8 * hb + 7])};
-      *(MLA_LDS u32x4*)(pl + ((rg * 4 + 2 * th + hb) * 64 + lane) * 16) = pk;
-    }
-    wg_barrier();  // ---- barrier 1: P visible
-
-    // ---- values: O^T[columns 128w..][64 rows] += C^T[.., 64 tokens] P^T
-    const int nkb = second_valid ? 4 : 2;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb >= nkb) break;
-      const bf16x8 b0 = *(const MLA_LDS bf16x8*)(pl + ((0 * 4 + kb) * 64 + lane) * 16);
-      const bf16x8 b1 = *(const MLA_LDS bf16x8*)(pl + ((1 * 4 + kb) * 64 + lane) * 16);
-      bf16x8 an[4];
-      if (kb + 1 < nkb) ldV(kb + 1, an);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        oacc[mt][0] = mfma32x32x16(av[mt], b0, oacc[mt][0]);
-        oacc[mt][1] = mfma32x32x16(av[mt], b1, oacc[mt][1]);
-      }
-      sched_fence();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) av[mt] = an[mt];
-    }
-    // ---- barrier 2: P may be overwritten, step st's tiles are free, step st+1 resident
-    wait_vmcnt<0>();
-    wg_barrier();
+  };
+  auto soft_store = [&](int s) __attribute__((always_inline)) {
+    const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    *(MLA_LDS u32x2*)(pbuf + (s & 1) * kPBytes + pwrite) = pk;
   };
 
-  for (bool first = true;; first = false) {  // one pass; repeated only after an overflow
+  // One pass; repeated once after an overflow.  The repeat uses each row's
+  // chunk maximum as its reference, so it cannot overflow again: two passes
+  // at most.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool first = pass == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) oacc[i][j] = f32x16{};
     l_part = 0.f;
+    m_hi = -__builtin_inff();
     ovf = false;
-    if (!first) issue_step(0, page_block(0));
-    wait_vmcnt<0>();
+    if (!first) {
+      issue_tile(0, blk_a);
+      issue_tile(1, blk_b);
+    }
+    wait_vmcnt<5>();  // tile 0 (tile 1 may still be in flight)
     wg_barrier();
 
-    int blk_next = page_block(1);
-    for (int st = 0; st < nsteps; st += 2) {
-      run_step(st, blk_next, first && st == 0, std::integral_constant<int, 0>{});
-      if (st + 1 < nsteps) run_step(st + 1, blk_next, false, std::integral_constant<int, 1>{});
+    // ---- tile 0: scores, the rows' reference maxima, softmax
+    int blk_next = tile_block(3);
+    if (ntiles > 0) {
+      issue_tile(2, tile_block(2));
+      f32x4 sacc;
+      scores(0, sacc, [](int) {});
+      soft_scale(0, sacc);
+      if (first) {
+        // each row's maximum over the whole first tile (both token halves);
+        // a row left at -inf sees no token of this chunk
+        float m = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (q4 == 0) xm[th * 64 + prow] = m;
+        wg_barrier();
+        m_ref = fmaxf(m, xm[(th ^ 1) * 64 + prow]);
+        mx = m;
+      }
+      soft_track();
+      soft_exp();
+      soft_store(0);
+      wait_vmcnt<5>();
+      wg_barrier();
     }
-    // ---- did any row overflow its reference?  (its pair partner may not know)
-    if (lane < 32) xm[th * 64 + rg * 32 + lane] = m_hi;
+
+    // ---- tiles 1 ..: scores of tile s with the first half of tile s-1's
+    // value product and the copies of tile s+2 between them; then the
+    // softmax of tile s with the second half between its parts.  Tile s+2
+    // goes into the buffer tile s-2 used (free since the last barrier).
+    for (int s = 1; s < ntiles; ++s) {
+      const TileSrc nsrc = tile_src(s + 2, blk_next);
+      blk_next = tile_block(s + 3);
+      f32x4 sacc;
+      bf16x8 av[2], bp[2];
+      values_load(s - 1, 0, av, bp);
+      scores(s, sacc, [&](int ks) __attribute__((always_inline)) {
+        if ((ks & 3) == 3 && ks < 16) values_mfma(ks >> 2, av, bp);
+        if ((ks & 3) == 1 && ks < 16) tile_chunk(nsrc, ks >> 2);
+      });
+      values_load(s - 1, 1, av, bp);
+      soft_scale(s, sacc);
+      values_mfma(0, av, bp);
+      sched_fence();
+      soft_track();
+      soft_exp();
+      values_mfma(1, av, bp);
+      sched_fence();
+      soft_store(s);
+      values_mfma(2, av, bp);
+      tile_chunk(nsrc, 4);
+      values_mfma(3, av, bp);
+      sched_fence();
+
+      // ---- tile s+1 resident (tile s+2's copies may stay in flight), P(s) visible
+      wait_vmcnt<5>();
+      wg_barrier();
+    }
+    wait_vmcnt<0>();  // copies issued for tiles past the chunk have landed
+    if (ntiles > 0) values_all(ntiles - 1);
+
+    // ---- did any row overflow its reference?  (its partner lanes may not know)
+    {
+      float m = fmaxf(m_hi, __shfl_xor(m_hi, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      m_hi = m;
+      if (q4 == 0) xm[th * 64 + prow] = m;
+    }
     // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
-    // would see lane 0's row alone)
+    // would see lane 0's rows alone)
     const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
     if (lane == 0) xf[wave] = wave_ovf;
     wg_barrier();
-    const bool again = xf[0] | xf[1] | xf[2] | xf[3];
-    if (!again) break;
-    m_ref = fmaxf(m_hi, xm[(th ^ 1) * 64 + rg * 32 + n32]);  // the row's chunk maximum
-    m_hi = -__builtin_inff();
+    bool again = false;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) again |= xf[w] != 0;
+    if (!again || !first) break;
+    m_ref = fmaxf(m_hi, xm[(th ^ 1) * 64 + prow]);
     wg_barrier();
   }
 
-  // ---- epilogue: complete row sums (two lane halves x two token halves)
-  const float l_half = l_part + __shfl_xor(l_part, 32, 64);
-  if (lane < 32) xm[th * 64 + rg * 32 + lane] = l_half;
+  // ---- epilogue: row sums (4 token quads x 2 token halves)
+  {
+    float l = l_part + __shfl_xor(l_part, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (q4 == 0) xl[th * 64 + prow] = l;
+  }
   wg_barrier();
-  if (lane < 32 && th == 0) {
-    const float lt = l_half + xm[64 + rg * 32 + lane];
-    xl[rg * 32 + lane] = lt;
-    if (qvalid) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -__builtin_inff();
+  if (th == 0 && q4 == 0) {
+    const float lt = xl[prow] + xl[64 + prow];
+    xm[prow] = lt;
+    if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -__builtin_inff();
   }
   wg_barrier();
   float* obase = a.o + slot * (int64_t)rows * 512;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int row = row_base + nt * 32 + n32;
-    const float lt = xl[nt * 32 + n32];
+    const float lt = xm[nt * 32 + n32];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float* orow = obase + (int64_t)row * 512 + wave * 128;
+    float* orow = obase + (int64_t)row * 512 + wave * 64;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 v = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
