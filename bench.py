@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time steps without cache eviction")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run three 256 MiB device-to-device copies and exit (the known-size reference "
+                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -99,6 +102,14 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
     import mla_inputs as MI
     from mla_latent_kv_17_amd.runner import DecodeStep, DeviceInputs
 

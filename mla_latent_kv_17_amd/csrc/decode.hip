@@ -303,21 +303,27 @@ decode_mfma_bf16(const DecodeArgs a) {
   issue_tile(1, blk_b);
   wait_vmcnt<10>();  // the queries (tiles 0 and 1 may still be in flight)
   wg_barrier();
-  bf16x8 qf[18];  // B operand: row 16 rq + i16, chunk 4 ks + q4
+  // B operand of k-step ks: row 16 rq + i16; latent chunk ks + 16 q4 for
+  // ks < 16 (each lane quarter walks its own quarter of the row: with the
+  // tile swizzle below this order keeps the tile reads free of bank
+  // conflicts, measured), RoPE chunk 4 (ks - 16) + q4 after
+  bf16x8 qf[18];
   {
     const int r = 16 * rq + i16;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks)
-      qf[ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + 4 * ks + q4) * 16);
+    for (int ks = 0; ks < 18; ++ks) {
+      const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
+      qf[ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + c) * 16);
+    }
   }
   wg_barrier();  // every wave holds its queries: tiles 2, 3 and P are free
 
   // ---- per-lane LDS offsets
-  // score operand: tile row 16 th + i16, chunk 4 ks + q4 (latent ks < 16, RoPE after)
+  // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits at byte
+  // 1024 row + 256 q4 + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4); RoPE
+  // chunk 4 (ks - 16) + q4 after the latent part
   const int tr = 16 * th + i16;
-  uint32_t c1_off[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) c1_off[k] = tr * 1024 + (((4 * k + q4) ^ s16(tr)) << 4);
+  const uint32_t c1_lat = tr * 1024 + q4 * 256 + (s16(tr) << 4);
   uint32_t c1_rope[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
@@ -383,7 +389,7 @@ decode_mfma_bf16(const DecodeArgs a) {
   auto scores = [&](int s, f32x4& sacc, auto hook) __attribute__((always_inline)) {
     const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
     auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
-      if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + c1_off[ks & 3] + (ks >> 2) * 256);
+      if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + (c1_lat ^ (uint32_t)(ks << 4)));
       return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
     };
     constexpr int kDepth = 4;
@@ -415,11 +421,13 @@ decode_mfma_bf16(const DecodeArgs a) {
     m_hi = fmaxf(m_hi, mx);
     ovf |= mx > m_ref + kRefSlack;
   };
+  // hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which
+  // cannot matter next to the row's largest weight (>= 1 after the first tile)
   auto soft_exp = [&]() __attribute__((always_inline)) {
     const float mu = m_ref == -__builtin_inff() ? 0.f : m_ref;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = exp2f(p[r] - mu);
+      p[r] = __builtin_amdgcn_exp2f(p[r] - mu);
       l_part += p[r];
     }
   };
