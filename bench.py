@@ -193,6 +193,8 @@ def main():
                    "steps_timed": "absorb_q + decode + split_combine + out_uv, caches evicted before each"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
+                                     "calibrated on a 256 MiB copy)",
                      "kernel": "decode_mfma_bf16", "launch_ms": dec_avg,
                      "algorithmic_bytes": cache_bytes},
         "decode_tflops": decode_flops / (dec_avg * 1e-3) / 1e12,
