@@ -10,8 +10,9 @@ synthetic workload B=32, H=128, T=4096, bf16 cache/queries/weights
 Before every timed step an untimed read of a 1 GiB buffer evicts the 256 MB
 Infinity Cache and the L2s, so the step streams its cache and weights from
 HBM as it would with other layers' data in between.  HIP events on the
-stream the library launches on (torch's current stream) time each step and
-each decode launch.  Prints one JSON line.
+stream the library launches on (torch's current stream) time each decode
+launch and each step (eager launches; --graph also times the step replayed
+from a HIP graph of the four calls).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -91,6 +92,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time steps without cache eviction")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph of the four calls (checked bit for bit "
+                         "against the eager step; not the headline: eager launches are already queued behind "
+                         "the eviction read, so a graph removes no gap and adds its own launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run three 256 MiB device-to-device copies and exit (the known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -170,7 +175,39 @@ def main():
         torch.cuda.synchronize()
         warm_ms = w0.elapsed_time(w1) / K
 
-    ms_per_step = float(step_ms.mean())
+    # the same four calls captured once as a HIP graph and replayed: the
+    # library allocates nothing and issues no memsets, so the step captures
+    # as is; the replay must reproduce the eager result bit for bit
+    graph_ms = None
+    if args.graph:
+        ref_out = step.run().clone()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step.run()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.run()
+        for _ in range(2):
+            do_flush()
+            graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(step.out, ref_out):
+            print("bench.py: graph replay differs from the eager step", file=sys.stderr)
+            sys.exit(1)
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            do_flush()
+            gev[i][0].record()
+            graph.replay()
+            gev[i][1].record()
+        torch.cuda.synchronize()
+        graph_ms = np.array([a.elapsed_time(b) for a, b in gev])
+
+    eager_ms_per_step = float(step_ms.mean())
+    ms_per_step = eager_ms_per_step
     dec_avg = float(dec_ms.mean())
     achieved = cache_bytes / (dec_avg * 1e-3)
     traffic = measured_traffic()
@@ -201,6 +238,7 @@ def main():
         "decode_mfma_frac": decode_flops / (dec_avg * 1e-3) / MFMA_BF16_PEAK,
         "kv_tokens_per_step": kv_tokens,
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "graph_ms_per_step": float(graph_ms.mean()) if graph_ms is not None else None,
         "decode_ms_p10_p50_p90": [float(np.percentile(dec_ms, q)) for q in (10, 50, 90)],
         "step_tflops": (decode_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
         "warm_ms_per_step": warm_ms,
