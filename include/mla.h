@@ -85,7 +85,8 @@ typedef struct mla_dims {
  *                (d_latent values of latent_dtype)
  *   rope row:    rope   + block * rope_block_stride   + row * rope_row_stride
  *                (d_rope values of rope_dtype)
- *   fp8 scale:   scale[block * scale_block_stride + row]  (fp32; fp8 only)
+ *   fp8 scale:   scale[block * scale_block_stride + row]  (fp32; fp8 only;
+ *                `scale` 16-byte aligned, scale_block_stride a multiple of 4)
  *
  * The 576-wide interleaved layout [c | k^R] is rope = latent + 512 with both
  * row strides 576 and both block strides 64 * 576.  Supported combinations:

@@ -123,7 +123,7 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   const int64_t rope_rs = kv->rope_row_stride * res, rope_bs = kv->rope_block_stride * res;
   if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(o) || !aligned16(kv->latent) ||
       !aligned16(kv->rope) || (lat_rs & 15) || (lat_bs & 15) || (rope_rs & 15) || (rope_bs & 15) ||
-      (fmt == 2 && ((uintptr_t)kv->scale & 3)))
+      (fmt == 2 && (((uintptr_t)kv->scale & 15) || (kv->scale_block_stride & 3))))
     return MLA_ERR_ALIGN;
   const int rows = dims->q_per_seq * dims->heads;
   if (dims->batch == 0) return MLA_OK;
@@ -156,18 +156,19 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   a.softmax_scale = dims->softmax_scale;
   a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
-  if (fmt == 1) {
+  if (fmt == 1 || fmt == 2) {
+    // matrix-core kernels: 8 waves per (sequence, chunk, 64-row block)
     const int64_t padded = (units + 7) / 8 * 8;
     const int64_t grid = padded * a.row_blocks;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    st = launch("mla::decode_mfma_bf16", (const void*)mla::decode_mfma_bf16, dim3((unsigned)grid), dim3(512), a, s);
+    if (fmt == 1)
+      st = launch("mla::decode_mfma_bf16", (const void*)mla::decode_mfma_bf16, dim3((unsigned)grid), dim3(512), a, s);
+    else
+      st = launch("mla::decode_mfma_fp8", (const void*)mla::decode_mfma_fp8, dim3((unsigned)grid), dim3(512), a, s);
   } else {
     const int64_t grid = units * rows;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    if (fmt == 0)
-      st = launch("mla::decode_scalar<0>", (const void*)mla::decode_scalar<0>, dim3((unsigned)grid), dim3(256), a, s);
-    else
-      st = launch("mla::decode_scalar<2>", (const void*)mla::decode_scalar<2>, dim3((unsigned)grid), dim3(256), a, s);
+    st = launch("mla::decode_scalar<0>", (const void*)mla::decode_scalar<0>, dim3((unsigned)grid), dim3(256), a, s);
   }
   return st;
 }

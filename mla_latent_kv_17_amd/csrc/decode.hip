@@ -567,6 +567,385 @@ decode_mfma_bf16(const DecodeArgs a) {
   }
 }
 
+// E4M3 cache (fp8 codes + fp32 per-token scale, bf16 k^R).  Same workgroup
+// shape, roles and tile pipeline as decode_mfma_bf16; the tiles are staged
+// through registers instead of LDS DMA because the codes are converted to
+// bf16 on the way (exactly: a 3-bit mantissa and the E4M3 exponent range fit
+// bf16), into the same swizzled LDS layout.  The per-token scale is applied
+// in fp32 to the latent part of each score (kept in its own accumulator) and
+// folded into P for the value product, so no dequantized value is rounded.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_mfma_fp8(const DecodeArgs a) {
+  constexpr int kBuf = 4;                         // tile ring
+  constexpr int kPBytes = 64 * 32 * 2;            // P of one tile: 64 rows x 32 tokens bf16
+  constexpr int kQStride = 73;                    // staged query row: 72 chunks + 1 pad
+  constexpr int kQBase = 2 * kTileBytes;          // queries are staged over tiles 2, 3 (+ P)
+  constexpr int kXOff = kBuf * kTileBytes + 2 * kPBytes;
+  static_assert(kQBase + 64 * kQStride * 16 <= kXOff, "query staging must fit before the exchange area");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280];
+  MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)&smem[0];
+  MLA_LDS uint8_t* const pbuf = tiles + kBuf * kTileBytes;
+  MLA_LDS float* const xm = (MLA_LDS float*)(tiles + kXOff);  // [2 token halves][64 rows]
+  MLA_LDS float* const xl = xm + 128;                         // [2][64] row sums
+  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 128);           // [8] overflow flags
+
+  // the roles below assume exactly eight waves
+  if (blockDim.x != 512) return;
+  Work wk;
+  if (!decode_work(a, wk)) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, 0..7
+  const int lane = tid & 63;
+  const int g = lane >> 5;        // k-half of a 32x32 operand
+  const int n32 = lane & 31;
+  const int q4 = lane >> 4;       // k-quarter of a 16x16 operand / token quad of its result
+  const int i16 = lane & 15;
+  const int th = wave & 1;        // score token half of a tile
+  const int rq = wave >> 1;       // score row quarter of the block
+  const int rows = a.rows;
+  const int row_base = wk.rb * kRowsPerWg;
+  const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
+  const int ntiles = wk.ntiles;
+  const uint32_t tiles_lds = lds_addr(tiles);
+
+  // ---- HBM -> registers -> LDS copies of one tile.  Wave w stages latent
+  // rows 4w + lane/16 (codes 8 (16 k + lane%16) .. +7 for k = 0..3, four
+  // 8-byte loads, converted exactly to bf16 and written as 16-byte chunks
+  // 16 k + lane%16 of the swizzled row) and the 8-byte RoPE piece lane%16 of
+  // the same row.  Rows at or past the sequence's length read zeros.  All
+  // loads are ordinary (compiler-tracked) loads.
+  const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
+  auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
+    return t < ntiles ? load_uniform(a.block_table, bt_row + ((wk.tok0 + t * kTileTok) >> 6)) : 0;
+  };
+  const int srow = 4 * wave + (lane >> 4);  // staged tile row of this lane
+  const int si = lane & 15;
+  struct Staged {
+    u32x2 lat[4];
+    u32x2 rope;
+  };
+  auto stage_load = [&](int t, int blk, Staged& st) __attribute__((always_inline)) {
+    const int tt = wk.tok0 + t * kTileTok;
+    const bool v = t < ntiles && tt + srow < wk.len;
+    const uint8_t* lp = v ? a.latent + blk * a.lat_bs + (int64_t)((tt & 63) + srow) * a.lat_rs + 8 * si
+                          : (const uint8_t*)g_zero_row;
+    const uint8_t* rp = v ? a.rope + blk * a.rope_bs + (int64_t)((tt & 63) + srow) * a.rope_rs + 8 * si
+                          : (const uint8_t*)g_zero_row;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st.lat[k] = *(const u32x2*)(lp + (v ? 128 * k : 0));
+    st.rope = *(const u32x2*)rp;
+  };
+  auto stage_store = [&](int t, const Staged& st) __attribute__((always_inline)) {
+    MLA_LDS uint8_t* tb = tiles + (t % kBuf) * kTileBytes;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 w = {e4m3x2_to_bf16x2<false>(st.lat[k][0]), e4m3x2_to_bf16x2<true>(st.lat[k][0]),
+                       e4m3x2_to_bf16x2<false>(st.lat[k][1]), e4m3x2_to_bf16x2<true>(st.lat[k][1])};
+      *(MLA_LDS u32x4*)(tb + srow * 1024 + 256 * k + ((si ^ s16(srow)) << 4)) = w;
+    }
+    *(MLA_LDS u32x2*)(tb + kLatBytes + (srow * 8 + ((si >> 1) ^ s8(srow))) * 16 + (si & 1) * 8) = st.rope;
+  };
+
+  // ---- this lane's score row: 16 rq + i16
+  const int qrow = row_base + 16 * rq + i16;
+  const int hi_tok = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
+
+  // ---- first pass prologue: stage the block's 64 query rows (q_lat | q_rope,
+  // 72 chunks of 16 bytes each, row stride 73 chunks) over tile buffers 2..3
+  // with DMA, start tiles 0 and 1, then pull the score operand into registers.
+  {
+    const int64_t qbase = (int64_t)wk.b * rows;
+    for (int i = wave; i < (64 * kQStride) / 64; i += 8) {
+      const int sl = i * 64 + lane;
+      const int r = sl / kQStride, c = sl - r * kQStride;
+      const int qr = min(row_base + r, rows - 1);
+      const uint8_t* src = c < 64 ? (const uint8_t*)(a.q_lat + (qbase + qr) * 512 + c * 8)
+                                  : (const uint8_t*)(a.q_rope + (qbase + qr) * 64 + (c < 72 ? c - 64 : 0) * 8);
+      dma16(src, tiles_lds + kQBase + i * 1024);
+    }
+  }
+  wait_vmcnt<0>();  // the staged queries (the only copies in flight)
+  wg_barrier();
+  bf16x8 qf[18];
+  {
+    const int r = 16 * rq + i16;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
+      qf[ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + c) * 16);
+    }
+  }
+  wg_barrier();  // every wave holds its queries: tiles 2, 3 and P are free
+
+  // ---- per-lane LDS offsets
+  // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits at byte
+  // 1024 row + 256 q4 + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4); RoPE
+  // chunk 4 (ks - 16) + q4 after the latent part
+  const int tr = 16 * th + i16;
+  const uint32_t c1_lat = tr * 1024 + q4 * 256 + (s16(tr) << 4);
+  uint32_t c1_rope[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
+  // value operand (transposing reads): token row 16 ks + 8 j2 + 4 g + i16/4 of
+  // the tile, latent columns 64 wave + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
+  const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
+  uint32_t voff[2][2];
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2) {
+    const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + (((8 * wave + 4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
+  }
+  // P^T operand of the value product: row R = 32 nt + n32, 16-byte chunk 2 ks + g
+  // holding tokens 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot
+  // 4 R + (chunk ^ (R/4 % 4)) of the tile's P buffer (rows 32.. are 2048 bytes on)
+  uint32_t pread[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
+  // P write of a score lane: row 16 rq + i16, tokens 16 th + 4 q4 + 0..3
+  const int prow = 16 * rq + i16;
+  const uint32_t pwrite = (4 * prow + ((2 * th + (q4 & 1)) ^ ((prow >> 2) & 3))) * 16 + 8 * (q4 >> 1);
+
+  // ---- accumulators.  A row's reference max m_ref is fixed at its first
+  // tile, so P and O never need rescaling.  If a later score exceeds it by
+  // more than 2^kRefSlack the pass is finished (its values are discarded)
+  // and repeated with the row's chunk maximum as the reference: exact either
+  // way, and never taken unless the scores of one row span more than 44 nats.
+  f32x16 oacc[2][2];
+  float m_ref = -__builtin_inff();
+  float m_hi, l_part;
+  bool ovf;
+
+  // value-product operands of one 16-token half (ks) of tile t
+  auto values_load = [&](int t, int ks, bf16x8 (&av)[2], bf16x8 (&bp)[2]) __attribute__((always_inline)) {
+    const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 1024;
+    const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes + pread[ks];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
+      const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
+      av[mt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+    bp[0] = *(const MLA_LDS bf16x8*)(pb);
+    bp[1] = *(const MLA_LDS bf16x8*)(pb + 2048);
+  };
+  // MFMA i of a half: O^T[cols 32 (i/2)..][rows 32 (i%2)..]
+  auto values_mfma = [&](int i, const bf16x8 (&av)[2], const bf16x8 (&bp)[2]) __attribute__((always_inline)) {
+    oacc[i >> 1][i & 1] = mfma32x32x16(av[i >> 1], bp[i & 1], oacc[i >> 1][i & 1]);
+  };
+  auto values_all = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 av[2], bp[2];
+      values_load(t, ks, av, bp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) values_mfma(i, av, bp);
+    }
+  };
+
+  // scores of tile s: 18 k-steps (16x16x32); the latent part (k-steps 0..15)
+  // and the RoPE part (16, 17) accumulate separately because only the former
+  // is scaled.  `hook(ks)` runs after k-step ks.
+  auto scores = [&](int s, f32x4& sacc, f32x4& sacc_r, auto hook) __attribute__((always_inline)) {
+    const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
+    auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
+      if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + (c1_lat ^ (uint32_t)(ks << 4)));
+      return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
+    };
+    constexpr int kDepth = 3;
+    sacc = f32x4{};
+    sacc_r = f32x4{};
+    bf16x8 ar[kDepth];
+#pragma unroll
+    for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      if (ks < 16)
+        sacc = mfma16x16x32(ar[ks % kDepth], qf[ks], sacc);
+      else
+        sacc_r = mfma16x16x32(ar[ks % kDepth], qf[ks], sacc_r);
+      if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
+      hook(ks);
+      sched_fence();
+    }
+  };
+
+  // softmax of tile s: lane holds tokens 16 th + 4 q4 + r of row 16 rq + i16.
+  // Score = scale_t (q_lat . code_t) + q_rope . k^R_t; the value product
+  // takes p_t scale_t against the codes, the row sum p_t.
+  float p[4], mx;
+  f32x4 tscale;  // the lane's four token scales (0 past the row's horizon)
+  auto load_scale = [&](int s, int blk) __attribute__((always_inline)) {
+    const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
+    const bool v = s < ntiles && tt < wk.len;
+    const float* sp = (const float*)(v ? a.kv_scale_bytes + blk * a.scale_bs + (int64_t)(tt & 63) * 4
+                                       : (const uint8_t*)g_zero_row);
+    tscale = *(const f32x4*)sp;
+  };
+  auto soft_scale = [&](int s, const f32x4& sacc, const f32x4& sacc_r) __attribute__((always_inline)) {
+    const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool vis = tt + r < hi_tok;
+      tscale[r] = vis ? tscale[r] : 0.f;
+      const float x = (sacc[r] * tscale[r] + sacc_r[r]) * a.scale_log2;
+      p[r] = vis ? x : -__builtin_inff();
+    }
+    mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+  };
+  auto soft_track = [&]() __attribute__((always_inline)) {
+    m_hi = fmaxf(m_hi, mx);
+    ovf |= mx > m_ref + kRefSlack;
+  };
+  // hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which
+  // cannot matter next to the row's largest weight (>= 1 after the first tile)
+  auto soft_exp = [&]() __attribute__((always_inline)) {
+    const float mu = m_ref == -__builtin_inff() ? 0.f : m_ref;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(p[r] - mu);
+      l_part += p[r];
+    }
+  };
+  auto soft_store = [&](int s) __attribute__((always_inline)) {
+    const u32x2 pk = {pack_bf16x2(p[0] * tscale[0], p[1] * tscale[1]), pack_bf16x2(p[2] * tscale[2], p[3] * tscale[3])};
+    *(MLA_LDS u32x2*)(pbuf + (s & 1) * kPBytes + pwrite) = pk;
+  };
+
+  // One pass; repeated once after an overflow.  The repeat uses each row's
+  // chunk maximum as its reference, so it cannot overflow again: two passes
+  // at most.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool first = pass == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) oacc[i][j] = f32x16{};
+    l_part = 0.f;
+    m_hi = -__builtin_inff();
+    ovf = false;
+    // tiles 0 and 1 into LDS, tile 2 staged in registers
+    Staged st;
+    stage_load(0, tile_block(0), st);
+    stage_store(0, st);
+    stage_load(1, tile_block(1), st);
+    stage_store(1, st);
+    stage_load(2, tile_block(2), st);
+    wg_barrier();  // tiles 0, 1 resident
+
+    // ---- tile 0: scores, the rows' reference maxima, softmax
+    int blk_next = tile_block(3);
+    if (ntiles > 0) {
+      stage_store(2, st);  // buffer 2 held the staged queries, free now
+      stage_load(3, blk_next, st);
+      load_scale(0, tile_block(0));
+      f32x4 sacc, sacc_r;
+      scores(0, sacc, sacc_r, [](int) {});
+      soft_scale(0, sacc, sacc_r);
+      if (first) {
+        // each row's maximum over the whole first tile (both token halves);
+        // a row left at -inf sees no token of this chunk
+        float m = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (q4 == 0) xm[th * 64 + prow] = m;
+        wg_barrier();
+        m_ref = fmaxf(m, xm[(th ^ 1) * 64 + prow]);
+        mx = m;
+      }
+      soft_track();
+      soft_exp();
+      soft_store(0);
+      wg_barrier();
+    }
+
+    // ---- tiles 1 ..: tile s+2 (staged last iteration) goes into the buffer
+    // tile s-2 used, tile s+3 is staged; scores of tile s with the first half
+    // of tile s-1's value product between them, then the softmax of tile s
+    // with the second half between its parts.
+    for (int s = 1; s < ntiles; ++s) {
+      const int blk_s = tile_block(s);
+      stage_store(s + 2, st);
+      const int blk3 = tile_block(s + 3);
+      stage_load(s + 3, blk3, st);
+      load_scale(s, blk_s);
+      f32x4 sacc, sacc_r;
+      bf16x8 av[2], bp[2];
+      values_load(s - 1, 0, av, bp);
+      scores(s, sacc, sacc_r, [&](int ks) __attribute__((always_inline)) {
+        if ((ks & 3) == 3 && ks < 16) values_mfma(ks >> 2, av, bp);
+      });
+      values_load(s - 1, 1, av, bp);
+      soft_scale(s, sacc, sacc_r);
+      values_mfma(0, av, bp);
+      sched_fence();
+      soft_track();
+      soft_exp();
+      values_mfma(1, av, bp);
+      sched_fence();
+      soft_store(s);
+      values_mfma(2, av, bp);
+      values_mfma(3, av, bp);
+      sched_fence();
+      wg_barrier();  // P(s) visible, tile s+1 resident, tile s-1 free
+    }
+    (void)blk_next;
+    if (ntiles > 0) values_all(ntiles - 1);
+
+    // ---- did any row overflow its reference?  (its partner lanes may not know)
+    {
+      float m = fmaxf(m_hi, __shfl_xor(m_hi, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      m_hi = m;
+      if (q4 == 0) xm[th * 64 + prow] = m;
+    }
+    // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
+    // would see lane 0's rows alone)
+    const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
+    if (lane == 0) xf[wave] = wave_ovf;
+    wg_barrier();
+    bool again = false;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) again |= xf[w] != 0;
+    if (!again || !first) break;
+    m_ref = fmaxf(m_hi, xm[(th ^ 1) * 64 + prow]);
+    wg_barrier();
+  }
+
+  // ---- epilogue: row sums (4 token quads x 2 token halves)
+  {
+    float l = l_part + __shfl_xor(l_part, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (q4 == 0) xl[th * 64 + prow] = l;
+  }
+  wg_barrier();
+  if (th == 0 && q4 == 0) {
+    const float lt = xl[prow] + xl[64 + prow];
+    xm[prow] = lt;
+    if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -__builtin_inff();
+  }
+  wg_barrier();
+  float* obase = a.o + slot * (int64_t)rows * 512;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = row_base + nt * 32 + n32;
+    const float lt = xm[nt * 32 + n32];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* orow = obase + (int64_t)row * 512 + wave * 64;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
+                         oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
+        if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = v;
+      }
+      sched_fence();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Plain fp32 path: one workgroup per (sequence, chunk, query row).
 // ---------------------------------------------------------------------------
