@@ -75,7 +75,7 @@ class Workload:
 WORKLOADS = {
     # fp32 everywhere; B=1, H=16, T=1024, contiguous.
     "fp32_b1_h16_t1k": Workload("fp32_b1_h16_t1k", batch=1, q_per_seq=1, heads=16,
-                                cache_dtype="f32", seq_len=1024, seed=1000),
+                                cache_dtype="f32", seq_len=1024, num_splits=0, seed=1000),
     # DeepSeek-V2 head shape, bf16 cache/q/weights; B=32, T=4096, contiguous.
     "bf16_b32_h128_t4k": Workload("bf16_b32_h128_t4k", batch=32, q_per_seq=1, heads=128,
                                   cache_dtype="bf16", seq_len=4096, num_splits=0, seed=1001),

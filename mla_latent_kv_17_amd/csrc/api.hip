@@ -168,7 +168,7 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   } else {
     const int64_t grid = units * rows;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    st = launch("mla::decode_scalar<0>", (const void*)mla::decode_scalar<0>, dim3((unsigned)grid), dim3(256), a, s);
+    st = launch("mla::decode_f32", (const void*)mla::decode_f32, dim3((unsigned)grid), dim3(256), a, s);
   }
   return st;
 }

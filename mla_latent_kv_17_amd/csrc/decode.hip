@@ -8,25 +8,16 @@
 // values", "absorption").  Per query row r and cached token t:
 //     s[r][t] = (q_lat[r] . c_t + q_rope[r] . k^R_t) * scale
 //     o_lat[r] = sum_t softmax(s[r])_t c_t,   lse[r] = ln sum_t exp s[r][t]
+// A KV chunk of a sequence (page-aligned split) yields its own normalised
+// o_lat and lse, merged by split_combine.
 //
-// Two kernels:
-//  * decode_mfma  (bf16 or fp8 cache): one workgroup = 4 waves owns one
-//    (sequence, KV chunk, block of 128 query rows).  32-token tiles of the
-//    576-wide rows are streamed HBM -> LDS (bf16: DMA loads that bypass
-//    registers; fp8: register-staged with E4M3 -> bf16 conversion) into a
-//    ring of tile buffers, and every tile is shared by all 128 rows.
-//      - scores:  wave w computes S^T[32 tokens][its 32 rows] with
-//        v_mfma_f32_32x32x16_bf16, A = cache rows from LDS, B = its queries
-//        (held in registers for the whole kernel), K = 576.
-//      - softmax: exp2-domain online softmax with a lazy reference max (the
-//        accumulator is rescaled only when a row's max grows by more than
-//        2^8), row sums kept per lane.
-//      - values:  P is exchanged through LDS and wave w accumulates
-//        O^T[its 128 latent columns][all 128 rows] += C^T P^T, A = cache
-//        columns read with the gfx950 transposing LDS load, so each cache
-//        element is read from LDS once per workgroup for this product.
-//  * decode_scalar (fp32 cache, and any dtype as a plain second path):
-//    one workgroup per (sequence, chunk, query row), fp32 VALU.
+// Three kernels:
+//  * decode_mfma_bf16 (bf16 cache): eight waves per (sequence, chunk, block
+//    of 64 query rows), 32-token tiles streamed HBM -> LDS by DMA, both
+//    contractions on the matrix cores, fixed per-row softmax reference.
+//  * decode_mfma_fp8 (E4M3 cache + fp32 token scales): the same pipeline with
+//    register-staged tiles converted to bf16 and the scales applied in fp32.
+//  * decode_f32 (fp32 cache): fp32 VALU, one workgroup per query row.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -947,12 +938,17 @@ decode_mfma_fp8(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Plain fp32 path: one workgroup per (sequence, chunk, query row).
+// fp32 cache and queries: one workgroup (256 threads) per (sequence, KV chunk,
+// query row), fp32 VALU throughout.  Tokens are taken 256 at a time: thread j
+// forms the score of token j (a 576-wide dot product, float4 loads of the
+// token's row, the block table read once per token), the block merges the
+// group's maximum and sum into its running ones (rescaling the output), and
+// thread c accumulates latent columns c and c + 256 over the group.
 // ---------------------------------------------------------------------------
-template <int kFmt>  // 0 = f32 cache, 1 = bf16 cache, 2 = E4M3 + scale, bf16 k^R
-__global__ void __launch_bounds__(256) decode_scalar(const DecodeArgs a) {
-  __shared__ float q_s[576];
-  __shared__ float sc_s[256];
+__global__ void __launch_bounds__(256) decode_f32(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float q_s[576];
+  __shared__ float p_s[256];
+  __shared__ const float* row_s[256];
   __shared__ float red[8];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = blockIdx.x % a.rows;
@@ -967,56 +963,60 @@ __global__ void __launch_bounds__(256) decode_scalar(const DecodeArgs a) {
   const int tok0 = p0 * 64;
   const int tok1 = min(min(p1 * 64, len), max(nvis, 0));
   const int64_t qoff = (int64_t)b * a.rows + row;
-  for (int i = tid; i < 576; i += 256) {
-    if (kFmt == 0)
-      q_s[i] = i < 512 ? ((const float*)a.q_lat)[qoff * 512 + i] : ((const float*)a.q_rope)[qoff * 64 + i - 512];
-    else
-      q_s[i] = i < 512 ? bf16_bits_to_f32(a.q_lat[qoff * 512 + i]) : bf16_bits_to_f32(a.q_rope[qoff * 64 + i - 512]);
-  }
+  const float* ql = (const float*)a.q_lat + qoff * 512;
+  const float* qr = (const float*)a.q_rope + qoff * 64;
+  for (int i = tid; i < 576; i += 256) q_s[i] = i < 512 ? ql[i] : qr[i - 512];
   __syncthreads();
-  auto elem = [&](int tok, int c) -> float {
-    const int blk = a.block_table[(int64_t)b * a.max_blocks + (tok >> 6)];
-    const int r = tok & 63;
-    if (c < 512) {
-      const uint8_t* p = a.latent + blk * a.lat_bs + r * a.lat_rs;
-      if (kFmt == 0) return ((const float*)p)[c];
-      if (kFmt == 1) return bf16_bits_to_f32(((const uint16_t*)p)[c]);
-      const uint32_t code = p[c];
-      const float sc = *(const float*)(a.kv_scale_bytes + blk * a.scale_bs + r * 4);
-      const uint32_t bits = ((code & 0x80u) << 24) | ((code & 0x7Fu) << 20);
-      return __builtin_bit_cast(float, bits) * 0x1p120f * sc;  // E4M3 -> f32, exact
-    }
-    const uint8_t* p = a.rope + blk * a.rope_bs + r * a.rope_rs;
-    if (kFmt == 0) return ((const float*)p)[c - 512];
-    return bf16_bits_to_f32(((const uint16_t*)p)[c - 512]);
+  auto block_reduce = [&](float v, bool is_max) -> float {
+    v = is_max ? wave_max(v) : wave_sum(v);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const float r = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return r;
   };
-  float m = -__builtin_inff(), l = 0.f;
-  float o0 = 0.f, o1 = 0.f;  // columns tid, tid + 256
+  float m = -__builtin_inff(), l = 0.f, o0 = 0.f, o1 = 0.f;
   for (int c0 = tok0; c0 < tok1; c0 += 256) {
     const int n = min(256, tok1 - c0);
-    // scores: one wave per token, lanes split the 576-wide dot product
-    for (int j = wave; j < n; j += 4) {
-      float part = 0.f;
-      for (int c = lane; c < 576; c += 64) part += q_s[c] * elem(c0 + j, c);
-      part = wave_sum(part);
-      if (lane == 0) sc_s[j] = part * a.softmax_scale;
+    float sc = -__builtin_inff();
+    if (tid < n) {
+      const int t = c0 + tid;
+      const int blk = a.block_table[(int64_t)b * a.max_blocks + (t >> 6)];
+      const float* lp = (const float*)(a.latent + blk * a.lat_bs + (int64_t)(t & 63) * a.lat_rs);
+      const float* rp = (const float*)(a.rope + blk * a.rope_bs + (int64_t)(t & 63) * a.rope_rs);
+      row_s[tid] = lp;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < 128; ++i) {
+        const f32x4 v = ((const f32x4*)lp)[i];
+        const f32x4 q = ((const MLA_LDS f32x4*)q_s)[i];
+        acc = fmaf(v[0], q[0], fmaf(v[1], q[1], fmaf(v[2], q[2], fmaf(v[3], q[3], acc))));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const f32x4 v = ((const f32x4*)rp)[i];
+        const f32x4 q = ((const MLA_LDS f32x4*)q_s)[128 + i];
+        acc = fmaf(v[0], q[0], fmaf(v[1], q[1], fmaf(v[2], q[2], fmaf(v[3], q[3], acc))));
+      }
+      sc = acc * a.softmax_scale;
     }
-    __syncthreads();
-    float cm = -__builtin_inff();
-    for (int j = 0; j < n; ++j) cm = fmaxf(cm, sc_s[j]);
-    const float mn = fmaxf(m, cm);
-    const float alpha = expf(m - mn);
-    l *= alpha; o0 *= alpha; o1 *= alpha;
-    for (int j = 0; j < n; ++j) {
-      const float pj = expf(sc_s[j] - mn);
-      l += pj;
-      o0 += pj * elem(c0 + j, tid);
-      o1 += pj * elem(c0 + j, tid + 256);
-    }
+    const float mn = fmaxf(m, block_reduce(sc, true));
+    const float alpha = m == -__builtin_inff() ? 0.f : expf(m - mn);
+    const float pj = tid < n ? expf(sc - mn) : 0.f;
+    p_s[tid] = pj;
+    const float gsum = block_reduce(pj, false);  // its barriers also publish p_s and row_s
+    l = l * alpha + gsum;
+    o0 *= alpha;
+    o1 *= alpha;
     m = mn;
-    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      const float w = p_s[j];
+      const float* lp = row_s[j];
+      o0 = fmaf(w, lp[tid], o0);
+      o1 = fmaf(w, lp[tid + 256], o1);
+    }
+    __syncthreads();  // p_s / row_s are rewritten by the next group
   }
-  (void)red;
   const int64_t slot = (int64_t)b * a.num_splits + split;
   float* orow = a.o + (slot * a.rows + row) * 512;
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1024,9 +1024,5 @@ __global__ void __launch_bounds__(256) decode_scalar(const DecodeArgs a) {
   orow[tid + 256] = o1 * inv;
   if (tid == 0) a.lse[slot * a.rows + row] = l > 0.f ? m + logf(l) : -__builtin_inff();
 }
-
-template __global__ void decode_scalar<0>(const DecodeArgs);
-template __global__ void decode_scalar<1>(const DecodeArgs);
-template __global__ void decode_scalar<2>(const DecodeArgs);
 
 }  // namespace mla

@@ -25,8 +25,7 @@ struct DecodeArgs {
 __global__ void decode_mfma_bf16(const DecodeArgs a);
 __global__ void decode_mfma_fp8(const DecodeArgs a);
 constexpr int kDecodeRowsPerWg = 64;
-template <int kFmt>
-__global__ void decode_scalar(const DecodeArgs a);
+__global__ void decode_f32(const DecodeArgs a);
 
 struct AbsorbArgs {
   const void* q_nope;  // [R][H][128]
