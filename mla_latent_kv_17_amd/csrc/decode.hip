@@ -228,6 +228,10 @@ decode_mfma_bf16(const DecodeArgs a) {
   // (one row per copy) and RoPE rows rb .. rb+7, rb = min(8w, 24): a copy
   // moves eight 128-byte RoPE rows, so four copies would do and waves 4..7
   // rewrite rows 24..31 with the same bytes (every wave issues five copies).
+  // Copies take every row of the tile's half page as it is; rows past the
+  // sequence's length (inside its last page, so still in the pool) are
+  // zeroed by fix_tail once the copies have landed, before the tile is used.
+  // Tiles past the chunk copy block 0 into a buffer nobody reads.
   const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
   auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
     return t < ntiles ? load_uniform(a.block_table, bt_row + ((wk.tok0 + t * kTileTok) >> 6)) : 0;
@@ -236,39 +240,47 @@ decode_mfma_bf16(const DecodeArgs a) {
   const int rope_r = rope_base + (lane >> 3);
   const uint32_t rope_lane = (uint32_t)((lane >> 3) * a.rope_rs) + ((((lane & 7) ^ s8(rope_r))) << 4);
   const uint32_t lane16 = (uint32_t)lane << 4;
+  const int64_t lat_w = (int64_t)(4 * wave) * a.lat_rs, rope_w = (int64_t)rope_base * a.rope_rs;
+  const int64_t lat_half = 32 * a.lat_rs, rope_half = 32 * a.rope_rs;
   struct TileSrc {
     const uint8_t* lat;   // latent row 4 wave of the tile
     const uint8_t* rope;  // RoPE row rope_base of the tile
     uint32_t lds;         // the tile's buffer
-    int vlat, vrope;      // rows (from those firsts) that hold tokens
   };
   auto tile_src = [&](int t, int blk) __attribute__((always_inline)) -> TileSrc {
-    const int tt = wk.tok0 + t * kTileTok;
-    const int r = tt & 63;
-    const int left = t < ntiles ? wk.len - tt : 0;
-    return TileSrc{a.latent + blk * a.lat_bs + (int64_t)(r + 4 * wave) * a.lat_rs,
-                   a.rope + blk * a.rope_bs + (int64_t)(r + rope_base) * a.rope_rs,
-                   tiles_lds + (uint32_t)((t % kBuf) * kTileBytes), left - 4 * wave, left - rope_base};
+    const bool upper = (t & 1) != 0;  // chunks start on a page: odd tiles are upper half pages
+    return TileSrc{a.latent + blk * a.lat_bs + (upper ? lat_half : 0) + lat_w,
+                   a.rope + blk * a.rope_bs + (upper ? rope_half : 0) + rope_w,
+                   tiles_lds + (uint32_t)((t % kBuf) * kTileBytes)};
   };
-  // copy j of a tile (j < 4: latent row 4 wave + j; j == 4: RoPE rows).
-  // Rows at or past the sequence's length (all rows, for a tile past the
-  // chunk) read the zero row.  Branch-free: uniform and per-lane selects.
+  // copy j of a tile (j < 4: latent row 4 wave + j; j == 4: RoPE rows)
   auto tile_chunk = [&](const TileSrc& src, int j) __attribute__((always_inline)) {
-    if (j < 4) {
-      const bool v = j < src.vlat;
-      const int sw = (j << 2) | (wave & 3);  // s16(4 wave + j)
-      dma16x(v ? (const void*)src.lat : (const void*)g_zero_row, lane16, v ? (uint32_t)sw << 4 : 0u,
-             v ? (uint32_t)(j * a.lat_rs) : 0u, src.lds + (4 * wave + j) * 1024);
-    } else {
-      const bool v = (lane >> 3) < src.vrope;
-      dma16(v ? (const void*)(src.rope + rope_lane) : (const void*)((const uint8_t*)g_zero_row + (lane << 4)),
-            src.lds + kLatBytes + rope_base * 128);
-    }
+    if (j < 4)
+      dma16x(src.lat, lane16, (uint32_t)((j << 2) | (wave & 3)) << 4,  // s16(4 wave + j)
+             (uint32_t)(j * a.lat_rs), src.lds + (4 * wave + j) * 1024);
+    else
+      dma16s(src.rope, rope_lane, src.lds + kLatBytes + rope_base * 128);
   };
   auto issue_tile = [&](int t, int blk) __attribute__((always_inline)) {
     const TileSrc src = tile_src(t, blk);
 #pragma unroll
     for (int j = 0; j < 5; ++j) tile_chunk(src, j);
+  };
+  // A sequence's last tile may end inside it: after every wave's copies of
+  // tile t have landed (the caller's wait plus the barrier here), zero its
+  // rows at or past the length, which the value product multiplies by P = 0
+  // (an uninitialised row could hold NaN).  Uniform: at most once per pass.
+  auto fix_tail = [&](int t) __attribute__((always_inline)) {
+    const int left = wk.len - (wk.tok0 + t * kTileTok);
+    if (t < ntiles && left < kTileTok) {
+      wg_barrier();
+      MLA_LDS uint8_t* tb = tiles + (t % kBuf) * kTileBytes;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * wave + j >= left) *(MLA_LDS u32x4*)(tb + (4 * wave + j) * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
+      if (wave < 4 && 8 * wave + (lane >> 3) >= left)
+        *(MLA_LDS u32x4*)(tb + kLatBytes + (64 * wave + lane) * 16) = u32x4{0, 0, 0, 0};
+    }
   };
 
   // ---- this lane's score row: 16 rq + i16
@@ -444,6 +456,7 @@ decode_mfma_bf16(const DecodeArgs a) {
       issue_tile(1, blk_b);
     }
     wait_vmcnt<5>();  // tile 0 (tile 1 may still be in flight)
+    fix_tail(0);
     wg_barrier();
 
     // ---- tile 0: scores, the rows' reference maxima, softmax
@@ -466,7 +479,8 @@ decode_mfma_bf16(const DecodeArgs a) {
       soft_track();
       soft_exp();
       soft_store(0);
-      wait_vmcnt<5>();
+      wait_vmcnt<5>();  // tile 1
+      fix_tail(1);
       wg_barrier();
     }
 
@@ -500,6 +514,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
       // ---- tile s+1 resident (tile s+2's copies may stay in flight), P(s) visible
       wait_vmcnt<5>();
+      fix_tail(s + 1);
       wg_barrier();
     }
     wait_vmcnt<0>();  // copies issued for tiles past the chunk have landed
