@@ -10,9 +10,14 @@ synthetic workload B=32, H=128, T=4096, bf16 cache/queries/weights
 Before every timed step an untimed read of a 1 GiB buffer evicts the 256 MB
 Infinity Cache and the L2s, so the step streams its cache and weights from
 HBM as it would with other layers' data in between.  HIP events on the
-stream the library launches on (torch's current stream) time each decode
-launch and each step (eager launches; --graph also times the step replayed
-from a HIP graph of the four calls).  Prints one JSON line.
+stream the library launches on (torch's current stream) bracket each step;
+none sits between the step's four launches, because an event recorded
+between two kernels delays the second by about 6 us.  The decode kernel on
+its own (the roofline line) is timed as K launches back to back between two
+events, each launch on its own copy of the cache, the copies together being
+several times larger than the Infinity Cache, so every launch streams from
+HBM.  --graph also times the step replayed from a HIP graph of the four
+calls.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -51,6 +56,26 @@ def measured_traffic():
     if c.get("decode_source_hash") != decode_source_hash():
         return None
     return c.get("hbm_bytes_per_launch")
+
+
+DECODE_KERNEL = {"bf16": "decode_mfma_bf16", "fp8": "decode_mfma_fp8", "f32": "decode_f32"}
+
+
+def rotation_caches(dev, gib: float):
+    """The cache and enough copies of its pages that together they exceed
+    `gib` GiB (at least two, at most sixteen): timing launches that rotate
+    over them keeps every launch's cache reads cold."""
+    import torch
+    from mla_latent_kv_17_amd import PagedCache
+    c = dev.cache
+    n = max(2, min(16, math.ceil(gib * (1 << 30) / max(dev.cache_bytes, 1))))
+    out = [c]
+    for _ in range(n - 1):
+        out.append(PagedCache(c.latent.clone(), c.block_table, c.seq_lens,
+                              rope=None if c.rope is None else c.rope.clone(),
+                              scale=None if c.scale is None else c.scale.clone()))
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -99,6 +124,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run three 256 MiB device-to-device copies and exit (the known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--rotate-gib", type=float, default=1.5,
+                    help="total size of the cache copies the decode timing rotates over")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -116,6 +143,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}), flush=True)
         return
     import mla_inputs as MI
+    from mla_latent_kv_17_amd import mla_decode
     from mla_latent_kv_17_amd.runner import DecodeStep, DeviceInputs
 
     wl = MI.WORKLOADS[args.workload]
@@ -144,24 +172,36 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
         do_flush()
-        e0, e1, e2, e3 = ev[i]
+        e0, e3 = ev[i]
         e0.record()
-        step.absorb()
-        e1.record()
-        step.decode()
-        e2.record()
-        step.combine()
-        step.project()
+        step.run()
         e3.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    # ---- the decode kernel alone: K launches back to back over rotating
+    # copies of the cache (every launch cold), between two events
+    caches = rotation_caches(dev, args.rotate_gib)
+    o_dec = step.o_part if step.num_splits > 1 else step.o_lat
+    l_dec = step.lse_part if step.num_splits > 1 else step.lse
+    for c in caches:
+        mla_decode(dev.dims, step.q_lat, dev.q_rope, c, step.num_splits, o_dec, l_dec)
+    do_flush()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for i in range(K):
+        mla_decode(dev.dims, step.q_lat, dev.q_rope, caches[i % len(caches)], step.num_splits, o_dec, l_dec)
+    d1.record()
+    torch.cuda.synchronize()
+    dec_avg = d0.elapsed_time(d1) / K
+    n_rot = len(caches)
+    del caches
 
     # warm (no eviction between steps): context only, never the headline; off by
     # default so that every decode launch of a default run is a cold one
@@ -208,7 +248,6 @@ def main():
 
     eager_ms_per_step = float(step_ms.mean())
     ms_per_step = eager_ms_per_step
-    dec_avg = float(dec_ms.mean())
     achieved = cache_bytes / (dec_avg * 1e-3)
     traffic = measured_traffic()
     out = {
@@ -232,14 +271,14 @@ def main():
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                                      "calibrated on a 256 MiB copy)",
-                     "kernel": "decode_mfma_bf16", "launch_ms": dec_avg,
+                     "kernel": DECODE_KERNEL[wl.cache_dtype], "launch_ms": dec_avg,
+                     "launch_timing": f"{K} back-to-back launches over {n_rot} cache copies, HIP events",
                      "algorithmic_bytes": cache_bytes},
         "decode_tflops": decode_flops / (dec_avg * 1e-3) / 1e12,
         "decode_mfma_frac": decode_flops / (dec_avg * 1e-3) / MFMA_BF16_PEAK,
         "kv_tokens_per_step": kv_tokens,
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "graph_ms_per_step": float(graph_ms.mean()) if graph_ms is not None else None,
-        "decode_ms_p10_p50_p90": [float(np.percentile(dec_ms, q)) for q in (10, 50, 90)],
         "step_tflops": (decode_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
         "warm_ms_per_step": warm_ms,
         "wall_s_timed_loop_incl_eviction": wall,

@@ -171,24 +171,23 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
 
 }  // namespace
 
-// bf16 cache.  Workgroup = 8 waves (two per SIMD) = one (sequence, KV chunk,
-// block of 64 query rows); the chunk is walked in 32-token tiles (half a
-// cache page).  Two waves per SIMD let one wave's LDS, memory and barrier
-// waits be covered by the other's matrix work.
-//
-// Per tile s, with a ring of four LDS tile buffers (s-1 being read by the
-// value product, s by the score product, s+1 and s+2 in flight):
-//   scores   wave w: S^T[16 tokens (half w&1)][16 rows (quarter w>>1)],
-//            v_mfma_f32_16x16x32_bf16 over K = 576; A = tile rows from LDS,
-//            B = the wave's queries in registers.
-//   softmax  of tile s (log2 domain, fixed per-row reference).
-//   values   of tile s-1: wave w accumulates O^T[latent columns 64w..+63]
+// bf16 cache.  Workgroup = 8 waves = one (sequence, KV chunk, block of 64
+// query rows); the chunk is walked in 32-token tiles (half a cache page).
+// Two wave roles, one of each per SIMD:
+//   score waves 0..3: wave w computes S^T[16 tokens (half w&1)][32 rows
+//            (half w>>1)] with v_mfma_f32_16x16x32_bf16 over K = 576 (A = tile
+//            rows from LDS, shared by the two 16-row blocks; B = the wave's
+//            queries, held in registers), then the softmax of those scores
+//            (log2 domain, fixed per-row reference) and writes P to LDS.
+//   value waves 4..7: wave 4+v accumulates O^T[latent columns 128v..+127]
 //            [64 rows] += C^T P^T with v_mfma_f32_32x32x16_bf16, C^T read by
 //            the transposing LDS load, P^T from a double-buffered LDS array.
-//   The matrix instructions of the two products, the softmax arithmetic and
-//   the five DMA copies each wave issues for tile s+2 are interleaved in
-//   program order; one barrier per tile (P(s) visible, tile s-1 free, tile
-//   s+1 resident).
+// Holding 32 query rows per score wave halves the LDS reads of the token
+// operand against 16-row waves, and the two roles share each SIMD's matrix
+// core: one wave's softmax arithmetic and LDS waits overlap the other's
+// products.  Per tile s, with a ring of four LDS tile buffers, the score
+// waves work on tile s, the value waves on tile s-1, tile s+1 lands and every
+// wave issues five DMA copies of tile s+2; one barrier per tile.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_bf16(const DecodeArgs a) {
   constexpr int kBuf = 4;                         // tile ring
@@ -202,7 +201,7 @@ decode_mfma_bf16(const DecodeArgs a) {
   MLA_LDS uint8_t* const pbuf = tiles + kBuf * kTileBytes;
   MLA_LDS float* const xm = (MLA_LDS float*)(tiles + kXOff);  // [2 token halves][64 rows]
   MLA_LDS float* const xl = xm + 128;                         // [2][64] row sums
-  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 128);           // [8] overflow flags
+  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 128);           // [4] overflow flags of the score waves
 
   // the roles below assume exactly eight waves
   if (blockDim.x != 512) return;
@@ -216,8 +215,6 @@ decode_mfma_bf16(const DecodeArgs a) {
   const int n32 = lane & 31;
   const int q4 = lane >> 4;       // k-quarter of a 16x16 operand / token quad of its result
   const int i16 = lane & 15;
-  const int th = wave & 1;        // score token half of a tile
-  const int rq = wave >> 1;       // score row quarter of the block
   const int rows = a.rows;
   const int row_base = wk.rb * kRowsPerWg;
   const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
@@ -283,13 +280,10 @@ decode_mfma_bf16(const DecodeArgs a) {
     }
   };
 
-  // ---- this lane's score row: 16 rq + i16
-  const int qrow = row_base + 16 * rq + i16;
-  const int hi_tok = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
-
-  // ---- first pass prologue: stage the block's 64 query rows (q_lat | q_rope,
-  // 72 chunks of 16 bytes each, row stride 73 chunks) over tile buffers 2..3
-  // with DMA, start tiles 0 and 1, then pull the score operand into registers.
+  // ---- prologue: stage the block's 64 query rows (q_lat | q_rope, 72 chunks
+  // of 16 bytes each, row stride 73 chunks) over tile buffers 2..3 with DMA,
+  // start tiles 0 and 1; the score waves then pull their queries into
+  // registers.
   {
     const int64_t qbase = (int64_t)wk.b * rows;
     for (int i = wave; i < (64 * kQStride) / 64; i += 8) {
@@ -306,269 +300,322 @@ decode_mfma_bf16(const DecodeArgs a) {
   issue_tile(1, blk_b);
   wait_vmcnt<10>();  // the queries (tiles 0 and 1 may still be in flight)
   wg_barrier();
-  // B operand of k-step ks: row 16 rq + i16; latent chunk ks + 16 q4 for
-  // ks < 16 (each lane quarter walks its own quarter of the row: with the
-  // tile swizzle below this order keeps the tile reads free of bank
-  // conflicts, measured), RoPE chunk 4 (ks - 16) + q4 after
-  bf16x8 qf[18];
-  {
-    const int r = 16 * rq + i16;
+
+  // The two roles run separate loops with the same sequence of barriers:
+  // per pass, the pass start, the reference exchange (first pass, non-empty
+  // chunk), tile 0's end, one per later tile, the overflow vote and (before a
+  // repeat) the new reference; after the last pass the row sums.  A row's
+  // reference max is fixed at its first tile, so P and O never need
+  // rescaling.  If a later score exceeds it by more than 2^kRefSlack the pass
+  // is finished (its values are discarded) and repeated with the row's chunk
+  // maximum as the reference: exact either way, never taken unless the
+  // scores of one row span more than 44 nats, and the repeat cannot
+  // overflow, so there are two passes at most.
+  if (wave < 4) {
+    // ================= score waves =================
+    const int th = wave & 1;  // token half of a tile
+    const int rh = wave >> 1;  // row half of the block
+    // B operand of k-step ks for row block rb: row 32 rh + 16 rb + i16; latent
+    // chunk ks + 16 q4 for ks < 16 (each lane quarter walks its own quarter of
+    // the row: with the tile swizzle this order keeps the tile reads free of
+    // bank conflicts, measured), RoPE chunk 4 (ks - 16) + q4 after
+    bf16x8 qf[2][18];
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
-      qf[ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + c) * 16);
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = 32 * rh + 16 * rb + i16;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
+        qf[rb][ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + c) * 16);
+      }
     }
-  }
-  wg_barrier();  // every wave holds its queries: tiles 2, 3 and P are free
+    wg_barrier();  // every score wave holds its queries: tiles 2, 3 and P are free
 
-  // ---- per-lane LDS offsets
-  // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits at byte
-  // 1024 row + 256 q4 + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4); RoPE
-  // chunk 4 (ks - 16) + q4 after the latent part
-  const int tr = 16 * th + i16;
-  const uint32_t c1_lat = tr * 1024 + q4 * 256 + (s16(tr) << 4);
-  uint32_t c1_rope[2];
+    // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits at
+    // byte 1024 row + 256 q4 + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4);
+    // RoPE chunk 4 (ks - 16) + q4 after the latent part
+    const int tr = 16 * th + i16;
+    const uint32_t c1_lat = tr * 1024 + q4 * 256 + (s16(tr) << 4);
+    uint32_t c1_rope[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
-  // value operand (transposing reads): token row 16 ks + 8 j2 + 4 g + i16/4 of
-  // the tile, latent columns 64 wave + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
-  const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
-  uint32_t voff[2][2];
+    for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
+    // this lane's score rows (block-relative), their causal limits and P
+    // slots: tokens 16 th + 4 q4 + 0..3 of row R sit in 16-byte chunk
+    // 2 th + (q4 & 1) (bytes 8 (q4 >> 1)..) at slot 4 R + (chunk ^ (R/4 % 4))
+    int prow[2], hi_tok[2];
+    uint32_t pwrite[2];
 #pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + (((8 * wave + 4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
-  }
-  // P^T operand of the value product: row R = 32 nt + n32, 16-byte chunk 2 ks + g
-  // holding tokens 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot
-  // 4 R + (chunk ^ (R/4 % 4)) of the tile's P buffer (rows 32.. are 2048 bytes on)
-  uint32_t pread[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
-  // P write of a score lane: row 16 rq + i16, tokens 16 th + 4 q4 + 0..3
-  const int prow = 16 * rq + i16;
-  const uint32_t pwrite = (4 * prow + ((2 * th + (q4 & 1)) ^ ((prow >> 2) & 3))) * 16 + 8 * (q4 >> 1);
+    for (int rb = 0; rb < 2; ++rb) {
+      prow[rb] = 32 * rh + 16 * rb + i16;
+      const int qrow = row_base + prow[rb];
+      hi_tok[rb] = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
+      pwrite[rb] = (4 * prow[rb] + ((2 * th + (q4 & 1)) ^ ((prow[rb] >> 2) & 3))) * 16 + 8 * (q4 >> 1);
+    }
 
-  // ---- accumulators.  A row's reference max m_ref is fixed at its first
-  // tile, so P and O never need rescaling.  If a later score exceeds it by
-  // more than 2^kRefSlack the pass is finished (its values are discarded)
-  // and repeated with the row's chunk maximum as the reference: exact either
-  // way, and never taken unless the scores of one row span more than 44 nats.
-  f32x16 oacc[2][2];
-  float m_ref = -__builtin_inff();
-  float m_hi, l_part;
-  bool ovf;
+    float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
+    float m_hi[2], l_part[2];
+    bool ovf;
 
-  // value-product operands of one 16-token half (ks) of tile t
-  auto values_load = [&](int t, int ks, bf16x8 (&av)[2], bf16x8 (&bp)[2]) __attribute__((always_inline)) {
-    const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 1024;
-    const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes + pread[ks];
+    // scores of tile s: 18 k-steps, two 16x16x32 products each (one per row
+    // block, same token operand).  `hook(ks)` runs after k-step ks.
+    f32x4 sacc[2];
+    auto scores = [&](int s, auto hook) __attribute__((always_inline)) {
+      const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
+      auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
+        if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + (c1_lat ^ (uint32_t)(ks << 4)));
+        return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
+      };
+      constexpr int kDepth = 4;
+      sacc[0] = f32x4{};
+      sacc[1] = f32x4{};
+      bf16x8 ar[kDepth];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        sacc[0] = mfma16x16x32(ar[ks % kDepth], qf[0][ks], sacc[0]);
+        sacc[1] = mfma16x16x32(ar[ks % kDepth], qf[1][ks], sacc[1]);
+        if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
+        hook(ks);
+        sched_fence();
+      }
+    };
+
+    // softmax of tile s: lane holds tokens 16 th + 4 q4 + r of rows prow[rb]
+    float p[2][4], mx[2];
+    auto soft_scale = [&](int s) __attribute__((always_inline)) {
+      const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = sacc[rb][r] * a.scale_log2;
+          p[rb][r] = tt + r < hi_tok[rb] ? x : -__builtin_inff();
+        }
+        mx[rb] = fmaxf(fmaxf(p[rb][0], p[rb][1]), fmaxf(p[rb][2], p[rb][3]));
+      }
+    };
+    // hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which
+    // cannot matter next to the row's largest weight (>= 1 after the first tile)
+    auto soft_finish = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        m_hi[rb] = fmaxf(m_hi[rb], mx[rb]);
+        ovf |= mx[rb] > m_ref[rb] + kRefSlack;
+        const float mu = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[rb][r] = __builtin_amdgcn_exp2f(p[rb][r] - mu);
+          l_part[rb] += p[rb][r];
+        }
+        const u32x2 pk = {pack_bf16x2(p[rb][0], p[rb][1]), pack_bf16x2(p[rb][2], p[rb][3])};
+        *(MLA_LDS u32x2*)(pbuf + (s & 1) * kPBytes + pwrite[rb]) = pk;
+      }
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool first = pass == 0;
+      l_part[0] = l_part[1] = 0.f;
+      m_hi[0] = m_hi[1] = -__builtin_inff();
+      ovf = false;
+      if (!first) {
+        issue_tile(0, blk_a);
+        issue_tile(1, blk_b);
+      }
+      wait_vmcnt<5>();  // tile 0 (tile 1 may still be in flight)
+      fix_tail(0);
+      wg_barrier();
+
+      int blk_next = tile_block(3);
+      if (ntiles > 0) {
+        issue_tile(2, tile_block(2));
+        scores(0, [](int) {});
+        soft_scale(0);
+        if (first) {
+          // each row's maximum over the whole first tile (both token halves);
+          // a row left at -inf sees no token of this chunk
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            float m = fmaxf(mx[rb], __shfl_xor(mx[rb], 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (q4 == 0) xm[th * 64 + prow[rb]] = m;
+            mx[rb] = m;
+          }
+          wg_barrier();
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(mx[rb], xm[(th ^ 1) * 64 + prow[rb]]);
+        }
+        soft_finish(0);
+        wait_vmcnt<5>();  // tile 1
+        fix_tail(1);
+        wg_barrier();
+      }
+
+      // tiles 1 ..: tile s+2 goes into the buffer tile s-2 used (the value
+      // waves finished it before the last barrier)
+      for (int s = 1; s < ntiles; ++s) {
+        const TileSrc nsrc = tile_src(s + 2, blk_next);
+        blk_next = tile_block(s + 3);
+        scores(s, [&](int ks) __attribute__((always_inline)) {
+          if (ks % 4 == 1) tile_chunk(nsrc, ks >> 2);  // copies 0..4 at ks 1, 5, .., 17
+        });
+        soft_scale(s);
+        soft_finish(s);
+        wait_vmcnt<5>();  // tile s+1 resident (tile s+2's copies may stay in flight)
+        fix_tail(s + 1);
+        wg_barrier();
+      }
+      wait_vmcnt<0>();  // copies issued for tiles past the chunk have landed
+
+      // ---- did any row overflow its reference?  (its partner lanes may not know)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float m = fmaxf(m_hi[rb], __shfl_xor(m_hi[rb], 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        m_hi[rb] = m;
+        if (q4 == 0) xm[th * 64 + prow[rb]] = m;
+      }
+      // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
+      // would see lane 0's rows alone)
+      const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
+      if (lane == 0) xf[wave] = wave_ovf;
+      wg_barrier();
+      const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
+      if (!again || !first) break;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(m_hi[rb], xm[(th ^ 1) * 64 + prow[rb]]);
+      wg_barrier();
+    }
+
+    // ---- row sums (4 token quads x 2 token halves) for the value waves; lse
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float l = l_part[rb] + __shfl_xor(l_part[rb], 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      if (q4 == 0) xl[th * 64 + prow[rb]] = l;
+    }
+    wg_barrier();
+    if (th == 0 && q4 == 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int qrow = row_base + prow[rb];
+        const float lt = xl[prow[rb]] + xl[64 + prow[rb]];
+        if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref[rb] + log2f(lt)) * kLn2 : -__builtin_inff();
+      }
+    }
+  } else {
+    // ================= value waves =================
+    const int v = wave - 4;
+    wg_barrier();  // the score waves hold their queries
+    // C^T operand (transposing reads): token row 16 ks + 8 j2 + 4 g + i16/4 of
+    // the tile, latent columns 128 v + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
+    const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
+    uint32_t voff[2][4];
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + (((16 * v + 4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
+    }
+    // P^T operand: row R = 32 nt + n32, 16-byte chunk 2 ks + g holding tokens
+    // 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot 4 R + (chunk ^
+    // (R/4 % 4)) of the tile's P buffer (rows 32.. are 2048 bytes on)
+    uint32_t pread[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
+
+    f32x16 oacc[4][2];
+    // C^T operand of tile t, 16-token half ks, 32-column block mt
+    auto av_load = [&](int t, int ks, int mt) __attribute__((always_inline)) -> bf16x8 {
+      const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 1024;
       const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
       const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
-      av[mt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-    bp[0] = *(const MLA_LDS bf16x8*)(pb);
-    bp[1] = *(const MLA_LDS bf16x8*)(pb + 2048);
-  };
-  // MFMA i of a half: O^T[cols 32 (i/2)..][rows 32 (i%2)..]
-  auto values_mfma = [&](int i, const bf16x8 (&av)[2], const bf16x8 (&bp)[2]) __attribute__((always_inline)) {
-    oacc[i >> 1][i & 1] = mfma32x32x16(av[i >> 1], bp[i & 1], oacc[i >> 1][i & 1]);
-  };
-  auto values_all = [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 av[2], bp[2];
-      values_load(t, ks, av, bp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) values_mfma(i, av, bp);
-    }
-  };
-
-  // scores of tile s: 18 k-steps (16x16x32).  `hook(ks)` runs after k-step ks.
-  auto scores = [&](int s, f32x4& sacc, auto hook) __attribute__((always_inline)) {
-    const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
-    auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
-      if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + (c1_lat ^ (uint32_t)(ks << 4)));
-      return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
+      return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    constexpr int kDepth = 4;
-    sacc = f32x4{};
-    bf16x8 ar[kDepth];
+    // value product of tile t: two 16-token halves, eight 32x32x16 products
+    // each; `hook(i)` runs after product i
+    auto values = [&](int t, auto hook) __attribute__((always_inline)) {
+      const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
+      bf16x8 av[2][4], bp[2][2];
 #pragma unroll
-    for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      sacc = mfma16x16x32(ar[ks % kDepth], qf[ks], sacc);
-      if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
-      hook(ks);
-      sched_fence();
-    }
-  };
-
-  // softmax of tile s: lane holds tokens 16 th + 4 q4 + r of row 16 rq + i16
-  float p[4], mx;
-  auto soft_scale = [&](int s, const f32x4& sacc) __attribute__((always_inline)) {
-    const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
+        for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = sacc[r] * a.scale_log2;
-      p[r] = tt + r < hi_tok ? x : -__builtin_inff();
-    }
-    mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-  };
-  auto soft_track = [&]() __attribute__((always_inline)) {
-    m_hi = fmaxf(m_hi, mx);
-    ovf |= mx > m_ref + kRefSlack;
-  };
-  // hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which
-  // cannot matter next to the row's largest weight (>= 1 after the first tile)
-  auto soft_exp = [&]() __attribute__((always_inline)) {
-    const float mu = m_ref == -__builtin_inff() ? 0.f : m_ref;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(p[r] - mu);
-      l_part += p[r];
-    }
-  };
-  auto soft_store = [&](int s) __attribute__((always_inline)) {
-    const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    *(MLA_LDS u32x2*)(pbuf + (s & 1) * kPBytes + pwrite) = pk;
-  };
-
-  // One pass; repeated once after an overflow.  The repeat uses each row's
-  // chunk maximum as its reference, so it cannot overflow again: two passes
-  // at most.
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool first = pass == 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) oacc[i][j] = f32x16{};
-    l_part = 0.f;
-    m_hi = -__builtin_inff();
-    ovf = false;
-    if (!first) {
-      issue_tile(0, blk_a);
-      issue_tile(1, blk_b);
-    }
-    wait_vmcnt<5>();  // tile 0 (tile 1 may still be in flight)
-    fix_tail(0);
-    wg_barrier();
-
-    // ---- tile 0: scores, the rows' reference maxima, softmax
-    int blk_next = tile_block(3);
-    if (ntiles > 0) {
-      issue_tile(2, tile_block(2));
-      f32x4 sacc;
-      scores(0, sacc, [](int) {});
-      soft_scale(0, sacc);
-      if (first) {
-        // each row's maximum over the whole first tile (both token halves);
-        // a row left at -inf sees no token of this chunk
-        float m = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        if (q4 == 0) xm[th * 64 + prow] = m;
-        wg_barrier();
-        m_ref = fmaxf(m, xm[(th ^ 1) * 64 + prow]);
-        mx = m;
+      for (int ks = 0; ks < 2; ++ks) {
+        bp[ks][0] = *(const MLA_LDS bf16x8*)(pb + pread[ks]);
+        bp[ks][1] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048);
       }
-      soft_track();
-      soft_exp();
-      soft_store(0);
-      wait_vmcnt<5>();  // tile 1
-      fix_tail(1);
-      wg_barrier();
-    }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 3, mt = (i >> 1) & 3, nt = i & 1;
+        oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
+        hook(i);
+        sched_fence();
+      }
+    };
 
-    // ---- tiles 1 ..: scores of tile s with the first half of tile s-1's
-    // value product and the copies of tile s+2 between them; then the
-    // softmax of tile s with the second half between its parts.  Tile s+2
-    // goes into the buffer tile s-2 used (free since the last barrier).
-    for (int s = 1; s < ntiles; ++s) {
-      const TileSrc nsrc = tile_src(s + 2, blk_next);
-      blk_next = tile_block(s + 3);
-      f32x4 sacc;
-      bf16x8 av[2], bp[2];
-      values_load(s - 1, 0, av, bp);
-      scores(s, sacc, [&](int ks) __attribute__((always_inline)) {
-        if ((ks & 3) == 3 && ks < 16) values_mfma(ks >> 2, av, bp);
-        if ((ks & 3) == 1 && ks < 16) tile_chunk(nsrc, ks >> 2);
-      });
-      values_load(s - 1, 1, av, bp);
-      soft_scale(s, sacc);
-      values_mfma(0, av, bp);
-      sched_fence();
-      soft_track();
-      soft_exp();
-      values_mfma(1, av, bp);
-      sched_fence();
-      soft_store(s);
-      values_mfma(2, av, bp);
-      tile_chunk(nsrc, 4);
-      values_mfma(3, av, bp);
-      sched_fence();
-
-      // ---- tile s+1 resident (tile s+2's copies may stay in flight), P(s) visible
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool first = pass == 0;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) oacc[mt][nt] = f32x16{};
+      if (!first) {
+        issue_tile(0, blk_a);
+        issue_tile(1, blk_b);
+      }
       wait_vmcnt<5>();
-      fix_tail(s + 1);
+      fix_tail(0);
       wg_barrier();
-    }
-    wait_vmcnt<0>();  // copies issued for tiles past the chunk have landed
-    if (ntiles > 0) values_all(ntiles - 1);
 
-    // ---- did any row overflow its reference?  (its partner lanes may not know)
-    {
-      float m = fmaxf(m_hi, __shfl_xor(m_hi, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      m_hi = m;
-      if (q4 == 0) xm[th * 64 + prow] = m;
-    }
-    // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
-    // would see lane 0's rows alone)
-    const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
-    if (lane == 0) xf[wave] = wave_ovf;
-    wg_barrier();
-    bool again = false;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) again |= xf[w] != 0;
-    if (!again || !first) break;
-    m_ref = fmaxf(m_hi, xm[(th ^ 1) * 64 + prow]);
-    wg_barrier();
-  }
-
-  // ---- epilogue: row sums (4 token quads x 2 token halves)
-  {
-    float l = l_part + __shfl_xor(l_part, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (q4 == 0) xl[th * 64 + prow] = l;
-  }
-  wg_barrier();
-  if (th == 0 && q4 == 0) {
-    const float lt = xl[prow] + xl[64 + prow];
-    xm[prow] = lt;
-    if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -__builtin_inff();
-  }
-  wg_barrier();
-  float* obase = a.o + slot * (int64_t)rows * 512;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = row_base + nt * 32 + n32;
-    const float lt = xm[nt * 32 + n32];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float* orow = obase + (int64_t)row * 512 + wave * 64;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
-                         oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
-        if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = v;
+      int blk_next = tile_block(3);
+      if (ntiles > 0) {
+        issue_tile(2, tile_block(2));
+        if (first) wg_barrier();  // the score waves' reference exchange
+        wait_vmcnt<5>();
+        fix_tail(1);
+        wg_barrier();
       }
-      sched_fence();
+      for (int s = 1; s < ntiles; ++s) {
+        const TileSrc nsrc = tile_src(s + 2, blk_next);
+        blk_next = tile_block(s + 3);
+        values(s - 1, [&](int i) __attribute__((always_inline)) {
+          if (i % 3 == 1) tile_chunk(nsrc, i / 3);  // copies 0..4 at products 1, 4, .., 13
+        });
+        wait_vmcnt<5>();
+        fix_tail(s + 1);
+        wg_barrier();
+      }
+      wait_vmcnt<0>();
+      if (ntiles > 0) values(ntiles - 1, [](int) {});
+      wg_barrier();  // overflow vote
+      const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
+      if (!again || !first) break;
+      wg_barrier();  // new reference
+    }
+
+    // ---- epilogue: normalise by the row sums and write this chunk's o_lat
+    wg_barrier();  // row sums
+    float* obase = a.o + slot * (int64_t)rows * 512;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = nt * 32 + n32;
+      const int row = row_base + r;
+      const float lt = xl[r] + xl[64 + r];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* orow = obase + (int64_t)row * 512 + v * 128;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 o = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
+                           oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
+          if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = o;
+        }
+        sched_fence();
+      }
     }
   }
 }
