@@ -46,7 +46,8 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+/* 2: adds mla_combine_out_uv */
+#define MLA_ABI_VERSION 2
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -166,6 +167,18 @@ int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_p
  * the result carries fp32-level accuracy at matrix-core speed. */
 int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32_t w_dtype,
                float* out, void* stream);
+
+/* The merge of mla_split_combine and the projection of mla_out_uv in one call,
+ * for num_splits > 1 (same formulas, same passages): o_lat is formed on the fly
+ * from the chunks' partials and never written,
+ *   out[r][h][d] = sum_c w_uv[h][d][c] * (sum_s exp(lse_s - lse) o_s[r][h][c]),
+ *   lse[r][h]    = ln sum_s exp(lse_s).
+ * o_part, lse_part: mla_decode's outputs for num_splits > 1 (layouts above);
+ * w_uv, w_dtype, out: as for mla_out_uv; lse: [batch*q_per_seq][heads] fp32, or NULL.
+ * Chunks with lse_s = -inf carry weight 0 (their o_s is not read); a row whose
+ * chunks all do gets out = 0 and lse = -inf.  Same accuracy as the two calls. */
+int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
+                       const void* w_uv, int32_t w_dtype, float* out, float* lse, void* stream);
 
 /* A launch-shape helper: the num_splits mla_decode should use so that the
  * device's compute units are filled, given the longest sequence length the

@@ -5,7 +5,7 @@ Argument marshalling only: every function passes device pointers, sizes and
 the current HIP stream to the C entry point of the same name and raises on a
 non-zero status.  All arithmetic runs in the library's HIP kernels; PyTorch
 provides device memory and streams.  The library must have been built
-(``python -m mla_latent_kv_17_amd.build``); importing fails loudly otherwise.
+(``python mla_latent_kv_17_amd/build.py``); importing fails loudly otherwise.
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 
 # the C entry points this binding exposes (also checked by the tests)
 EXPORTS = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_decode",
-           "mla_split_combine", "mla_out_uv", "mla_decode_num_splits"]
+           "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits"]
 
 
 class MlaDims(ctypes.Structure):
@@ -62,7 +62,7 @@ def _hip_runtimes():
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mla_latent_kv_17_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python mla_latent_kv_17_amd/build.py`")
     # torch brings its own HIP runtime; load it first so that libmla.so binds to
     # the same runtime (same soname) instead of a second copy whose streams and
     # allocations would be foreign to torch's.
@@ -82,6 +82,7 @@ def _load():
         "mla_decode": ([dp, vp, vp, i32, kvp, i32, f32p, f32p, vp], ctypes.c_int),
         "mla_split_combine": ([dp, i32, f32p, f32p, f32p, f32p, vp], ctypes.c_int),
         "mla_out_uv": ([dp, f32p, vp, i32, f32p, vp], ctypes.c_int),
+        "mla_combine_out_uv": ([dp, i32, f32p, f32p, vp, i32, f32p, f32p, vp], ctypes.c_int),
         "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -179,6 +180,13 @@ def mla_out_uv(dims: MlaDims, o_lat, w_uv, out, stream=None):
     """out[r][h][:] = W_UV[h] o_lat[r][h][:]."""
     _check("mla_out_uv", _lib.mla_out_uv(ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _dtype_code(w_uv),
                                          _ptr(out), _stream(stream)))
+
+
+def mla_combine_out_uv(dims: MlaDims, num_splits: int, o_part, lse_part, w_uv, out, lse=None, stream=None):
+    """out[r][h][:] = W_UV[h] (log-sum-exp merge of the chunk partials), lse = merged lse."""
+    _check("mla_combine_out_uv", _lib.mla_combine_out_uv(ctypes.byref(dims), int(num_splits), _ptr(o_part),
+                                                         _ptr(lse_part), _ptr(w_uv), _dtype_code(w_uv), _ptr(out),
+                                                         _ptr(lse), _stream(stream)))
 
 
 def mla_decode_num_splits(dims: MlaDims, max_seq_len: int) -> int:

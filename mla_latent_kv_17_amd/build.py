@@ -1,6 +1,8 @@
 """Build libmla.so (the C-ABI HIP library) in-tree for gfx950.
 
-    python -m mla_latent_kv_17_amd.build [--verbose]
+    python mla_latent_kv_17_amd/build.py [--verbose]
+
+(run as a script: importing the package would load the library being rebuilt)
 
 Each kernel source is compiled to an object with hipcc, then linked into
 ``mla_latent_kv_17_amd/libmla.so``.  Always rebuilds (the sources are small).

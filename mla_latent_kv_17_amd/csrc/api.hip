@@ -198,13 +198,37 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
   if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
   const int rows = dims->batch * dims->q_per_seq;
   if (rows == 0) return MLA_OK;
-  mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads};
+  mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads, nullptr, nullptr, nullptr, 1, dims->q_per_seq};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
-    st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3(dims->heads * (kDH / 64)), dim3(256), a, s);
+    st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3((dims->heads + 7) / 8 * 16),
+                dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;
-    st = launch("mla::out_uv_f32", (const void*)mla::out_uv_f32, dim3(dims->heads, rows), dim3(128), a, s);
+    st = launch("mla::out_uv_f32", (const void*)mla::out_uv_f32<false>, dim3(dims->heads, rows), dim3(128), a, s);
+  }
+  return st;
+}
+
+int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
+                       const void* w_uv, int32_t w_dtype, float* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!o_part || !lse_part || !w_uv || !out) return MLA_ERR_NULL;
+  if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
+  if (w_dtype != MLA_F32 && w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (!aligned16(o_part) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  const int rows = dims->batch * dims->q_per_seq;
+  if (rows == 0) return MLA_OK;
+  mla::OutUvArgs a{nullptr, w_uv, out, rows, dims->heads, o_part, lse_part, lse, num_splits, dims->q_per_seq};
+  hipStream_t s = (hipStream_t)stream;
+  if (w_dtype == MLA_BF16) {
+    st = launch("mla::merge_out_uv_mfma", (const void*)mla::merge_out_uv_mfma, dim3((dims->heads + 7) / 8 * 16),
+                dim3(256), a, s);
+  } else {
+    if (rows > 65535) return MLA_ERR_SHAPE;
+    st = launch("mla::out_uv_f32<merge>", (const void*)mla::out_uv_f32<true>, dim3(dims->heads, rows), dim3(128), a,
+                s);
   }
   return st;
 }

@@ -2,8 +2,10 @@
 
     absorb:  q_lat = W_UK^T q_nope              (mla_absorb_q)
     decode:  o_lat, lse over the paged cache     (mla_decode)
-    merge:   log-sum-exp merge of KV chunks      (mla_split_combine, num_splits > 1)
-    output:  o = W_UV o_lat                      (mla_out_uv)
+    output:  o = W_UV o_lat                      (mla_out_uv; with num_splits > 1
+             the log-sum-exp merge of the KV chunks is done on the way, by
+             mla_combine_out_uv, and o_lat itself is never written;
+             latent_output() runs mla_split_combine to get it)
 
 Host-side plumbing only: uploads arrays, allocates outputs and the split-KV
 workspace with torch, and calls the binding.  Inputs are any object with the
@@ -14,7 +16,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PagedCache, make_dims, mla_absorb_q, mla_decode, mla_decode_num_splits,
+from . import (PagedCache, make_dims, mla_absorb_q, mla_combine_out_uv, mla_decode, mla_decode_num_splits,
                mla_out_uv, mla_split_combine)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -104,7 +106,28 @@ class DecodeStep:
     def project(self, stream=None):
         mla_out_uv(self.dev.dims, self.o_lat, self.dev.w_uv, self.out, stream)
 
+    def merge_project(self, stream=None):
+        """out and lse; with num_splits > 1 the merge is fused into the projection."""
+        if self.num_splits > 1:
+            mla_combine_out_uv(self.dev.dims, self.num_splits, self.o_part, self.lse_part, self.dev.w_uv, self.out,
+                               self.lse, stream)
+        else:
+            self.project(stream)
+
+    def latent_output(self, stream=None):
+        """o_lat of the last decode (merged by mla_split_combine when split; lse untouched)."""
+        if self.num_splits > 1:
+            mla_split_combine(self.dev.dims, self.num_splits, self.o_part, self.lse_part, self.o_lat, None, stream)
+        return self.o_lat
+
     def run(self, stream=None):
+        self.absorb(stream)
+        self.decode(stream)
+        self.merge_project(stream)
+        return self.out
+
+    def run_unfused(self, stream=None):
+        """The same step through mla_split_combine and mla_out_uv."""
         self.absorb(stream)
         self.decode(stream)
         self.combine(stream)

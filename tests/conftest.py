@@ -14,8 +14,11 @@ def _ensure_built():
     """Build the HIP library in-tree when nothing is built yet."""
     lib = os.path.join(ROOT, "mla_latent_kv_17_amd", "libmla.so")
     if not os.path.exists(lib):
-        from mla_latent_kv_17_amd.build import build
-        build()
+        import importlib.util  # by path: importing the package needs the library
+        spec = importlib.util.spec_from_file_location("_mla_build", os.path.join(ROOT, "mla_latent_kv_17_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 _ensure_built()

@@ -105,3 +105,44 @@ def test_split_combine(B, ns, Sq, heads):
     assert np.array_equal(np.isneginf(gl), none)
     assert (got[none] == 0).all()
     assert np.max(np.abs(gl[~none] - lse_ref[~none])) <= 1e-5 * max(1.0, np.abs(lse_ref[~none]).max())
+
+
+@pytest.mark.parametrize("B,ns,Sq,heads,wdt", [(3, 5, 2, 128, "bf16"), (37, 3, 1, 100, "bf16"),
+                                               (2, 64, 1, 128, "bf16"), (5, 7, 2, 16, "f32")])
+def test_combine_out_uv(B, ns, Sq, heads, wdt):
+    """The merge fused into the projection against the fp64 merge followed by
+    the fp64 projection, and against mla_split_combine + mla_out_uv."""
+    import torch
+    import mla_latent_kv_17_amd as M
+    print(f"[case] combine_out_uv B={B} ns={ns} Sq={Sq} H={heads} w={wdt}", flush=True)
+    o_part, lse_part = _combine_case(B, ns, Sq, heads, 3400 + ns)
+    o_part *= np.float32(0.05)
+    rng = np.random.default_rng(3500 + heads)
+    wf = rng.standard_normal((heads, 128, 512), dtype=np.float32) * np.float32(1.0 / math.sqrt(512))
+    if wdt == "bf16":
+        wb = MI.bf16_bits(wf)
+        w_dev, w64 = _bf16_tensor(wb), O.decode_bf16(wb)
+    else:
+        w_dev, w64 = torch.from_numpy(wf).cuda(), wf.astype(np.float64)
+    dims = M.make_dims(B, Sq, heads)
+    op, lp = torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda()
+    out = torch.empty((B * Sq, heads, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B * Sq, heads), dtype=torch.float32, device="cuda")
+    M.mla_combine_out_uv(dims, ns, op, lp, w_dev, out, lse)
+    o_ref, lse_ref = O.combine_partials(o_part, lse_part)
+    ref = O.project_output(o_ref.reshape(B * Sq, heads, 512), w64)
+    got, gl = out.cpu().numpy(), lse.cpu().numpy().reshape(B, Sq, heads)
+    assert np.isfinite(got).all()
+    check(f"combine_out_uv ns={ns} H={heads} {wdt}", got, ref, "f32")
+    none = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(gl), none)
+    assert (got.reshape(B, Sq, heads, 128)[none] == 0).all()
+    assert np.max(np.abs(gl[~none] - lse_ref[~none])) <= 1e-5 * max(1.0, np.abs(lse_ref[~none]).max())
+    # the two-call form of the same step
+    o_lat = torch.empty((B * Sq, heads, 512), dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out)
+    M.mla_split_combine(dims, ns, op, lp, o_lat, None)
+    M.mla_out_uv(dims, o_lat, w_dev, out2)
+    m = metrics(got, out2.cpu().numpy())
+    print(f"[parity] fused vs two calls: rel_l2 {m['rel_l2']:.2e} max_abs {m['max_abs']:.2e}", flush=True)
+    assert m["rel_l2"] <= 1e-5  # both are fp32 merges, summed in different orders

@@ -22,9 +22,18 @@ def run(inp, ns):
     print(f"[case] {wl.name} B={wl.batch} Sq={wl.q_per_seq} H={wl.heads} {wl.cache_dtype} "
           f"lens={list(inp.seq_lens)[:8]} ns={ns}", flush=True)
     step = DecodeStep(DeviceInputs(inp), ns)
-    step.run()
+    step.run()  # merge fused into the projection when split
     torch.cuda.synchronize()
-    return step.out.cpu().numpy(), step.o_lat.cpu().numpy(), step.lse.cpu().numpy()
+    out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
+    o_lat = step.latent_output().cpu().numpy()
+    step.run_unfused()  # mla_split_combine + mla_out_uv
+    torch.cuda.synchronize()
+    out2, lse2 = step.out.cpu().numpy(), step.lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse2))
+    fin = ~np.isneginf(lse)
+    assert np.max(np.abs(lse[fin] - lse2[fin]), initial=0.0) <= 1e-5 * max(1.0, np.abs(lse[fin]).max(initial=0.0))
+    assert np.max(np.abs(out - out2), initial=0.0) <= 1e-5 * max(1.0, np.abs(out2).max(initial=0.0))
+    return out, o_lat, lse
 
 
 def compare(inp, ns):

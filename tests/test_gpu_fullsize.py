@@ -53,8 +53,8 @@ def test_full_size_sampled(name):
     step.run()
     torch.cuda.synchronize()
     out = step.out.cpu().numpy()
-    o_lat = step.o_lat.cpu().numpy()
     lse = step.lse.cpu().numpy()
+    o_lat = step.latent_output().cpu().numpy()
     del dev, step
 
     # properties of every row

@@ -17,9 +17,11 @@ def run_gpu(inp, num_splits=None):
     dev = DeviceInputs(inp)
     ns = inp.wl.num_splits if num_splits is None else num_splits
     step = DecodeStep(dev, ns)
-    step.run()
+    step.run()  # merge fused into the projection when split
     torch.cuda.synchronize()
-    return (step.out.cpu().numpy(), step.o_lat.cpu().numpy(), step.lse.cpu().numpy(), step)
+    out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
+    o_lat = step.latent_output().cpu().numpy()  # the merge on its own
+    return out, o_lat, lse, step
 
 
 @pytest.mark.parametrize("name", list(MI.small_variants()))
