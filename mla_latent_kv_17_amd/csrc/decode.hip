@@ -147,15 +147,18 @@ struct Work {
   int len, tok0, tok1, ntiles;
 };
 
-// XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs,
-// so the row blocks of one (sequence, chunk) get ids 8 apart and land on the
-// same XCD, where the second read of each tile is an L2 hit.
+// XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs
+// (id % 8), so each XCD takes a contiguous range of (sequence, chunk) units
+// and runs the row blocks of a unit back to back: a tile is fetched from HBM
+// once and read from that XCD's L2 by the other row blocks, and the chunks of
+// one sequence, which share its query block, mostly run on one XCD too.
 __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
   const int id = blockIdx.x;
   const int xcd = id & 7, k = id >> 3;
+  const int upx = (a.units + 7) >> 3;  // units per XCD
+  const int unit = xcd * upx + k / a.row_blocks;
   w.rb = k % a.row_blocks;
-  const int unit = (k / a.row_blocks) * 8 + xcd;
-  if (unit >= a.units) return false;
+  if (k >= upx * a.row_blocks || unit >= a.units) return false;
   w.b = unit / a.num_splits;
   w.split = unit - w.b * a.num_splits;
   w.len = a.seq_lens[w.b];
