@@ -48,8 +48,6 @@ constexpr float kRefSlack = 64.0f;              // log2 headroom above a row's r
 // the 128-byte RoPE rows.
 __device__ __forceinline__ int s16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int s8(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int lat_off(int r, int q) { return (r * 64 + (q ^ s16(r))) * 16; }
-__device__ __forceinline__ int rope_off(int r, int q) { return kLatBytes + (r * 8 + (q ^ s8(r))) * 16; }
 
 __device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) { return (uint32_t)(size_t)p; }
 
@@ -95,12 +93,11 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t 
       : "memory");
 }
 
-// Same copy where lane i's byte offset is ((16 i) ^ x16) + row, for
-// wave-uniform x16 and row: the offset is formed inside the asm block, so the
-// compiler keeps one lane register and one base per tile instead of a 64-bit
-// address (and a hoisted offset register) for every copy.
-__device__ __forceinline__ void dma16x(const void* base, uint32_t lane16, uint32_t x16, uint32_t row,
-                                       uint32_t lds_base) {
+// Same copy where lane i's byte offset is (lc_i ^ x16) + lrow_i + row: a
+// per-lane chunk offset (XORed with a wave-uniform swizzle) and row offset
+// plus a wave-uniform row offset.
+__device__ __forceinline__ void dma16xy(const void* base, uint32_t lc, uint32_t x16, uint32_t lrow, uint32_t row,
+                                        uint32_t lds_base) {
   lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   x16 = __builtin_amdgcn_readfirstlane(x16);
   row = __builtin_amdgcn_readfirstlane(row);
@@ -111,14 +108,14 @@ __device__ __forceinline__ void dma16x(const void* base, uint32_t lane16, uint32
   uint32_t saved, off;
   asm volatile(
       "v_xor_b32 %1, %2, %3\n\t"
-      "v_add_u32 %1, %1, %4\n\t"
+      "v_add3_u32 %1, %1, %4, %5\n\t"
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %6\n\t"
+      "s_mov_b32 m0, %7\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %1, %6\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved), "=&v"(off)
-      : "v"(lane16), "s"(x16), "s"(row), "s"(base), "s"(lds_base)
+      : "v"(lc), "s"(x16), "v"(lrow), "s"(row), "s"(base), "s"(lds_base)
       : "memory");
 }
 
@@ -189,8 +186,9 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
 // operand against 16-row waves, and the two roles share each SIMD's matrix
 // core: one wave's softmax arithmetic and LDS waits overlap the other's
 // products.  Per tile s, with a ring of four LDS tile buffers, the score
-// waves work on tile s, the value waves on tile s-1, tile s+1 lands and every
-// wave issues five DMA copies of tile s+2; one barrier per tile.
+// waves work on tile s, the value waves on tile s-1 (and refill their slices
+// of its buffer with tile s+3 once read), tiles s+1 .. s+3 are in flight;
+// one barrier per tile.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_bf16(const DecodeArgs a) {
   constexpr int kBuf = 4;                         // tile ring
@@ -224,62 +222,76 @@ decode_mfma_bf16(const DecodeArgs a) {
   const int ntiles = wk.ntiles;
   const uint32_t tiles_lds = lds_addr(tiles);
 
-  // ---- HBM -> LDS copies of one tile: 5 per wave.  Latent rows 4w .. 4w+3
-  // (one row per copy) and RoPE rows rb .. rb+7, rb = min(8w, 24): a copy
-  // moves eight 128-byte RoPE rows, so four copies would do and waves 4..7
-  // rewrite rows 24..31 with the same bytes (every wave issues five copies).
+  // ---- HBM -> LDS copies.  Tile layout here: the latent part is four 8 KB
+  // slices, slice v holding latent columns 128 v .. 128 v + 127 of the 32 rows
+  // (row r at 256 r in the slice, its 16-byte chunk q at slot q ^ s16(r)); the
+  // RoPE part follows (row r at 128 r, chunk q at slot q ^ s8(r)).  Value wave
+  // 4 + v copies slice v of every tile (eight copies of four 256-byte row
+  // slices) and is the only wave that reads it in the value product; score
+  // wave w copies RoPE rows 8w .. 8w+7 (one copy).  So in the iteration that
+  // multiplies tile s-1, value wave 4 + v refills its slice of that buffer
+  // with tile s+3 as soon as its own reads are done, and the score waves
+  // refill the RoPE rows (free since the previous iteration): three tiles are
+  // in flight while two are in use, in four buffers, with no extra barrier.
   // Copies take every row of the tile's half page as it is; rows past the
   // sequence's length (inside its last page, so still in the pool) are
-  // zeroed by fix_tail once the copies have landed, before the tile is used.
-  // Tiles past the chunk copy block 0 into a buffer nobody reads.
+  // zeroed by each wave in its own part once its copies have landed.  Tiles
+  // past the chunk copy block 0 into a buffer nobody reads.
+  constexpr int kSliceBytes = 32 * 256;
   const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
   auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
     return t < ntiles ? load_uniform(a.block_table, bt_row + ((wk.tok0 + t * kTileTok) >> 6)) : 0;
   };
-  const int rope_base = min(8 * wave, 24);
-  const int rope_r = rope_base + (lane >> 3);
+  const bool valw = wave >= 4;
+  const int v = wave & 3;      // slice of a value wave; RoPE rows 8 v .. of a score wave
+  const int lrq = lane >> 4;   // row of a latent-copy lane among its copy's four
+  // s16(4k + lrq) = (lrq << 2) | (k & 3): the lane part and the copy part
+  const uint32_t lat_lc = (uint32_t)(((lane & 15) ^ (lrq << 2)) << 4);
+  const uint32_t lat_lrow = (uint32_t)(lrq * a.lat_rs);
+  const int rope_r = 8 * v + (lane >> 3);
   const uint32_t rope_lane = (uint32_t)((lane >> 3) * a.rope_rs) + ((((lane & 7) ^ s8(rope_r))) << 4);
-  const uint32_t lane16 = (uint32_t)lane << 4;
-  const int64_t lat_w = (int64_t)(4 * wave) * a.lat_rs, rope_w = (int64_t)rope_base * a.rope_rs;
   const int64_t lat_half = 32 * a.lat_rs, rope_half = 32 * a.rope_rs;
   struct TileSrc {
-    const uint8_t* lat;   // latent row 4 wave of the tile
-    const uint8_t* rope;  // RoPE row rope_base of the tile
+    const uint8_t* lat;   // latent row 0 of the tile
+    const uint8_t* rope;  // RoPE row 8 v of the tile
     uint32_t lds;         // the tile's buffer
   };
   auto tile_src = [&](int t, int blk) __attribute__((always_inline)) -> TileSrc {
     const bool upper = (t & 1) != 0;  // chunks start on a page: odd tiles are upper half pages
-    return TileSrc{a.latent + blk * a.lat_bs + (upper ? lat_half : 0) + lat_w,
-                   a.rope + blk * a.rope_bs + (upper ? rope_half : 0) + rope_w,
+    return TileSrc{a.latent + blk * a.lat_bs + (upper ? lat_half : 0),
+                   a.rope + blk * a.rope_bs + (upper ? rope_half : 0) + (int64_t)(8 * v) * a.rope_rs,
                    tiles_lds + (uint32_t)((t % kBuf) * kTileBytes)};
   };
-  // copy j of a tile (j < 4: latent row 4 wave + j; j == 4: RoPE rows)
-  auto tile_chunk = [&](const TileSrc& src, int j) __attribute__((always_inline)) {
-    if (j < 4)
-      dma16x(src.lat, lane16, (uint32_t)((j << 2) | (wave & 3)) << 4,  // s16(4 wave + j)
-             (uint32_t)(j * a.lat_rs), src.lds + (4 * wave + j) * 1024);
-    else
-      dma16s(src.rope, rope_lane, src.lds + kLatBytes + rope_base * 128);
+  // value wave: copy k = rows 4k .. 4k+3 of slice v
+  auto lat_copy = [&](const TileSrc& src, int k) __attribute__((always_inline)) {
+    dma16xy(src.lat, lat_lc, (uint32_t)(k & 3) << 4, lat_lrow, (uint32_t)(4 * k * a.lat_rs + 256 * v),
+            src.lds + v * kSliceBytes + 1024 * k);
   };
-  auto issue_tile = [&](int t, int blk) __attribute__((always_inline)) {
+  auto issue_tile = [&](int t, int blk) __attribute__((always_inline)) {  // this wave's copies of tile t
     const TileSrc src = tile_src(t, blk);
+    if (valw) {
 #pragma unroll
-    for (int j = 0; j < 5; ++j) tile_chunk(src, j);
+      for (int k = 0; k < 8; ++k) lat_copy(src, k);
+    } else {
+      dma16s(src.rope, rope_lane, src.lds + kLatBytes + 1024 * v);
+    }
   };
-  // A sequence's last tile may end inside it: after every wave's copies of
-  // tile t have landed (the caller's wait plus the barrier here), zero its
-  // rows at or past the length, which the value product multiplies by P = 0
-  // (an uninitialised row could hold NaN).  Uniform: at most once per pass.
+  // A sequence's last tile may end inside it: once this wave's copies of
+  // tile t have landed, zero its part of the rows at or past the length,
+  // which the value product multiplies by P = 0 (an uninitialised row could
+  // hold NaN).  Uniform: at most once per pass.
   auto fix_tail = [&](int t) __attribute__((always_inline)) {
     const int left = wk.len - (wk.tok0 + t * kTileTok);
     if (t < ntiles && left < kTileTok) {
-      wg_barrier();
       MLA_LDS uint8_t* tb = tiles + (t % kBuf) * kTileBytes;
+      if (valw) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * wave + j >= left) *(MLA_LDS u32x4*)(tb + (4 * wave + j) * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
-      if (wave < 4 && 8 * wave + (lane >> 3) >= left)
-        *(MLA_LDS u32x4*)(tb + kLatBytes + (64 * wave + lane) * 16) = u32x4{0, 0, 0, 0};
+        for (int k = 0; k < 8; ++k)
+          if (4 * k + lrq >= left)
+            *(MLA_LDS u32x4*)(tb + v * kSliceBytes + (4 * k + lrq) * 256 + (lane & 15) * 16) = u32x4{0, 0, 0, 0};
+      } else if (rope_r >= left) {
+        *(MLA_LDS u32x4*)(tb + kLatBytes + 1024 * v + lane * 16) = u32x4{0, 0, 0, 0};
+      }
     }
   };
 
@@ -301,7 +313,12 @@ decode_mfma_bf16(const DecodeArgs a) {
   const int blk_a = tile_block(0), blk_b = tile_block(1);
   issue_tile(0, blk_a);
   issue_tile(1, blk_b);
-  wait_vmcnt<10>();  // the queries (tiles 0 and 1 may still be in flight)
+  // the queries (tiles 0 and 1 may still be in flight: 8 copies each for a
+  // value wave, 1 for a score wave)
+  if (valw)
+    wait_vmcnt<16>();
+  else
+    wait_vmcnt<2>();
   wg_barrier();
 
   // The two roles run separate loops with the same sequence of barriers:
@@ -334,11 +351,11 @@ decode_mfma_bf16(const DecodeArgs a) {
     }
     wg_barrier();  // every score wave holds its queries: tiles 2, 3 and P are free
 
-    // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits at
-    // byte 1024 row + 256 q4 + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4);
+    // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits in
+    // slice q4 at byte 256 row + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4);
     // RoPE chunk 4 (ks - 16) + q4 after the latent part
     const int tr = 16 * th + i16;
-    const uint32_t c1_lat = tr * 1024 + q4 * 256 + (s16(tr) << 4);
+    const uint32_t c1_lat = q4 * kSliceBytes + tr * 256 + (s16(tr) << 4);
     uint32_t c1_rope[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
@@ -425,13 +442,14 @@ decode_mfma_bf16(const DecodeArgs a) {
         issue_tile(0, blk_a);
         issue_tile(1, blk_b);
       }
-      wait_vmcnt<5>();  // tile 0 (tile 1 may still be in flight)
+      wait_vmcnt<1>();  // tile 0 (tile 1 may still be in flight)
       fix_tail(0);
       wg_barrier();
 
-      int blk_next = tile_block(3);
+      int blk_next = tile_block(4);
       if (ntiles > 0) {
-        issue_tile(2, tile_block(2));
+        issue_tile(2, tile_block(2));  // buffers 2, 3 are free (queries held, or the last pass over)
+        issue_tile(3, tile_block(3));
         scores(0, [](int) {});
         soft_scale(0);
         if (first) {
@@ -449,22 +467,20 @@ decode_mfma_bf16(const DecodeArgs a) {
           for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(mx[rb], xm[(th ^ 1) * 64 + prow[rb]]);
         }
         soft_finish(0);
-        wait_vmcnt<5>();  // tile 1
+        wait_vmcnt<2>();  // tile 1 (tiles 2, 3 may still be in flight)
         fix_tail(1);
         wg_barrier();
       }
 
-      // tiles 1 ..: tile s+2 goes into the buffer tile s-2 used (the value
-      // waves finished it before the last barrier)
+      // tiles 1 ..: the RoPE rows of tile s+3 go into the buffer of tile s-1,
+      // whose RoPE rows were read in the previous iteration
       for (int s = 1; s < ntiles; ++s) {
-        const TileSrc nsrc = tile_src(s + 2, blk_next);
-        blk_next = tile_block(s + 3);
-        scores(s, [&](int ks) __attribute__((always_inline)) {
-          if (ks % 4 == 1) tile_chunk(nsrc, ks >> 2);  // copies 0..4 at ks 1, 5, .., 17
-        });
+        issue_tile(s + 3, blk_next);
+        scores(s, [](int) {});
         soft_scale(s);
         soft_finish(s);
-        wait_vmcnt<5>();  // tile s+1 resident (tile s+2's copies may stay in flight)
+        blk_next = tile_block(s + 4);  // a scalar load: read here, its wait joins the barrier's
+        wait_vmcnt<2>();  // tile s+1 (tiles s+2, s+3 may still be in flight)
         fix_tail(s + 1);
         wg_barrier();
       }
@@ -508,10 +524,9 @@ decode_mfma_bf16(const DecodeArgs a) {
     }
   } else {
     // ================= value waves =================
-    const int v = wave - 4;
     wg_barrier();  // the score waves hold their queries
-    // C^T operand (transposing reads): token row 16 ks + 8 j2 + 4 g + i16/4 of
-    // the tile, latent columns 128 v + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
+    // C^T operand (transposing reads, slice v): token row 16 ks + 8 j2 + 4 g +
+    // i16/4 of the tile, latent columns 128 v + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
     const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
     uint32_t voff[2][4];
 #pragma unroll
@@ -519,7 +534,7 @@ decode_mfma_bf16(const DecodeArgs a) {
       const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + (((16 * v + 4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
+        voff[j2][mt] = v * kSliceBytes + (8 * j2 + 4 * g + (i16 >> 2)) * 256 + (((4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
     }
     // P^T operand: row R = 32 nt + n32, 16-byte chunk 2 ks + g holding tokens
     // 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot 4 R + (chunk ^
@@ -531,14 +546,16 @@ decode_mfma_bf16(const DecodeArgs a) {
     f32x16 oacc[4][2];
     // C^T operand of tile t, 16-token half ks, 32-column block mt
     auto av_load = [&](int t, int ks, int mt) __attribute__((always_inline)) -> bf16x8 {
-      const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 1024;
+      const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 256;
       const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
       const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
       return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
     // value product of tile t: two 16-token halves, eight 32x32x16 products
-    // each; `hook(i)` runs after product i
-    auto values = [&](int t, auto hook) __attribute__((always_inline)) {
+    // each.  With `refill`, once every operand read of slice v has completed,
+    // the slice is refilled with tile nsrc: its eight copies go between the
+    // products, whose execution covers their issue.
+    auto values = [&](int t, bool refill, const TileSrc& nsrc) __attribute__((always_inline)) {
       const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
       bf16x8 av[2][4], bp[2][2];
 #pragma unroll
@@ -550,11 +567,12 @@ decode_mfma_bf16(const DecodeArgs a) {
         bp[ks][0] = *(const MLA_LDS bf16x8*)(pb + pread[ks]);
         bp[ks][1] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048);
       }
+      if (refill) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of slice v are done
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int ks = i >> 3, mt = (i >> 1) & 3, nt = i & 1;
         oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
-        hook(i);
+        if (refill && (i & 1) == 0) lat_copy(nsrc, i >> 1);
         sched_fence();
       }
     };
@@ -569,30 +587,29 @@ decode_mfma_bf16(const DecodeArgs a) {
         issue_tile(0, blk_a);
         issue_tile(1, blk_b);
       }
-      wait_vmcnt<5>();
+      wait_vmcnt<8>();  // tile 0 (tile 1 may still be in flight)
       fix_tail(0);
       wg_barrier();
 
-      int blk_next = tile_block(3);
+      int blk_next = tile_block(4);
       if (ntiles > 0) {
         issue_tile(2, tile_block(2));
+        issue_tile(3, tile_block(3));
         if (first) wg_barrier();  // the score waves' reference exchange
-        wait_vmcnt<5>();
+        wait_vmcnt<16>();  // tile 1 (tiles 2, 3 may still be in flight)
         fix_tail(1);
         wg_barrier();
       }
       for (int s = 1; s < ntiles; ++s) {
-        const TileSrc nsrc = tile_src(s + 2, blk_next);
-        blk_next = tile_block(s + 3);
-        values(s - 1, [&](int i) __attribute__((always_inline)) {
-          if (i % 3 == 1) tile_chunk(nsrc, i / 3);  // copies 0..4 at products 1, 4, .., 13
-        });
-        wait_vmcnt<5>();
+        const TileSrc nsrc = tile_src(s + 3, blk_next);
+        values(s - 1, true, nsrc);  // slice v of tile s-1's buffer takes tile s+3
+        blk_next = tile_block(s + 4);
+        wait_vmcnt<16>();  // tile s+1 (tiles s+2, s+3 may still be in flight)
         fix_tail(s + 1);
         wg_barrier();
       }
       wait_vmcnt<0>();
-      if (ntiles > 0) values(ntiles - 1, [](int) {});
+      if (ntiles > 0) values(ntiles - 1, false, tile_src(0, 0));
       wg_barrier();  // overflow vote
       const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
       if (!again || !first) break;
