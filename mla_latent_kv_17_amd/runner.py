@@ -106,9 +106,19 @@ class DecodeStep:
     def project(self, stream=None):
         mla_out_uv(self.dev.dims, self.o_lat, self.dev.w_uv, self.out, stream)
 
+    # the fused merge walks the chunks a few at a time per 32-row tile, so it
+    # pays one memory latency per round: with many chunks and few query rows
+    # the separate merge, which spreads rows over workgroups, is faster
+    FUSED_MERGE_MAX_SPLITS = 8
+
     def merge_project(self, stream=None):
-        """out and lse; with num_splits > 1 the merge is fused into the projection."""
-        if self.num_splits > 1:
+        """out and lse; with 1 < num_splits <= FUSED_MERGE_MAX_SPLITS the merge is
+        fused into the projection (mla_combine_out_uv), otherwise mla_split_combine
+        then mla_out_uv."""
+        if self.num_splits > self.FUSED_MERGE_MAX_SPLITS:
+            self.combine(stream)
+            self.project(stream)
+        elif self.num_splits > 1:
             mla_combine_out_uv(self.dev.dims, self.num_splits, self.o_part, self.lse_part, self.dev.w_uv, self.out,
                                self.lse, stream)
         else:
