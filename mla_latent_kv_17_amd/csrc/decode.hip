@@ -640,13 +640,17 @@ decode_mfma_bf16(const DecodeArgs a) {
   }
 }
 
-// E4M3 cache (fp8 codes + fp32 per-token scale, bf16 k^R).  Same workgroup
-// shape, roles and tile pipeline as decode_mfma_bf16; the tiles are staged
-// through registers instead of LDS DMA because the codes are converted to
-// bf16 on the way (exactly: a 3-bit mantissa and the E4M3 exponent range fit
-// bf16), into the same swizzled LDS layout.  The per-token scale is applied
-// in fp32 to the latent part of each score (kept in its own accumulator) and
-// folded into P for the value product, so no dequantized value is rounded.
+// E4M3 cache (fp8 codes + fp32 per-token scale, bf16 k^R).  The workgroup,
+// wave roles, tile ring and slice-major tile layout of decode_mfma_bf16, with
+// three differences.  Value wave 4+v stages slice v of each tile through
+// registers: it loads the tile's codes of its 128 latent columns, converts
+// them exactly to bf16 (a 3-bit mantissa and the E4M3 exponent range fit
+// bf16; rows past the sequence's length become zeros there) and writes them
+// into its slice once its own reads of the buffer's previous tile are done.
+// The score waves copy the RoPE rows by DMA and score wave 0 the tile's 32
+// token scales.  The per-token scale is applied in fp32 to the latent part of
+// each score (kept in its own accumulator) and folded into P for the value
+// product, so no dequantized value is rounded.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_fp8(const DecodeArgs a) {
   constexpr int kBuf = 4;                         // tile ring
@@ -655,12 +659,13 @@ decode_mfma_fp8(const DecodeArgs a) {
   constexpr int kQBase = 2 * kTileBytes;          // queries are staged over tiles 2, 3 (+ P)
   constexpr int kXOff = kBuf * kTileBytes + 2 * kPBytes;
   static_assert(kQBase + 64 * kQStride * 16 <= kXOff, "query staging must fit before the exchange area");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280 + kBuf * 128];
   MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)&smem[0];
   MLA_LDS uint8_t* const pbuf = tiles + kBuf * kTileBytes;
   MLA_LDS float* const xm = (MLA_LDS float*)(tiles + kXOff);  // [2 token halves][64 rows]
   MLA_LDS float* const xl = xm + 128;                         // [2][64] row sums
-  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 128);           // [8] overflow flags
+  MLA_LDS int* const xf = (MLA_LDS int*)(xl + 128);           // [4] overflow flags of the score waves
+  MLA_LDS float* const scl = (MLA_LDS float*)(tiles + kXOff + 1280);  // [kBuf][32] token scales
 
   // the roles below assume exactly eight waves
   if (blockDim.x != 512) return;
@@ -674,59 +679,101 @@ decode_mfma_fp8(const DecodeArgs a) {
   const int n32 = lane & 31;
   const int q4 = lane >> 4;       // k-quarter of a 16x16 operand / token quad of its result
   const int i16 = lane & 15;
-  const int th = wave & 1;        // score token half of a tile
-  const int rq = wave >> 1;       // score row quarter of the block
   const int rows = a.rows;
   const int row_base = wk.rb * kRowsPerWg;
   const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
   const int ntiles = wk.ntiles;
   const uint32_t tiles_lds = lds_addr(tiles);
 
-  // ---- HBM -> registers -> LDS copies of one tile.  Wave w stages latent
-  // rows 4w + lane/16 (codes 8 (16 k + lane%16) .. +7 for k = 0..3, four
-  // 8-byte loads, converted exactly to bf16 and written as 16-byte chunks
-  // 16 k + lane%16 of the swizzled row) and the 8-byte RoPE piece lane%16 of
-  // the same row.  Rows at or past the sequence's length read zeros.  All
-  // loads are ordinary (compiler-tracked) loads.
+  // ---- copies.  Tile layout as in decode_mfma_bf16 (four 8 KB latent
+  // slices, then the RoPE rows); the tile's token scales go to scl.
+  // Value wave 4+v stages slice v: lane l takes row l/2, codes 128 v +
+  // 64 (l%2) .. +63 (four 16-byte loads), ordinary loads tracked by the
+  // compiler; rows at or past the sequence's length, and tiles past the
+  // chunk (whose loads read block 0), are stored as zeros.  Score wave w copies RoPE rows 8w .. 8w+7 (one DMA
+  // copy) and score wave 0 also the 128 bytes of token scales (one copy on 8
+  // lanes); rows past the length are zeroed by fix_tail once landed.
+  constexpr int kSliceBytes = 32 * 256;
   const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
   auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
     return t < ntiles ? load_uniform(a.block_table, bt_row + ((wk.tok0 + t * kTileTok) >> 6)) : 0;
   };
-  const int srow = 4 * wave + (lane >> 4);  // staged tile row of this lane
-  const int si = lane & 15;
+  const bool valw = wave >= 4;
+  const int v = wave & 3;      // slice of a value wave; RoPE rows 8 v .. of a score wave
+  const int rope_r = 8 * v + (lane >> 3);
+  const uint32_t rope_lane = (uint32_t)((lane >> 3) * a.rope_rs) + ((((lane & 7) ^ s8(rope_r))) << 4);
+  const int64_t rope_half = 32 * a.rope_rs;
+  const uint32_t scl_lds = tiles_lds + (kXOff + 1280);
+  // score waves: this wave's DMA copies of tile t (1, or 2 for wave 0)
+  auto issue_tile = [&](int t, int blk) __attribute__((always_inline)) {
+    const bool upper = (t & 1) != 0;  // chunks start on a page: odd tiles are upper half pages
+    const uint32_t buf = tiles_lds + (uint32_t)((t % kBuf) * kTileBytes);
+    dma16s(a.rope + blk * a.rope_bs + (upper ? rope_half : 0) + (int64_t)(8 * v) * a.rope_rs, rope_lane,
+           buf + kLatBytes + 1024 * v);
+    if (wave == 0 && lane < 8)
+      dma16(a.kv_scale_bytes + blk * a.scale_bs + (upper ? 128 : 0) + 16 * lane, scl_lds + (t % kBuf) * 128);
+  };
+  // score waves: wait until at most n tiles' copies are in flight
+  auto wait_tiles2 = [&]() __attribute__((always_inline)) {
+    if (wave == 0)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<2>();
+  };
+  auto wait_tiles1 = [&]() __attribute__((always_inline)) {
+    if (wave == 0)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<1>();
+  };
+  // value waves: slice v of tile t staged in registers
+  const int srow = lane >> 1, shalf = lane & 1;
   struct Staged {
-    u32x2 lat[4];
-    u32x2 rope;
+    u32x4 c[4];
+  };
+  auto stage_src = [&](int t, int blk) __attribute__((always_inline)) -> const uint8_t* {
+    const bool upper = (t & 1) != 0;
+    return a.latent + blk * a.lat_bs + (int64_t)((upper ? 32 : 0) + srow) * a.lat_rs + 128 * v + 64 * shalf;
   };
   auto stage_load = [&](int t, int blk, Staged& st) __attribute__((always_inline)) {
-    const int tt = wk.tok0 + t * kTileTok;
-    const bool v = t < ntiles && tt + srow < wk.len;
-    const uint8_t* lp = v ? a.latent + blk * a.lat_bs + (int64_t)((tt & 63) + srow) * a.lat_rs + 8 * si
-                          : (const uint8_t*)g_zero_row;
-    const uint8_t* rp = v ? a.rope + blk * a.rope_bs + (int64_t)((tt & 63) + srow) * a.rope_rs + 8 * si
-                          : (const uint8_t*)g_zero_row;
+    const uint8_t* lp = stage_src(t, blk);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) st.lat[k] = *(const u32x2*)(lp + (v ? 128 * k : 0));
-    st.rope = *(const u32x2*)rp;
+    for (int j = 0; j < 4; ++j) st.c[j] = *(const u32x4*)(lp + 16 * j);
+  };
+  // 16 codes -> two 16-byte chunks (8 bf16 each) of row srow, local chunks
+  // 8 shalf + 2 j, +1, at slot q ^ s16(srow) of slice v; a row at or past the
+  // length (or a tile past the chunk) is stored as zeros.  The test sits here,
+  // not after the loads, so that nothing waits for them before this point.
+  auto stage_piece = [&](int t, const Staged& st, int j, int e) __attribute__((always_inline)) {
+    MLA_LDS uint8_t* sb = tiles + (t % kBuf) * kTileBytes + v * kSliceBytes + srow * 256;
+    const bool ok = t < ntiles && wk.tok0 + t * kTileTok + srow < wk.len;
+    const uint32_t w0 = ok ? st.c[j][2 * e] : 0u, w1 = ok ? st.c[j][2 * e + 1] : 0u;
+    const u32x4 bf = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
+                      e4m3x2_to_bf16x2<true>(w1)};
+    const int q = 8 * shalf + 2 * j + e;
+    *(MLA_LDS u32x4*)(sb + ((q ^ s16(srow)) << 4)) = bf;
   };
   auto stage_store = [&](int t, const Staged& st) __attribute__((always_inline)) {
-    MLA_LDS uint8_t* tb = tiles + (t % kBuf) * kTileBytes;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4 w = {e4m3x2_to_bf16x2<false>(st.lat[k][0]), e4m3x2_to_bf16x2<true>(st.lat[k][0]),
-                       e4m3x2_to_bf16x2<false>(st.lat[k][1]), e4m3x2_to_bf16x2<true>(st.lat[k][1])};
-      *(MLA_LDS u32x4*)(tb + srow * 1024 + 256 * k + ((si ^ s16(srow)) << 4)) = w;
+    for (int j = 0; j < 4; ++j) {
+      stage_piece(t, st, j, 0);
+      stage_piece(t, st, j, 1);
     }
-    *(MLA_LDS u32x2*)(tb + kLatBytes + (srow * 8 + ((si >> 1) ^ s8(srow))) * 16 + (si & 1) * 8) = st.rope;
+  };
+  // A sequence's last tile may end inside it: once this score wave's RoPE
+  // copy of tile t has landed, zero the RoPE rows at or past the length
+  // (uninitialised pool rows could hold NaN; the latent part was staged as
+  // zeros).  Uniform: at most once per pass.
+  auto fix_tail = [&](int t) __attribute__((always_inline)) {
+    const int left = wk.len - (wk.tok0 + t * kTileTok);
+    if (t < ntiles && left < kTileTok && rope_r >= left)
+      *(MLA_LDS u32x4*)(tiles + (t % kBuf) * kTileBytes + kLatBytes + 1024 * v + lane * 16) = u32x4{0, 0, 0, 0};
   };
 
-  // ---- this lane's score row: 16 rq + i16
-  const int qrow = row_base + 16 * rq + i16;
-  const int hi_tok = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
-
-  // ---- first pass prologue: stage the block's 64 query rows (q_lat | q_rope,
-  // 72 chunks of 16 bytes each, row stride 73 chunks) over tile buffers 2..3
-  // with DMA, start tiles 0 and 1, then pull the score operand into registers.
+  // ---- prologue: stage the block's 64 query rows (q_lat | q_rope, 72 chunks
+  // of 16 bytes each, row stride 73 chunks) over tile buffers 2..3 with DMA,
+  // start tiles 0 and 1; the score waves then pull their queries into
+  // registers.
   {
     const int64_t qbase = (int64_t)wk.b * rows;
     for (int i = wave; i < (64 * kQStride) / 64; i += 8) {
@@ -738,286 +785,354 @@ decode_mfma_fp8(const DecodeArgs a) {
       dma16(src, tiles_lds + kQBase + i * 1024);
     }
   }
-  wait_vmcnt<0>();  // the staged queries (the only copies in flight)
-  wg_barrier();
-  bf16x8 qf[18];
-  {
-    const int r = 16 * rq + i16;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
-      qf[ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + c) * 16);
-    }
-  }
-  wg_barrier();  // every wave holds its queries: tiles 2, 3 and P are free
-
-  // ---- per-lane LDS offsets
-  // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits at byte
-  // 1024 row + 256 q4 + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4); RoPE
-  // chunk 4 (ks - 16) + q4 after the latent part
-  const int tr = 16 * th + i16;
-  const uint32_t c1_lat = tr * 1024 + q4 * 256 + (s16(tr) << 4);
-  uint32_t c1_rope[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
-  // value operand (transposing reads): token row 16 ks + 8 j2 + 4 g + i16/4 of
-  // the tile, latent columns 64 wave + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
-  const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
-  uint32_t voff[2][2];
-#pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      voff[j2][mt] = (8 * j2 + 4 * g + (i16 >> 2)) * 1024 + (((8 * wave + 4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
-  }
-  // P^T operand of the value product: row R = 32 nt + n32, 16-byte chunk 2 ks + g
-  // holding tokens 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot
-  // 4 R + (chunk ^ (R/4 % 4)) of the tile's P buffer (rows 32.. are 2048 bytes on)
-  uint32_t pread[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
-  // P write of a score lane: row 16 rq + i16, tokens 16 th + 4 q4 + 0..3
-  const int prow = 16 * rq + i16;
-  const uint32_t pwrite = (4 * prow + ((2 * th + (q4 & 1)) ^ ((prow >> 2) & 3))) * 16 + 8 * (q4 >> 1);
-
-  // ---- accumulators.  A row's reference max m_ref is fixed at its first
-  // tile, so P and O never need rescaling.  If a later score exceeds it by
-  // more than 2^kRefSlack the pass is finished (its values are discarded)
-  // and repeated with the row's chunk maximum as the reference: exact either
-  // way, and never taken unless the scores of one row span more than 44 nats.
-  f32x16 oacc[2][2];
-  float m_ref = -__builtin_inff();
-  float m_hi, l_part;
-  bool ovf;
-
-  // value-product operands of one 16-token half (ks) of tile t
-  auto values_load = [&](int t, int ks, bf16x8 (&av)[2], bf16x8 (&bp)[2]) __attribute__((always_inline)) {
-    const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 1024;
-    const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes + pread[ks];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
-      const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
-      av[mt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-    bp[0] = *(const MLA_LDS bf16x8*)(pb);
-    bp[1] = *(const MLA_LDS bf16x8*)(pb + 2048);
-  };
-  // MFMA i of a half: O^T[cols 32 (i/2)..][rows 32 (i%2)..]
-  auto values_mfma = [&](int i, const bf16x8 (&av)[2], const bf16x8 (&bp)[2]) __attribute__((always_inline)) {
-    oacc[i >> 1][i & 1] = mfma32x32x16(av[i >> 1], bp[i & 1], oacc[i >> 1][i & 1]);
-  };
-  auto values_all = [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 av[2], bp[2];
-      values_load(t, ks, av, bp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) values_mfma(i, av, bp);
-    }
-  };
-
-  // scores of tile s: 18 k-steps (16x16x32); the latent part (k-steps 0..15)
-  // and the RoPE part (16, 17) accumulate separately because only the former
-  // is scaled.  `hook(ks)` runs after k-step ks.
-  auto scores = [&](int s, f32x4& sacc, f32x4& sacc_r, auto hook) __attribute__((always_inline)) {
-    const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
-    auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
-      if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + (c1_lat ^ (uint32_t)(ks << 4)));
-      return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
-    };
-    constexpr int kDepth = 3;
-    sacc = f32x4{};
-    sacc_r = f32x4{};
-    bf16x8 ar[kDepth];
-#pragma unroll
-    for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if (ks < 16)
-        sacc = mfma16x16x32(ar[ks % kDepth], qf[ks], sacc);
-      else
-        sacc_r = mfma16x16x32(ar[ks % kDepth], qf[ks], sacc_r);
-      if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
-      hook(ks);
-      sched_fence();
-    }
-  };
-
-  // softmax of tile s: lane holds tokens 16 th + 4 q4 + r of row 16 rq + i16.
-  // Score = scale_t (q_lat . code_t) + q_rope . k^R_t; the value product
-  // takes p_t scale_t against the codes, the row sum p_t.
-  float p[4], mx;
-  f32x4 tscale;  // the lane's four token scales (0 past the row's horizon)
-  auto load_scale = [&](int s, int blk) __attribute__((always_inline)) {
-    const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
-    const bool v = s < ntiles && tt < wk.len;
-    const float* sp = (const float*)(v ? a.kv_scale_bytes + blk * a.scale_bs + (int64_t)(tt & 63) * 4
-                                       : (const uint8_t*)g_zero_row);
-    tscale = *(const f32x4*)sp;
-  };
-  auto soft_scale = [&](int s, const f32x4& sacc, const f32x4& sacc_r) __attribute__((always_inline)) {
-    const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool vis = tt + r < hi_tok;
-      tscale[r] = vis ? tscale[r] : 0.f;
-      const float x = (sacc[r] * tscale[r] + sacc_r[r]) * a.scale_log2;
-      p[r] = vis ? x : -__builtin_inff();
-    }
-    mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-  };
-  auto soft_track = [&]() __attribute__((always_inline)) {
-    m_hi = fmaxf(m_hi, mx);
-    ovf |= mx > m_ref + kRefSlack;
-  };
-  // hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which
-  // cannot matter next to the row's largest weight (>= 1 after the first tile)
-  auto soft_exp = [&]() __attribute__((always_inline)) {
-    const float mu = m_ref == -__builtin_inff() ? 0.f : m_ref;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(p[r] - mu);
-      l_part += p[r];
-    }
-  };
-  auto soft_store = [&](int s) __attribute__((always_inline)) {
-    const u32x2 pk = {pack_bf16x2(p[0] * tscale[0], p[1] * tscale[1]), pack_bf16x2(p[2] * tscale[2], p[3] * tscale[3])};
-    *(MLA_LDS u32x2*)(pbuf + (s & 1) * kPBytes + pwrite) = pk;
-  };
-
-  // One pass; repeated once after an overflow.  The repeat uses each row's
-  // chunk maximum as its reference, so it cannot overflow again: two passes
-  // at most.
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool first = pass == 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) oacc[i][j] = f32x16{};
-    l_part = 0.f;
-    m_hi = -__builtin_inff();
-    ovf = false;
-    // tiles 0 and 1 into LDS, tile 2 staged in registers
+  const int blk_a = tile_block(0), blk_b = tile_block(1);
+  if (valw) {
     Staged st;
-    stage_load(0, tile_block(0), st);
+    stage_load(0, blk_a, st);
     stage_store(0, st);
-    stage_load(1, tile_block(1), st);
+    stage_load(1, blk_b, st);
     stage_store(1, st);
-    stage_load(2, tile_block(2), st);
-    wg_barrier();  // tiles 0, 1 resident
+    wait_vmcnt<0>();  // the queries
+  } else {
+    issue_tile(0, blk_a);
+    issue_tile(1, blk_b);
+    wait_tiles2();  // the queries (tiles 0 and 1 may still be in flight)
+  }
+  wg_barrier();
 
-    // ---- tile 0: scores, the rows' reference maxima, softmax
-    int blk_next = tile_block(3);
-    if (ntiles > 0) {
-      stage_store(2, st);  // buffer 2 held the staged queries, free now
-      stage_load(3, blk_next, st);
-      load_scale(0, tile_block(0));
-      f32x4 sacc, sacc_r;
-      scores(0, sacc, sacc_r, [](int) {});
-      soft_scale(0, sacc, sacc_r);
-      if (first) {
-        // each row's maximum over the whole first tile (both token halves);
-        // a row left at -inf sees no token of this chunk
-        float m = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        if (q4 == 0) xm[th * 64 + prow] = m;
-        wg_barrier();
-        m_ref = fmaxf(m, xm[(th ^ 1) * 64 + prow]);
-        mx = m;
+  // The two roles run separate loops with the same sequence of barriers:
+  // per pass, the pass start, the reference exchange (first pass, non-empty
+  // chunk), tile 0's end, one per later tile, the overflow vote and (before a
+  // repeat) the new reference; after the last pass the row sums.  A row's
+  // reference max is fixed at its first tile, so P and O never need
+  // rescaling.  If a later score exceeds it by more than 2^kRefSlack the pass
+  // is finished (its values are discarded) and repeated with the row's chunk
+  // maximum as the reference: exact either way, never taken unless the
+  // scores of one row span more than 44 nats, and the repeat cannot
+  // overflow, so there are two passes at most.
+  if (wave < 4) {
+    // ================= score waves =================
+    const int th = wave & 1;  // token half of a tile
+    const int rh = wave >> 1;  // row half of the block
+    // B operand of k-step ks for row block rb: row 32 rh + 16 rb + i16; latent
+    // chunk ks + 16 q4 for ks < 16 (each lane quarter walks its own quarter of
+    // the row: with the tile swizzle this order keeps the tile reads free of
+    // bank conflicts, measured), RoPE chunk 4 (ks - 16) + q4 after
+    bf16x8 qf[2][18];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = 32 * rh + 16 * rb + i16;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
+        qf[rb][ks] = *(const MLA_LDS bf16x8*)(tiles + kQBase + (r * kQStride + c) * 16);
       }
-      soft_track();
-      soft_exp();
-      soft_store(0);
+    }
+    wg_barrier();  // every score wave holds its queries: tiles 2, 3 and P are free
+
+    // score operand: tile row 16 th + i16; latent chunk ks + 16 q4 sits in
+    // slice q4 at byte 256 row + ((ks ^ s16(row)) << 4) = c1_lat ^ (ks << 4);
+    // RoPE chunk 4 (ks - 16) + q4 after the latent part
+    const int tr = 16 * th + i16;
+    const uint32_t c1_lat = q4 * kSliceBytes + tr * 256 + (s16(tr) << 4);
+    uint32_t c1_rope[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) c1_rope[k] = kLatBytes + tr * 128 + (((4 * k + q4) ^ s8(tr)) << 4);
+    // this lane's score rows (block-relative), their causal limits and P
+    // slots: tokens 16 th + 4 q4 + 0..3 of row R sit in 16-byte chunk
+    // 2 th + (q4 & 1) (bytes 8 (q4 >> 1)..) at slot 4 R + (chunk ^ (R/4 % 4))
+    int prow[2], hi_tok[2];
+    uint32_t pwrite[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      prow[rb] = 32 * rh + 16 * rb + i16;
+      const int qrow = row_base + prow[rb];
+      hi_tok[rb] = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
+      pwrite[rb] = (4 * prow[rb] + ((2 * th + (q4 & 1)) ^ ((prow[rb] >> 2) & 3))) * 16 + 8 * (q4 >> 1);
+    }
+
+    float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
+    float m_hi[2], l_part[2];
+    bool ovf;
+
+    // scores of tile s: 18 k-steps, two 16x16x32 products each (one per row
+    // block, same token operand); the latent part (k-steps 0..15) and the
+    // RoPE part (16, 17) accumulate separately because only the former is
+    // scaled.  `hook(ks)` runs after k-step ks.
+    f32x4 sacc[2], sacc_r[2];
+    auto scores = [&](int s, auto hook) __attribute__((always_inline)) {
+      const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
+      auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
+        if (ks < 16) return *(const MLA_LDS bf16x8*)(tb + (c1_lat ^ (uint32_t)(ks << 4)));
+        return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
+      };
+      constexpr int kDepth = 4;
+      sacc[0] = sacc[1] = sacc_r[0] = sacc_r[1] = f32x4{};
+      bf16x8 ar[kDepth];
+#pragma unroll
+      for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks < 16) {
+          sacc[0] = mfma16x16x32(ar[ks % kDepth], qf[0][ks], sacc[0]);
+          sacc[1] = mfma16x16x32(ar[ks % kDepth], qf[1][ks], sacc[1]);
+        } else {
+          sacc_r[0] = mfma16x16x32(ar[ks % kDepth], qf[0][ks], sacc_r[0]);
+          sacc_r[1] = mfma16x16x32(ar[ks % kDepth], qf[1][ks], sacc_r[1]);
+        }
+        if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
+        hook(ks);
+        sched_fence();
+      }
+    };
+
+    // softmax of tile s: lane holds tokens 16 th + 4 q4 + r of rows prow[rb].
+    // Score = scale_t (q_lat . code_t) + q_rope . k^R_t; the value product
+    // takes p_t scale_t against the codes, the row sum p_t.
+    float p[2][4], mx[2];
+    f32x4 tsc[2];  // the lane's four token scales per row block (0 past the row's horizon)
+    auto soft_scale = [&](int s) __attribute__((always_inline)) {
+      const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
+      const f32x4 sc = *(const MLA_LDS f32x4*)(scl + (s % kBuf) * 32 + 16 * th + 4 * q4);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool vis = tt + r < hi_tok[rb];
+          tsc[rb][r] = vis ? sc[r] : 0.f;
+          const float x = (sacc[rb][r] * sc[r] + sacc_r[rb][r]) * a.scale_log2;
+          p[rb][r] = vis ? x : -__builtin_inff();
+        }
+        mx[rb] = fmaxf(fmaxf(p[rb][0], p[rb][1]), fmaxf(p[rb][2], p[rb][3]));
+      }
+    };
+    // hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which
+    // cannot matter next to the row's largest weight (>= 1 after the first tile)
+    auto soft_finish = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        m_hi[rb] = fmaxf(m_hi[rb], mx[rb]);
+        ovf |= mx[rb] > m_ref[rb] + kRefSlack;
+        const float mu = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[rb][r] = __builtin_amdgcn_exp2f(p[rb][r] - mu);
+          l_part[rb] += p[rb][r];
+        }
+        const u32x2 pk = {pack_bf16x2(p[rb][0] * tsc[rb][0], p[rb][1] * tsc[rb][1]),
+                          pack_bf16x2(p[rb][2] * tsc[rb][2], p[rb][3] * tsc[rb][3])};
+        *(MLA_LDS u32x2*)(pbuf + (s & 1) * kPBytes + pwrite[rb]) = pk;
+      }
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool first = pass == 0;
+      l_part[0] = l_part[1] = 0.f;
+      m_hi[0] = m_hi[1] = -__builtin_inff();
+      ovf = false;
+      if (!first) {
+        issue_tile(0, blk_a);
+        issue_tile(1, blk_b);
+      }
+      wait_tiles1();  // tile 0 (tile 1 may still be in flight)
+      fix_tail(0);
+      wg_barrier();
+
+      int blk_next = tile_block(4);
+      if (ntiles > 0) {
+        issue_tile(2, tile_block(2));  // buffers 2, 3 are free (queries held, or the last pass over)
+        issue_tile(3, tile_block(3));
+        scores(0, [](int) {});
+        soft_scale(0);
+        if (first) {
+          // each row's maximum over the whole first tile (both token halves);
+          // a row left at -inf sees no token of this chunk
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            float m = fmaxf(mx[rb], __shfl_xor(mx[rb], 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (q4 == 0) xm[th * 64 + prow[rb]] = m;
+            mx[rb] = m;
+          }
+          wg_barrier();
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(mx[rb], xm[(th ^ 1) * 64 + prow[rb]]);
+        }
+        soft_finish(0);
+        wait_tiles2();  // tile 1 (tiles 2, 3 may still be in flight)
+        fix_tail(1);
+        wg_barrier();
+      }
+
+      // tiles 1 ..: the RoPE rows and scales of tile s+3 go into the buffer of
+      // tile s-1, whose RoPE rows and scales were read in the previous iteration
+      for (int s = 1; s < ntiles; ++s) {
+        issue_tile(s + 3, blk_next);
+        scores(s, [](int) {});
+        soft_scale(s);
+        soft_finish(s);
+        blk_next = tile_block(s + 4);  // a scalar load: read here, its wait joins the barrier's
+        wait_tiles2();  // tile s+1 (tiles s+2, s+3 may still be in flight)
+        fix_tail(s + 1);
+        wg_barrier();
+      }
+      wait_vmcnt<0>();  // copies issued for tiles past the chunk have landed
+
+      // ---- did any row overflow its reference?  (its partner lanes may not know)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float m = fmaxf(m_hi[rb], __shfl_xor(m_hi[rb], 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        m_hi[rb] = m;
+        if (q4 == 0) xm[th * 64 + prow[rb]] = m;
+      }
+      // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
+      // would see lane 0's rows alone)
+      const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
+      if (lane == 0) xf[wave] = wave_ovf;
+      wg_barrier();
+      const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
+      if (!again || !first) break;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(m_hi[rb], xm[(th ^ 1) * 64 + prow[rb]]);
       wg_barrier();
     }
 
-    // ---- tiles 1 ..: tile s+2 (staged last iteration) goes into the buffer
-    // tile s-2 used, tile s+3 is staged; scores of tile s with the first half
-    // of tile s-1's value product between them, then the softmax of tile s
-    // with the second half between its parts.
-    for (int s = 1; s < ntiles; ++s) {
-      const int blk_s = tile_block(s);
-      stage_store(s + 2, st);
-      const int blk3 = tile_block(s + 3);
-      stage_load(s + 3, blk3, st);
-      load_scale(s, blk_s);
-      f32x4 sacc, sacc_r;
-      bf16x8 av[2], bp[2];
-      values_load(s - 1, 0, av, bp);
-      scores(s, sacc, sacc_r, [&](int ks) __attribute__((always_inline)) {
-        if ((ks & 3) == 3 && ks < 16) values_mfma(ks >> 2, av, bp);
-      });
-      values_load(s - 1, 1, av, bp);
-      soft_scale(s, sacc, sacc_r);
-      values_mfma(0, av, bp);
-      sched_fence();
-      soft_track();
-      soft_exp();
-      values_mfma(1, av, bp);
-      sched_fence();
-      soft_store(s);
-      values_mfma(2, av, bp);
-      values_mfma(3, av, bp);
-      sched_fence();
-      wg_barrier();  // P(s) visible, tile s+1 resident, tile s-1 free
+    // ---- row sums (4 token quads x 2 token halves) for the value waves; lse
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float l = l_part[rb] + __shfl_xor(l_part[rb], 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      if (q4 == 0) xl[th * 64 + prow[rb]] = l;
     }
-    (void)blk_next;
-    if (ntiles > 0) values_all(ntiles - 1);
-
-    // ---- did any row overflow its reference?  (its partner lanes may not know)
-    {
-      float m = fmaxf(m_hi, __shfl_xor(m_hi, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      m_hi = m;
-      if (q4 == 0) xm[th * 64 + prow] = m;
-    }
-    // the vote runs in every lane (a ballot taken inside `if (lane == 0)`
-    // would see lane 0's rows alone)
-    const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
-    if (lane == 0) xf[wave] = wave_ovf;
     wg_barrier();
-    bool again = false;
+    if (th == 0 && q4 == 0) {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) again |= xf[w] != 0;
-    if (!again || !first) break;
-    m_ref = fmaxf(m_hi, xm[(th ^ 1) * 64 + prow]);
-    wg_barrier();
-  }
-
-  // ---- epilogue: row sums (4 token quads x 2 token halves)
-  {
-    float l = l_part + __shfl_xor(l_part, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (q4 == 0) xl[th * 64 + prow] = l;
-  }
-  wg_barrier();
-  if (th == 0 && q4 == 0) {
-    const float lt = xl[prow] + xl[64 + prow];
-    xm[prow] = lt;
-    if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -__builtin_inff();
-  }
-  wg_barrier();
-  float* obase = a.o + slot * (int64_t)rows * 512;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = row_base + nt * 32 + n32;
-    const float lt = xm[nt * 32 + n32];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float* orow = obase + (int64_t)row * 512 + wave * 64;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
-                         oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
-        if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = v;
+      for (int rb = 0; rb < 2; ++rb) {
+        const int qrow = row_base + prow[rb];
+        const float lt = xl[prow[rb]] + xl[64 + prow[rb]];
+        if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref[rb] + log2f(lt)) * kLn2 : -__builtin_inff();
       }
-      sched_fence();
+    }
+  } else {
+    // ================= value waves =================
+    wg_barrier();  // the score waves hold their queries
+    // C^T operand (transposing reads, slice v): token row 16 ks + 8 j2 + 4 g +
+    // i16/4 of the tile, latent columns 128 v + 32 mt + 16 (lane/16 % 2) + 4 (i16 % 4)
+    const int vy = 2 * ((lane >> 4) & 1) + ((i16 >> 1) & 1);
+    uint32_t voff[2][4];
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const int sw = (((i16 >> 2) & 3) << 2) | ((2 * j2 + g) & 3);  // s16 of the row
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        voff[j2][mt] = v * kSliceBytes + (8 * j2 + 4 * g + (i16 >> 2)) * 256 + (((4 * mt + vy) ^ sw) << 4) + (i16 & 1) * 8;
+    }
+    // P^T operand: row R = 32 nt + n32, 16-byte chunk 2 ks + g holding tokens
+    // 16 ks + 4 g + 0..3 and 16 ks + 8 + 4 g + 0..3, at slot 4 R + (chunk ^
+    // (R/4 % 4)) of the tile's P buffer (rows 32.. are 2048 bytes on)
+    uint32_t pread[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
+
+    f32x16 oacc[4][2];
+    // C^T operand of tile t, 16-token half ks, 32-column block mt
+    auto av_load = [&](int t, int ks, int mt) __attribute__((always_inline)) -> bf16x8 {
+      const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 256;
+      const u32x2 lo = lds_read_tr16_b64(vt + voff[0][mt]);
+      const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
+      return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    // value product of tile t: two 16-token halves, eight 32x32x16 products
+    // each.  With `refill`, once every operand read of slice v has completed,
+    // the staged tile t+4 is converted into the slice and tile t+5 staged,
+    // one 16-byte piece after each of the first eight products.
+    Staged st;
+    auto values = [&](int t, bool refill, int nblk) __attribute__((always_inline)) {
+      const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
+      bf16x8 av[2][4], bp[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bp[ks][0] = *(const MLA_LDS bf16x8*)(pb + pread[ks]);
+        bp[ks][1] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048);
+      }
+      if (refill) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of slice v are done
+      const uint8_t* lp = stage_src(t + 5, nblk);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 3, mt = (i >> 1) & 3, nt = i & 1;
+        oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
+        if (refill && i < 8) {
+          stage_piece(t + 4, st, i >> 1, i & 1);
+          if (i & 1) st.c[i >> 1] = *(const u32x4*)(lp + 16 * (i >> 1));
+        }
+        sched_fence();
+      }
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool first = pass == 0;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) oacc[mt][nt] = f32x16{};
+      if (!first) {
+        stage_load(0, blk_a, st);
+        stage_store(0, st);
+        stage_load(1, blk_b, st);
+        stage_store(1, st);
+      }
+      wg_barrier();
+
+      if (ntiles > 0) {
+        stage_load(2, tile_block(2), st);  // buffers 2, 3 are free (queries held, or the last pass over)
+        stage_store(2, st);
+        stage_load(3, tile_block(3), st);
+        stage_store(3, st);
+        stage_load(4, tile_block(4), st);
+        if (first) wg_barrier();  // the score waves' reference exchange
+        wg_barrier();
+      }
+      for (int s = 1; s < ntiles; ++s) {
+        // slice v of tile s-1's buffer takes tile s+3 (staged last iteration); tile s+4 is staged
+        values(s - 1, true, tile_block(s + 4));
+        wg_barrier();
+      }
+      if (ntiles > 0) values(ntiles - 1, false, 0);
+      wg_barrier();  // overflow vote
+      const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
+      if (!again || !first) break;
+      wg_barrier();  // new reference
+    }
+
+    // ---- epilogue: normalise by the row sums and write this chunk's o_lat
+    wg_barrier();  // row sums
+    float* obase = a.o + slot * (int64_t)rows * 512;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = nt * 32 + n32;
+      const int row = row_base + r;
+      const float lt = xl[r] + xl[64 + r];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* orow = obase + (int64_t)row * 512 + v * 128;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 o = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
+                           oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
+          if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = o;
+        }
+        sched_fence();
+      }
     }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // fp32 cache and queries: one workgroup (256 threads) per (sequence, KV chunk,
