@@ -551,17 +551,24 @@ decode_mfma_bf16(const DecodeArgs a) {
       const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
       return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    // value product of tile t: two 16-token halves, eight 32x32x16 products
-    // each.  With `refill`, once every operand read of slice v has completed,
-    // the slice is refilled with tile nsrc: its eight copies go between the
-    // products, whose execution covers their issue.
-    auto values = [&](int t, bool refill, const TileSrc& nsrc) __attribute__((always_inline)) {
-      const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
-      bf16x8 av[2][4], bp[2][2];
+    // the C^T operands of the next tile are read ahead, at the end of the
+    // previous product (its tile has landed by then), so that a product
+    // waits only for its P reads
+    bf16x8 av[2][4];
+    auto load_av = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
+    };
+    // value product of tile t (its C^T operands already in av): two 16-token
+    // halves, eight 32x32x16 products each.  With `refill`, once every
+    // operand read of slice v has completed, the slice is refilled with tile
+    // nsrc: its eight copies go between the products, whose execution covers
+    // their issue.  Then the operands of tile `next` (if >= 0) are read.
+    auto values = [&](int t, bool refill, const TileSrc& nsrc, int next) __attribute__((always_inline)) {
+      const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
+      bf16x8 bp[2][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bp[ks][0] = *(const MLA_LDS bf16x8*)(pb + pread[ks]);
@@ -575,6 +582,7 @@ decode_mfma_bf16(const DecodeArgs a) {
         if (refill && (i & 1) == 0) lat_copy(nsrc, i >> 1);
         sched_fence();
       }
+      if (next >= 0) load_av(next);
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -593,6 +601,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
       int blk_next = tile_block(4);
       if (ntiles > 0) {
+        load_av(0);
         issue_tile(2, tile_block(2));
         issue_tile(3, tile_block(3));
         if (first) wg_barrier();  // the score waves' reference exchange
@@ -602,14 +611,14 @@ decode_mfma_bf16(const DecodeArgs a) {
       }
       for (int s = 1; s < ntiles; ++s) {
         const TileSrc nsrc = tile_src(s + 3, blk_next);
-        values(s - 1, true, nsrc);  // slice v of tile s-1's buffer takes tile s+3
+        values(s - 1, true, nsrc, s);  // slice v of tile s-1's buffer takes tile s+3
         blk_next = tile_block(s + 4);
         wait_vmcnt<16>();  // tile s+1 (tiles s+2, s+3 may still be in flight)
         fix_tail(s + 1);
         wg_barrier();
       }
       wait_vmcnt<0>();
-      if (ntiles > 0) values(ntiles - 1, false, tile_src(0, 0));
+      if (ntiles > 0) values(ntiles - 1, false, tile_src(0, 0), -1);
       wg_barrier();  // overflow vote
       const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
       if (!again || !first) break;
@@ -687,12 +696,12 @@ decode_mfma_fp8(const DecodeArgs a) {
 
   // ---- copies.  Tile layout as in decode_mfma_bf16 (four 8 KB latent
   // slices, then the RoPE rows); the tile's token scales go to scl.
-  // Value wave 4+v stages slice v: lane l takes row l/2, codes 128 v +
-  // 64 (l%2) .. +63 (four 16-byte loads), ordinary loads tracked by the
-  // compiler; rows at or past the sequence's length, and tiles past the
-  // chunk (whose loads read block 0), are stored as zeros.  Score wave w copies RoPE rows 8w .. 8w+7 (one DMA
-  // copy) and score wave 0 also the 128 bytes of token scales (one copy on 8
-  // lanes); rows past the length are zeroed by fix_tail once landed.
+  // Value wave 4+v stages slice v (four 16-byte loads per lane, ordinary
+  // loads tracked by the compiler); rows at or past the sequence's length,
+  // and tiles past the chunk (whose loads read block 0), are stored as
+  // zeros.  Score wave w copies RoPE rows 8w .. 8w+7 (one DMA copy) and score
+  // wave 0 also the 128 bytes of token scales (one copy on 8 lanes); RoPE
+  // rows past the length are zeroed by fix_tail once landed.
   constexpr int kSliceBytes = 32 * 256;
   const int64_t bt_row = (int64_t)wk.b * a.max_blocks;
   auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
@@ -727,31 +736,41 @@ decode_mfma_fp8(const DecodeArgs a) {
       wait_vmcnt<1>();
   };
   // value waves: slice v of tile t staged in registers
-  const int srow = lane >> 1, shalf = lane & 1;
+  // Piece j of a lane is row 8 j + srow, codes 16 sc .. +15 of the slice
+  // (local chunks 2 sc, 2 sc + 1).  The eight lanes of a row read its 128
+  // contiguous codes; the rows of lanes 0-7 and 8-15 (and so on) differ in
+  // bit 2, which flips the parity of the row's swizzle, so the 16 lanes of a
+  // store hit 16 distinct bank groups.
+  const int srow = ((lane >> 3) & 1) * 4 + (lane >> 4), sc = lane & 7;
   struct Staged {
     u32x4 c[4];
   };
+  // wave-uniform base of tile t's rows, plus a per-lane 32-bit offset (a
+  // block's 64 rows span well under 4 GB)
+  uint32_t soff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) soff[j] = (uint32_t)((8 * j + srow) * a.lat_rs) + 128 * v + 16 * sc;
   auto stage_src = [&](int t, int blk) __attribute__((always_inline)) -> const uint8_t* {
     const bool upper = (t & 1) != 0;
-    return a.latent + blk * a.lat_bs + (int64_t)((upper ? 32 : 0) + srow) * a.lat_rs + 128 * v + 64 * shalf;
+    return a.latent + blk * a.lat_bs + (upper ? 32 * a.lat_rs : 0);
   };
   auto stage_load = [&](int t, int blk, Staged& st) __attribute__((always_inline)) {
     const uint8_t* lp = stage_src(t, blk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.c[j] = *(const u32x4*)(lp + 16 * j);
+    for (int j = 0; j < 4; ++j) st.c[j] = *(const u32x4*)(lp + soff[j]);
   };
-  // 16 codes -> two 16-byte chunks (8 bf16 each) of row srow, local chunks
-  // 8 shalf + 2 j, +1, at slot q ^ s16(srow) of slice v; a row at or past the
-  // length (or a tile past the chunk) is stored as zeros.  The test sits here,
-  // not after the loads, so that nothing waits for them before this point.
+  // piece j -> two 16-byte chunks (8 bf16 each) of row 8 j + srow, at slots
+  // (2 sc + e) ^ s16(row) of slice v; a row at or past the length (or a tile
+  // past the chunk) is stored as zeros.  The test sits here, not after the
+  // loads, so that nothing waits for them before this point.
   auto stage_piece = [&](int t, const Staged& st, int j, int e) __attribute__((always_inline)) {
-    MLA_LDS uint8_t* sb = tiles + (t % kBuf) * kTileBytes + v * kSliceBytes + srow * 256;
-    const bool ok = t < ntiles && wk.tok0 + t * kTileTok + srow < wk.len;
+    const int row = 8 * j + srow;
+    MLA_LDS uint8_t* sb = tiles + (t % kBuf) * kTileBytes + v * kSliceBytes + row * 256;
+    const bool ok = t < ntiles && wk.tok0 + t * kTileTok + row < wk.len;
     const uint32_t w0 = ok ? st.c[j][2 * e] : 0u, w1 = ok ? st.c[j][2 * e + 1] : 0u;
     const u32x4 bf = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
                       e4m3x2_to_bf16x2<true>(w1)};
-    const int q = 8 * shalf + 2 * j + e;
-    *(MLA_LDS u32x4*)(sb + ((q ^ s16(srow)) << 4)) = bf;
+    *(MLA_LDS u32x4*)(sb + (((2 * sc + e) ^ s16(row)) << 4)) = bf;
   };
   auto stage_store = [&](int t, const Staged& st) __attribute__((always_inline)) {
 #pragma unroll
@@ -1047,14 +1066,19 @@ decode_mfma_fp8(const DecodeArgs a) {
     // each.  With `refill`, once every operand read of slice v has completed,
     // the staged tile t+4 is converted into the slice and tile t+5 staged,
     // one 16-byte piece after each of the first eight products.
+    // Its C^T operands are read ahead, at the end of the previous product,
+    // as in decode_mfma_bf16; then the operands of tile `next` (if >= 0).
     Staged st;
-    auto values = [&](int t, bool refill, int nblk) __attribute__((always_inline)) {
-      const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
-      bf16x8 av[2][4], bp[2][2];
+    bf16x8 av[2][4];
+    auto load_av = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
+    };
+    auto values = [&](int t, bool refill, int nblk, int next) __attribute__((always_inline)) {
+      const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
+      bf16x8 bp[2][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bp[ks][0] = *(const MLA_LDS bf16x8*)(pb + pread[ks]);
@@ -1068,10 +1092,11 @@ decode_mfma_fp8(const DecodeArgs a) {
         oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
         if (refill && i < 8) {
           stage_piece(t + 4, st, i >> 1, i & 1);
-          if (i & 1) st.c[i >> 1] = *(const u32x4*)(lp + 16 * (i >> 1));
+          if (i & 1) st.c[i >> 1] = *(const u32x4*)(lp + soff[i >> 1]);
         }
         sched_fence();
       }
+      if (next >= 0) load_av(next);
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -1089,6 +1114,7 @@ decode_mfma_fp8(const DecodeArgs a) {
       wg_barrier();
 
       if (ntiles > 0) {
+        load_av(0);
         stage_load(2, tile_block(2), st);  // buffers 2, 3 are free (queries held, or the last pass over)
         stage_store(2, st);
         stage_load(3, tile_block(3), st);
@@ -1099,10 +1125,10 @@ decode_mfma_fp8(const DecodeArgs a) {
       }
       for (int s = 1; s < ntiles; ++s) {
         // slice v of tile s-1's buffer takes tile s+3 (staged last iteration); tile s+4 is staged
-        values(s - 1, true, tile_block(s + 4));
+        values(s - 1, true, tile_block(s + 4), s);
         wg_barrier();
       }
-      if (ntiles > 0) values(ntiles - 1, false, 0);
+      if (ntiles > 0) values(ntiles - 1, false, 0, -1);
       wg_barrier();  // overflow vote
       const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
       if (!again || !first) break;
