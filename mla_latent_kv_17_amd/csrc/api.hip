@@ -83,7 +83,7 @@ int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int
   mla::AbsorbArgs a{q_nope, w_uk, q_lat, rows, dims->heads};
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == MLA_BF16) {
-    dim3 grid(dims->heads * 2);  // (head, half of d_latent)
+    dim3 grid(dims->heads * 4);  // (head, quarter of d_latent)
     if (q_lat_dtype == MLA_BF16)
       st = launch("mla::absorb_q_mfma<true>", (const void*)mla::absorb_q_mfma<true>, grid, dim3(256), a, s);
     else
