@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s
+FP32_VECTOR_PEAK = 157.3e12  # fp32 vector FLOP/s
 METRIC = "MLA decode KV-tokens/s + achieved TB/s & TFLOP/s vs roofline (H=128,B=32,T=4K)"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_bf16_b32_h128_t4k_counters.json")
 
@@ -46,14 +47,15 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    or None when the decode kernel source changed since they were taken."""
+    or None for another workload than theirs, or when the decode kernel
+    source changed since they were taken."""
     try:
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    if c.get("decode_source_hash") != decode_source_hash():
+    if not str(c.get("workload", "")).startswith(workload + " ") or c.get("decode_source_hash") != decode_source_hash():
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -248,8 +250,18 @@ def main():
 
     eager_ms_per_step = float(step_ms.mean())
     ms_per_step = eager_ms_per_step
-    achieved = cache_bytes / (dec_avg * 1e-3)
-    traffic = measured_traffic()
+    traffic = measured_traffic(wl.name)
+    # which roof bounds the decode: its flops per cache byte against the ridge
+    # of the peak it would run at (bf16 matrix cores, or fp32 vector ALUs for
+    # the fp32 cache)
+    flop_peak = FP32_VECTOR_PEAK if wl.cache_dtype == "f32" else MFMA_BF16_PEAK
+    if decode_flops / cache_bytes > flop_peak / HBM_PEAK:
+        roof = {"bound": "mfma" if wl.cache_dtype != "f32" else "alu",
+                "achieved": decode_flops / (dec_avg * 1e-3) / 1e12, "peak": flop_peak / 1e12, "unit": "TFLOP/s",
+                "frac": decode_flops / (dec_avg * 1e-3) / flop_peak, "algorithmic_flops": decode_flops}
+    else:
+        roof = {"bound": "hbm", "achieved": cache_bytes / (dec_avg * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": cache_bytes / (dec_avg * 1e-3) / HBM_PEAK}
     out = {
         "metric": METRIC,
         "value": kv_tokens / (ms_per_step * 1e-3),
@@ -267,8 +279,7 @@ def main():
                    "q_per_seq": wl.q_per_seq, "heads": wl.heads, "d_latent": 512, "d_rope": 64, "d_head": 128,
                    "block_size": 64, "cache_dtype": wl.cache_dtype, "num_splits": step.num_splits,
                    "steps_timed": "absorb_q + decode + split_combine + out_uv, caches evicted before each"},
-        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": traffic,
+        "roofline": {**roof, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                                      "calibrated on a 256 MiB copy)",
                      "kernel": DECODE_KERNEL[wl.cache_dtype], "launch_ms": dec_avg,
