@@ -106,7 +106,28 @@ def cpu_baseline(inp, budget_s: float):
     kv_equiv = sum(int(inp.seq_lens[b]) for b, _ in done) / wl.heads
     return {"value": kv_equiv / el, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(done)} (sequence, head) rows of {wl.name} ({wl.batch * wl.heads} in a step), "
-                      f"explicit fp64 K/V reconstruction, {el:.1f} s"}
+                      f"explicit fp64 K/V reconstruction, {el:.1f} s",
+            "cpu_model": cpu_model(), "blas": blas_vendor()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def blas_vendor() -> str:
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001
+        return "unknown"
 
 
 def main():
@@ -161,6 +182,10 @@ def main():
     pairs = sum(max(0, int(L) - (wl.q_per_seq - 1 - i)) for L in inp.seq_lens for i in range(wl.q_per_seq))
     decode_flops = pairs * wl.heads * 2 * (576 + 512)
     proj_flops = 2 * (wl.batch * wl.q_per_seq) * wl.heads * 2 * 128 * 512
+    # queries read (q_lat | q_rope) and outputs written (o_lat, or the chunk
+    # partials, and lse) by the decode
+    q_bytes = wl.batch * rows * (512 + 64) * (4 if wl.q_dtype == "f32" else 2)
+    io_bytes = q_bytes + wl.batch * step.num_splits * rows * (512 + 1) * 4
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     flush.fill_(1.0)
@@ -278,7 +303,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": int(inp.seq_lens.max()),
                    "q_per_seq": wl.q_per_seq, "heads": wl.heads, "d_latent": 512, "d_rope": 64, "d_head": 128,
                    "block_size": 64, "cache_dtype": wl.cache_dtype, "num_splits": step.num_splits,
-                   "steps_timed": "absorb_q + decode + split_combine + out_uv, caches evicted before each"},
+                   "steps_timed": "absorb_q + decode + the split merge fused into out_uv (combine_out_uv; split_combine "
+                                  "+ out_uv above 8 chunks, out_uv alone for one chunk), caches evicted before each"},
         "roofline": {**roof, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                                      "calibrated on a 256 MiB copy)",
@@ -288,6 +314,11 @@ def main():
         "decode_tflops": decode_flops / (dec_avg * 1e-3) / 1e12,
         "decode_mfma_frac": decode_flops / (dec_avg * 1e-3) / MFMA_BF16_PEAK,
         "kv_tokens_per_step": kv_tokens,
+        # (query token, visible KV token) pairs: differs from KV tokens when S_q > 1
+        "query_kv_pairs_per_step": pairs,
+        "query_kv_pairs_per_s": pairs / (ms_per_step * 1e-3),
+        # the decode's bytes with its queries read and its outputs written
+        "decode_gbps_cache_q_o": (cache_bytes + io_bytes) / (dec_avg * 1e-3) / 1e9,
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "graph_ms_per_step": float(graph_ms.mean()) if graph_ms is not None else None,
         "step_tflops": (decode_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,

@@ -32,7 +32,13 @@
  *  - Arguments are validated on the host before any launch; an invalid call
  *    returns a negative mla_status and enqueues nothing.  Device-side data
  *    (block_table, seq_lens) is trusted: entries must name blocks below
- *    num_blocks and lengths must fit max_blocks_per_seq * block_size.
+ *    num_blocks and lengths must fit max_blocks_per_seq * block_size.  With
+ *    the environment variable MLA_CHECK set to 1 at the call, mla_decode
+ *    checks them too: it copies both arrays to the host on `stream`,
+ *    synchronizes it (the one exception to the rule below), and returns
+ *    MLA_ERR_SHAPE without launching if a length is negative or too long or
+ *    a block id among a sequence's first ceil(len / block_size) entries is
+ *    outside [0, num_blocks); MLA_ERR_DEVICE if the copy fails.
  *  - Supported sizes: d_latent = 512, d_rope = 64, d_head = 128,
  *    block_size = 64, 1 <= q_per_seq <= 2; anything else is MLA_ERR_SHAPE.
  *  - Thread-safe: the library holds no mutable global state.
@@ -46,8 +52,8 @@
 extern "C" {
 #endif
 
-/* 2: adds mla_combine_out_uv */
-#define MLA_ABI_VERSION 2
+/* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode */
+#define MLA_ABI_VERSION 3
 
 typedef enum mla_dtype {
   MLA_F32 = 0,

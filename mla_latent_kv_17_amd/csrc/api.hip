@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "mla.h"
 #include "mla_kernels.h"
 
@@ -23,6 +25,34 @@ int elem_size(int32_t dt) {
     case MLA_FP8_E4M3: return 1;
     default: return 0;
   }
+}
+
+// MLA_CHECK=1 in the environment at the call: mla_decode validates the
+// device-side paging data before launching (read back on the stream).
+bool check_mode() {
+  const char* e = getenv("MLA_CHECK");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// Every length in [0, max_blocks_per_seq * block_size] and every block id a
+// sequence uses (its first ceil(len / block_size) table entries) in
+// [0, num_blocks); MLA_ERR_DEVICE if the read-back fails.
+int check_paging(int32_t batch, const mla_paged_kv* kv, hipStream_t s) {
+  std::vector<int32_t> lens((size_t)batch), table((size_t)batch * kv->max_blocks_per_seq);
+  if (hipMemcpyAsync(lens.data(), kv->seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(table.data(), kv->block_table, table.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = lens[b];
+    if (len < 0 || len > (int64_t)kv->max_blocks_per_seq * kv->block_size) return MLA_ERR_SHAPE;
+    const int64_t pages = (len + kv->block_size - 1) / kv->block_size;
+    for (int64_t p = 0; p < pages; ++p) {
+      const int32_t blk = table[(size_t)b * kv->max_blocks_per_seq + p];
+      if (blk < 0 || blk >= kv->num_blocks) return MLA_ERR_SHAPE;
+    }
+  }
+  return MLA_OK;
 }
 
 int check_dims(const mla_dims* d) {
@@ -129,6 +159,10 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   if (dims->batch == 0) return MLA_OK;
   const int64_t units = (int64_t)dims->batch * num_splits;
   if (units > (1 << 24)) return MLA_ERR_SHAPE;
+  if (check_mode()) {
+    st = check_paging(dims->batch, kv, (hipStream_t)stream);
+    if (st) return st;
+  }
 
   mla::DecodeArgs a;
   a.q_lat = (const uint16_t*)q_lat;

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 2
+    assert M.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
