@@ -52,8 +52,9 @@
 extern "C" {
 #endif
 
-/* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode */
-#define MLA_ABI_VERSION 3
+/* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
+ * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv */
+#define MLA_ABI_VERSION 4
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -168,11 +169,12 @@ int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_p
  *   out[r][h][d] = sum_c w_uv[h][d][c] * o_lat[r][h][c].
  * o_lat: [batch*q_per_seq][heads][d_latent] fp32
  * w_uv:  [heads][d_head][d_latent], w_dtype (F32 or BF16)
- * out:   [batch*q_per_seq][heads][d_head] fp32
+ * out:   [batch*q_per_seq][heads][d_head], out_dtype: F32, or BF16 rounded to
+ *        nearest-even from the fp32 sum; anything else is MLA_ERR_DTYPE
  * With BF16 weights the fp32 o_lat is split into two bf16 terms (hi + lo), so
- * the result carries fp32-level accuracy at matrix-core speed. */
+ * the sum carries fp32-level accuracy at matrix-core speed. */
 int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32_t w_dtype,
-               float* out, void* stream);
+               void* out, int32_t out_dtype, void* stream);
 
 /* The merge of mla_split_combine and the projection of mla_out_uv in one call,
  * for num_splits > 1 (same formulas, same passages): o_lat is formed on the fly
@@ -180,11 +182,13 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
  *   out[r][h][d] = sum_c w_uv[h][d][c] * (sum_s exp(lse_s - lse) o_s[r][h][c]),
  *   lse[r][h]    = ln sum_s exp(lse_s).
  * o_part, lse_part: mla_decode's outputs for num_splits > 1 (layouts above);
- * w_uv, w_dtype, out: as for mla_out_uv; lse: [batch*q_per_seq][heads] fp32, or NULL.
+ * w_uv, w_dtype, out, out_dtype: as for mla_out_uv; lse: [batch*q_per_seq][heads]
+ * fp32, or NULL.
  * Chunks with lse_s = -inf carry weight 0 (their o_s is not read); a row whose
  * chunks all do gets out = 0 and lse = -inf.  Same accuracy as the two calls. */
 int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
-                       const void* w_uv, int32_t w_dtype, float* out, float* lse, void* stream);
+                       const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, float* lse,
+                       void* stream);
 
 /* A launch-shape helper: the num_splits mla_decode should use so that the
  * device's compute units are filled, given the longest sequence length the

@@ -81,8 +81,8 @@ def _load():
         "mla_absorb_q": ([dp, vp, vp, i32, vp, i32, vp], ctypes.c_int),
         "mla_decode": ([dp, vp, vp, i32, kvp, i32, f32p, f32p, vp], ctypes.c_int),
         "mla_split_combine": ([dp, i32, f32p, f32p, f32p, f32p, vp], ctypes.c_int),
-        "mla_out_uv": ([dp, f32p, vp, i32, f32p, vp], ctypes.c_int),
-        "mla_combine_out_uv": ([dp, i32, f32p, f32p, vp, i32, f32p, f32p, vp], ctypes.c_int),
+        "mla_out_uv": ([dp, f32p, vp, i32, vp, i32, vp], ctypes.c_int),
+        "mla_combine_out_uv": ([dp, i32, f32p, f32p, vp, i32, vp, i32, f32p, vp], ctypes.c_int),
         "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -177,16 +177,16 @@ def mla_split_combine(dims: MlaDims, num_splits: int, o_part, lse_part, o_lat, l
 
 
 def mla_out_uv(dims: MlaDims, o_lat, w_uv, out, stream=None):
-    """out[r][h][:] = W_UV[h] o_lat[r][h][:]."""
+    """out[r][h][:] = W_UV[h] o_lat[r][h][:]; out is fp32 or bf16."""
     _check("mla_out_uv", _lib.mla_out_uv(ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _dtype_code(w_uv),
-                                         _ptr(out), _stream(stream)))
+                                         _ptr(out), _dtype_code(out), _stream(stream)))
 
 
 def mla_combine_out_uv(dims: MlaDims, num_splits: int, o_part, lse_part, w_uv, out, lse=None, stream=None):
-    """out[r][h][:] = W_UV[h] (log-sum-exp merge of the chunk partials), lse = merged lse."""
+    """out[r][h][:] = W_UV[h] (log-sum-exp merge of the chunk partials), lse = merged lse; out is fp32 or bf16."""
     _check("mla_combine_out_uv", _lib.mla_combine_out_uv(ctypes.byref(dims), int(num_splits), _ptr(o_part),
                                                          _ptr(lse_part), _ptr(w_uv), _dtype_code(w_uv), _ptr(out),
-                                                         _ptr(lse), _stream(stream)))
+                                                         _dtype_code(out), _ptr(lse), _stream(stream)))
 
 
 def mla_decode_num_splits(dims: MlaDims, max_seq_len: int) -> int:

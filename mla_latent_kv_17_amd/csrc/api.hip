@@ -223,16 +223,18 @@ int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_p
   return st;
 }
 
-int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32_t w_dtype, float* out,
-               void* stream) {
+int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32_t w_dtype, void* out,
+               int32_t out_dtype, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
   if (w_dtype != MLA_F32 && w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
   const int rows = dims->batch * dims->q_per_seq;
   if (rows == 0) return MLA_OK;
-  mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads, nullptr, nullptr, nullptr, 1, dims->q_per_seq};
+  mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads, nullptr, nullptr, nullptr, 1, dims->q_per_seq,
+                   out_dtype == MLA_BF16};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
     st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3((dims->heads + 7) / 8 * 16),
@@ -245,16 +247,18 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
 }
 
 int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
-                       const void* w_uv, int32_t w_dtype, float* out, float* lse, void* stream) {
+                       const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, float* lse, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!o_part || !lse_part || !w_uv || !out) return MLA_ERR_NULL;
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
   if (w_dtype != MLA_F32 && w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (!aligned16(o_part) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
   const int rows = dims->batch * dims->q_per_seq;
   if (rows == 0) return MLA_OK;
-  mla::OutUvArgs a{nullptr, w_uv, out, rows, dims->heads, o_part, lse_part, lse, num_splits, dims->q_per_seq};
+  mla::OutUvArgs a{nullptr, w_uv, out, rows, dims->heads, o_part, lse_part, lse, num_splits, dims->q_per_seq,
+                   out_dtype == MLA_BF16};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
     st = launch("mla::merge_out_uv_mfma", (const void*)mla::merge_out_uv_mfma, dim3((dims->heads + 7) / 8 * 16),

@@ -34,6 +34,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {
   return __builtin_bit_cast(uint16_t, (__bf16)a);
 }
 
+// One output element of the projections: fp32, or rounded to bf16.
+__device__ __forceinline__ void store_out(void* out, int64_t i, float v, int bf16) {
+  if (bf16)
+    ((uint16_t*)out)[i] = f32_to_bf16_bits(v);
+  else
+    ((float*)out)[i] = v;
+}
+
 // Two OCP E4M3FN codes (bytes 0,1 or bytes 2,3 of `w`) -> two bf16; exact
 // (a 3-bit mantissa and the E4M3 exponent range fit bf16).
 template <bool kHi>

@@ -50,13 +50,14 @@ __global__ void split_combine(const CombineArgs a);
 struct OutUvArgs {
   const float* o_lat;     // [R][H][512] (unmerged form)
   const void* w;          // [H][128][512]
-  float* out;             // [R][H][128]
+  void* out;              // [R][H][128], fp32 or (out_bf16) bf16 bits
   int rows, heads;        // R = B * S_q
   // merged form: o_lat = log-sum-exp merge of the chunk partials
   const float* o_part;    // [B][ns][S_q][H][512]
   const float* lse_part;  // [B][ns][S_q][H]
   float* lse;             // [R][H] or null
   int num_splits, sq;
+  int out_bf16;           // 1: round the fp32 sums to bf16 (nearest even)
 };
 __global__ void out_uv_mfma(const OutUvArgs a);        // bf16 weights, hi/lo split of o_lat
 __global__ void merge_out_uv_mfma(const OutUvArgs a);  // the same with the chunk merge on the way

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256) out_uv_mfma(const OutUvArgs a) {
       const int row = idx >> 6, d = idx & 63, nt = d >> 5, n = d & 31;
       const float v = red[0][nt][row * kPad + n] + red[1][nt][row * kPad + n] + red[2][nt][row * kPad + n] +
                       red[3][nt][row * kPad + n];
-      if (m0 + row < a.rows) a.out[((int64_t)(m0 + row) * a.heads + h) * 128 + half * 64 + d] = v;
+      if (m0 + row < a.rows) store_out(a.out, ((int64_t)(m0 + row) * a.heads + h) * 128 + half * 64 + d, v, a.out_bf16);
     }
     __syncthreads();
   }
@@ -278,7 +278,7 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
       const int row = idx >> 6, d = idx & 63, nt = d >> 5, n = d & 31;
       const float v = red[0][nt][row * kPad + n] + red[1][nt][row * kPad + n] + red[2][nt][row * kPad + n] +
                       red[3][nt][row * kPad + n];
-      if (m0 + row < a.rows) a.out[((int64_t)(m0 + row) * a.heads + h) * 128 + half * 64 + d] = v;
+      if (m0 + row < a.rows) store_out(a.out, ((int64_t)(m0 + row) * a.heads + h) * 128 + half * 64 + d, v, a.out_bf16);
     }
     __syncthreads();  // red, xs and wt are rewritten by the next tile
   }
@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(128) out_uv_f32(const OutUvArgs a) {
     acc = fmaf(wv[2], xs[c + 2], acc);
     acc = fmaf(wv[3], xs[c + 3], acc);
   }
-  a.out[((int64_t)r * a.heads + h) * 128 + d] = acc;
+  store_out(a.out, ((int64_t)r * a.heads + h) * 128 + d, acc, a.out_bf16);
 }
 
 template __global__ void out_uv_f32<false>(const OutUvArgs);

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 3
+    assert M.abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -78,8 +78,14 @@ def test_other_entry_points_validation():
     assert L.mla_split_combine(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, None, None) == M.MLA_ERR_SPLITS
     assert L.mla_split_combine(ctypes.byref(d), 4, None, 0x2000, 0x3000, None, None) == M.MLA_ERR_NULL
     assert L.mla_split_combine(ctypes.byref(d), 4, 0x1004, 0x2000, 0x3000, None, None) == M.MLA_ERR_ALIGN
-    assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_FP8_E4M3, 0x3000, None) == M.MLA_ERR_DTYPE
-    assert L.mla_out_uv(ctypes.byref(d), None, 0x2000, M.MLA_BF16, 0x3000, None) == M.MLA_ERR_NULL
+    assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_FP8_E4M3, 0x3000, M.MLA_F32, None) == M.MLA_ERR_DTYPE
+    assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_BF16, 0x3000, M.MLA_FP8_E4M3, None) == M.MLA_ERR_DTYPE
+    assert L.mla_out_uv(ctypes.byref(d), None, 0x2000, M.MLA_BF16, 0x3000, M.MLA_F32, None) == M.MLA_ERR_NULL
+    assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_BF16, 0x3008, M.MLA_BF16, None) == M.MLA_ERR_ALIGN
+    assert L.mla_combine_out_uv(ctypes.byref(d), 4, 0x1000, 0x2000, 0x3000, M.MLA_BF16, 0x4000, 7, None,
+                                None) == M.MLA_ERR_DTYPE
+    assert L.mla_combine_out_uv(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, M.MLA_BF16, 0x4000, M.MLA_F32, None,
+                                None) == M.MLA_ERR_SPLITS
     out = ctypes.c_int32(0)
     assert L.mla_decode_num_splits(ctypes.byref(d), 100, None) == M.MLA_ERR_NULL
     assert L.mla_decode_num_splits(ctypes.byref(d), -1, ctypes.byref(out)) == M.MLA_ERR_SHAPE

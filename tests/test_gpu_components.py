@@ -72,6 +72,33 @@ def test_out_uv_bf16_weights(rows):
     check(f"out_uv rows={rows}", out.cpu().numpy(), ref, "f32")
 
 
+@pytest.mark.parametrize("rows,wdt,ns", [(37, "bf16", 1), (5, "f32", 1), (6, "bf16", 3), (3, "f32", 3)])
+def test_projection_bf16_output(rows, wdt, ns):
+    """A bf16 output is the round-to-nearest-even of the same call's fp32
+    output, bit for bit (the sums are the same; only the store differs)."""
+    import torch
+    import mla_latent_kv_17_amd as M
+    print(f"[case] projection bf16 out rows={rows} w={wdt} ns={ns}", flush=True)
+    rng = np.random.default_rng(3600 + rows)
+    wf = rng.standard_normal((H, 128, 512), dtype=np.float32) * np.float32(1.0 / math.sqrt(512))
+    w_dev = _bf16_tensor(MI.bf16_bits(wf)) if wdt == "bf16" else torch.from_numpy(wf).cuda()
+    dims = M.make_dims(rows, 1, H)
+    out32 = torch.empty((rows, H, 128), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((rows, H, 128), dtype=torch.bfloat16, device="cuda")
+    if ns == 1:
+        o_lat = torch.from_numpy(rng.standard_normal((rows, H, 512)).astype(np.float32) * np.float32(0.05)).cuda()
+        M.mla_out_uv(dims, o_lat, w_dev, out32)
+        M.mla_out_uv(dims, o_lat, w_dev, out16)
+    else:
+        o_part, lse_part = _combine_case(rows, ns, 1, H, 3700 + rows)
+        op, lp = torch.from_numpy(o_part * np.float32(0.05)).cuda(), torch.from_numpy(lse_part).cuda()
+        M.mla_combine_out_uv(dims, ns, op, lp, w_dev, out32)
+        M.mla_combine_out_uv(dims, ns, op, lp, w_dev, out16)
+    got = out16.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = MI.bf16_bits(out32.cpu().numpy())
+    assert np.array_equal(got, want)
+
+
 def _combine_case(B, ns, Sq, heads, seed):
     rng = np.random.default_rng(seed)
     o_part = rng.standard_normal((B, ns, Sq, heads, 512)).astype(np.float32)
