@@ -323,6 +323,46 @@ def generate(wl: Workload, seed: Optional[int] = None, poison: bool = True) -> I
     )
 
 
+# ----------------------------------------------------------------------------
+# cache-append inputs (the step that writes the S_q new tokens of a sequence)
+# ----------------------------------------------------------------------------
+
+# Hidden width of the tokens entering the cache.  The pages do not state it;
+# 5120 is DeepSeek-V2's published model width, used as the measured size
+# (the append takes any multiple of 64).
+APPEND_D_MODEL = 5120
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    d_model: int
+    h: np.ndarray        # [B*S_q][d_model]   hidden states of the new tokens
+    w_dkv: np.ndarray    # [512][d_model]     latent down-projection
+    w_kr: np.ndarray     # [64][d_model]      position-key projection
+    rope_theta: float
+
+
+def generate_append(wl: Workload, d_model: int = APPEND_D_MODEL, seed: Optional[int] = None,
+                    one_hot: bool = False) -> AppendInputs:
+    """Draws h ~ N(0, 1) and both projections ~ N(0, std 1/sqrt(d_model)), so
+    c and the position key come out near unit variance like the cached rows;
+    encoded as the workload's weights (bf16, or fp32 for the fp32 cache).
+    Draw order: h, W_DKV, W_KR, from seed + 500.  With `one_hot`, row r of h
+    is instead the unit vector e_(r*7 mod d_model): each product is then a
+    single weight, exact in every precision."""
+    rng = np.random.default_rng((wl.seed if seed is None else seed) + 500)
+    T = wl.batch * wl.q_per_seq
+    h = rng.standard_normal((T, d_model), dtype=np.float32)
+    std = np.float32(1.0 / math.sqrt(d_model))
+    w_dkv = rng.standard_normal((D_LATENT, d_model), dtype=np.float32) * std
+    w_kr = rng.standard_normal((D_ROPE, d_model), dtype=np.float32) * std
+    if one_hot:
+        h = np.zeros((T, d_model), dtype=np.float32)
+        h[np.arange(T), (np.arange(T) * 7) % d_model] = 1.0
+    return AppendInputs(d_model=d_model, h=_encode(h, wl.w_dtype), w_dkv=_encode(w_dkv, wl.w_dtype),
+                        w_kr=_encode(w_kr, wl.w_dtype), rope_theta=10000.0)
+
+
 def depaged(inp: Inputs) -> Inputs:
     """Same logical cache, rewritten as a contiguous pool with an identity
     page table (sequence b owns blocks b*max_blocks ...).  Used to check that

@@ -23,12 +23,20 @@ Sources (the pages this follows; the short names are used below):
   Interviews": MHA caches 2 x n_heads x d_head, GQA 2 x n_groups x d_head, MLA
   d_latent plus the small RoPE part, per token per layer.
 
+The cache append (the step before decode) follows [DF-latent] too: the
+latent is the down-projection c_t = W_DKV h_t, and a separate 64-wide key
+carries the position because RoPE would break the absorbed projections.
+
 What the pages leave open (read plainly, listed with reasons in the design
 notes of the repository): the softmax scale is 1/sqrt(d_head + d_rope); one
 k^R row per token is shared by all heads while q_rope is per head; inputs are
 already RoPE-rotated; W_UK and W_UV are stored per head as [d_head][d_latent]
 so that k = W_UK c; with S_q query tokens per sequence, query i sees the first
-len - (S_q - 1 - i) cached tokens (its own included).
+len - (S_q - 1 - i) cached tokens (its own included).  For the append: the
+position key is k^R = RoPE_p(W_KR h) with the textbook rotation (pairs
+(2j, 2j+1) turned by p * theta^(-2j/64), theta = 10000); the S_q new tokens
+of a sequence sit at positions len - S_q + i; an fp8 cache row holds E4M3
+codes of c / s with s = max |c| / 448.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 facts fixed outside this file -- numbers the pages print, closed forms, a
@@ -53,6 +61,8 @@ __all__ = [
     "explicit_decode", "absorbed_decode", "split_ranges", "split_partials",
     "combine_partials", "cache_numbers_per_token_layer", "cache_bytes",
     "default_softmax_scale", "absorb_queries", "project_output",
+    "down_project", "rope_angles", "rope_rotate", "e4m3_values", "e4m3_round_codes",
+    "quantize_latent", "appended_tokens",
 ]
 
 
@@ -347,3 +357,86 @@ def cache_numbers_per_token_layer(scheme: str, *, heads: int = 0, d_head: int = 
 def cache_bytes(numbers_per_token_layer: float, layers: int, context: int, bytes_per: int = 2):
     """Whole-cache bytes for one sequence."""
     return numbers_per_token_layer * layers * context * bytes_per
+
+
+# ----------------------------------------------------------------------------
+# cache append ([DF-latent]: c_t = W_DKV h_t, and a separate 64-wide key that
+# carries the position)
+# ----------------------------------------------------------------------------
+
+def down_project(h: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Rows of h times W^T in fp64: c[r][n] = sum_k w[n][k] h[r][k]
+    (c_t = W_DKV h_t for each token; the same map gives W_KR h_t)."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def rope_angles(pos: int, theta: float = 10000.0, d: int = D_ROPE) -> np.ndarray:
+    """Rotation angle of each pair (2j, 2j+1) of a d-wide key at position pos:
+    pos * theta^(-2j/d)."""
+    j = np.arange(d // 2, dtype=np.float64)
+    return float(pos) * np.power(float(theta), -2.0 * j / d)
+
+
+def rope_rotate(x: np.ndarray, pos: int, theta: float = 10000.0) -> np.ndarray:
+    """Turn each pair (x[2j], x[2j+1]) of the last axis by its angle at pos."""
+    x = np.asarray(x, dtype=np.float64)
+    a = rope_angles(pos, theta, x.shape[-1])
+    c, s = np.cos(a), np.sin(a)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def e4m3_values() -> np.ndarray:
+    """Values of the finite non-negative OCP E4M3FN codes 0x00 .. 0x7E (the
+    decoding definition above applied to each code)."""
+    return decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_round_codes(x: np.ndarray) -> np.ndarray:
+    """E4M3FN code bytes of finite values with |x| <= 448: the nearest code
+    value by exhaustive comparison, a tie going to the even code; the sign
+    goes to bit 7 (also for zero, from the sign bit)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x).reshape(-1)
+    vals = e4m3_values()
+    d = np.abs(a[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among equally near codes (at most two, adjacent) take the even one
+    even = cand & (np.arange(vals.size)[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1)).astype(np.uint8)
+    return np.where(np.signbit(x.reshape(-1)), pick | np.uint8(0x80), pick).reshape(x.shape)
+
+
+def quantize_latent(c: np.ndarray):
+    """One token's fp8 cache row, the decisions taken in float32 as the
+    encoder that writes the cache takes them: s = max|c| / 448 (1 for an
+    all-zero c), q = c / s clamped to +-448, codes = E4M3 of q.
+    Returns (codes uint8, s float32)."""
+    c = np.asarray(c, dtype=np.float32)
+    amax = np.float32(np.abs(c).max())
+    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    q = np.clip(c / s, np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    return e4m3_round_codes(q.astype(np.float64)), s
+
+
+def appended_tokens(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, seq_lens, q_per_seq: int,
+                    theta: float = 10000.0):
+    """The rows the append writes: for token i of sequence b (row b*S_q + i of
+    h) at position p = len_b - S_q + i >= 0, c = W_DKV h and
+    k^R = RoPE_p(W_KR h) in fp64.  Returns a list of (b, p, c, k^R)."""
+    out = []
+    c_all = down_project(h, w_dkv)
+    k_all = down_project(h, w_kr)
+    for b, ln in enumerate(np.asarray(seq_lens)):
+        for i in range(q_per_seq):
+            p = int(ln) - q_per_seq + i
+            if p < 0:
+                continue
+            r = b * q_per_seq + i
+            out.append((b, p, c_all[r], rope_rotate(k_all[r], p, theta)))
+    return out
+

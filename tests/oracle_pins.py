@@ -16,6 +16,8 @@ from types import SimpleNamespace
 
 import numpy as np
 
+import mla_inputs as MI
+
 import oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -356,7 +358,96 @@ def check_absorb_project_identities():
         assert ob[0, h, d] == sum(float(t.w_uv[h, d, c]) * x[0, h, c] for c in range(DL))
 
 
+def check_append_projection():
+    """c_t = W_DKV h_t ([DF-latent], formula box): a one-hot h picks one column
+    of W exactly, and a hand-computed case."""
+    rng = np.random.default_rng(21)
+    w = rng.standard_normal((DL, 320))
+    for k in (0, 7, 319):
+        h = np.zeros((1, 320))
+        h[0, k] = 1.0
+        assert np.array_equal(O.down_project(h, w)[0], w[:, k])
+    # [[1, 2, 3], [4, 5, 6]] times (1, -1, 2): (1 - 2 + 6, 4 - 5 + 12)
+    got = O.down_project(np.array([[1.0, -1.0, 2.0]]), np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]]))
+    assert np.array_equal(got, np.array([[5.0, 11.0]]))
+
+
+def check_rope():
+    """The position key's rotation: textbook values (pair (2j, 2j+1) turned by
+    p * 10000^(-2j/64)) and the properties that define it."""
+    a = O.rope_angles(1)
+    assert a.shape == (32,) and a[0] == 1.0
+    assert abs(a[8] - 0.1) < 1e-15 and abs(a[16] - 0.01) < 1e-15     # 10000^(-1/4), 10000^(-1/2)
+    cos1, sin1 = 0.5403023058681398, 0.8414709848078965              # cos 1, sin 1
+    x = np.zeros(64)
+    x[0] = 1.0
+    y = O.rope_rotate(x, 1)
+    assert abs(y[0] - cos1) < 1e-15 and abs(y[1] - sin1) < 1e-15 and not y[2:].any()
+    x = np.zeros(64)
+    x[33] = 1.0                                                       # pair 16, second member
+    y = O.rope_rotate(x, 100)                                         # angle 100 * 0.01 = 1
+    assert abs(y[32] + sin1) < 1e-14 and abs(y[33] - cos1) < 1e-14
+    assert not np.delete(y, [32, 33]).any()
+    rng = np.random.default_rng(22)
+    v, u = rng.standard_normal(64), rng.standard_normal(64)
+    assert np.array_equal(O.rope_rotate(v, 0), v)
+    r = O.rope_rotate(v, 12345)
+    assert np.allclose(r[0::2] ** 2 + r[1::2] ** 2, v[0::2] ** 2 + v[1::2] ** 2, rtol=1e-12)
+    assert rel_l2(O.rope_rotate(O.rope_rotate(v, 5), 7), O.rope_rotate(v, 12)) <= 1e-13
+    # scores depend on the distance between positions only
+    d1 = O.rope_rotate(v, 40) @ O.rope_rotate(u, 17)
+    d2 = O.rope_rotate(v, 1040) @ O.rope_rotate(u, 1017)
+    assert abs(d1 - d2) <= 1e-10 * max(1.0, abs(d1))
+
+
+def check_e4m3_encoding():
+    """Encoding to OCP E4M3FN: hand-derived codes (nearest code value, a tie
+    going to the even code) and agreement with the input generator's
+    bit-level encoder, a separate implementation."""
+    cases = {1.0: 0x38, 1.0625: 0x38, 1.1875: 0x3A, -1.0: 0xB8, 448.0: 0x7E, 240.0: 0x77,
+             0.1: 0x1D, 2.0 ** -6: 0x08, 2.0 ** -10: 0x00, 1.5 * 2.0 ** -9: 0x02, -0.0: 0x80}
+    got = O.e4m3_round_codes(np.array(list(cases)))
+    assert list(got) == list(cases.values()), list(got)
+    rng = np.random.default_rng(23)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 2.0 ** -7,
+                        rng.standard_normal(2000)]).astype(np.float32)
+    assert np.array_equal(O.e4m3_round_codes(x.astype(np.float64)), MI.e4m3_codes(x))
+
+
+def check_fp8_row():
+    """One token's fp8 cache row: the worked example by hand (scale 3/448;
+    0.5/scale = 74.67 -> 72 = code 105, -3/scale = -448 -> 0xFE, 1/scale =
+    149.3 -> 144 = code 113), the largest element at +-448 exactly, zeros."""
+    codes, s = O.quantize_latent(np.array([0.5, -3.0, 1.0], dtype=np.float32))
+    assert s == np.float32(3.0) / np.float32(448.0)
+    assert list(codes) == [105, 254, 113]
+    codes, s = O.quantize_latent(np.zeros(512, dtype=np.float32))
+    assert s == 1.0 and not codes.any()
+    rng = np.random.default_rng(24)
+    c = rng.standard_normal(512).astype(np.float32)
+    codes, s = O.quantize_latent(c)
+    k = int(np.argmax(np.abs(c)))
+    assert codes[k] & 0x7F == 0x7E
+    back = O.decode_e4m3(codes) * float(s)
+    # within half a code step (relative 1/16 at most) of the value
+    assert np.all(np.abs(back - c) <= np.abs(c) / 16 + 2.0 ** -10 * float(s))
+
+
+def check_append_positions():
+    """The rows the append writes: token i of sequence b at position
+    len_b - S_q + i, none where that is negative; the key of a position-0
+    token is its plain projection."""
+    rng = np.random.default_rng(25)
+    h = rng.standard_normal((4, 64))
+    w_dkv, w_kr = rng.standard_normal((DL, 64)), rng.standard_normal((64, 64))
+    out = O.appended_tokens(h, w_dkv, w_kr, [5, 1], 2)
+    assert [(b, p) for b, p, _, _ in out] == [(0, 3), (0, 4), (1, 0)]
+    b, p, c, kr = out[2]
+    assert np.allclose(c, w_dkv @ h[3], rtol=0, atol=1e-12) and np.allclose(kr, w_kr @ h[3], rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [check_cache_arithmetic, check_decode_tables, check_softmax,
               check_textbook_reduction, check_closed_forms, check_brute_force_exact,
               check_paging_invariance, check_causal_two_tokens, check_split_combine,
-              check_absorb_project_identities]
+              check_absorb_project_identities, check_append_projection, check_rope,
+              check_e4m3_encoding, check_fp8_row, check_append_positions]

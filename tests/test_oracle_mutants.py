@@ -139,7 +139,75 @@ def _project_drops_last_column(o_lat, w_uv):
     return np.stack([o_lat[:, h, :-1] @ w[h, :, :-1].T for h in range(o_lat.shape[1])], axis=1)
 
 
+def _down_project_drops_last(h, w):
+    return np.asarray(h, dtype=np.float64)[:, :-1] @ np.asarray(w, dtype=np.float64)[:, :-1].T
+
+
+def _rope_half_split(x, pos, theta=10000.0):
+    # pairs (j, j + 32) instead of (2j, 2j + 1)
+    x = np.asarray(x, dtype=np.float64)
+    a = _orig["rope_angles"](pos, theta, x.shape[-1])
+    h = x.shape[-1] // 2
+    out = np.empty_like(x)
+    out[..., :h] = x[..., :h] * np.cos(a) - x[..., h:] * np.sin(a)
+    out[..., h:] = x[..., :h] * np.sin(a) + x[..., h:] * np.cos(a)
+    return out
+
+
+def _rope_wrong_sign(x, pos, theta=10000.0):
+    return _orig["rope_rotate"](x, -pos, theta)
+
+
+def _rope_angles_full_width(pos, theta=10000.0, d=64):
+    j = np.arange(d // 2, dtype=np.float64)
+    return float(pos) * np.power(float(theta), -j / d)
+
+
+def _e4m3_ties_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = _orig["e4m3_values"]()
+    a = np.abs(x).reshape(-1)
+    d = np.abs(a[:, None] - vals[None, :])
+    pick = (d.shape[1] - 1 - np.argmin(d[:, ::-1], axis=1)).astype(np.uint8)   # the larger of two equally near
+    return np.where(np.signbit(x.reshape(-1)), pick | np.uint8(0x80), pick).reshape(x.shape)
+
+
+def _e4m3_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = _orig["e4m3_values"]()
+    a = np.abs(x).reshape(-1)
+    pick = (np.searchsorted(vals, a, side="right") - 1).astype(np.uint8)
+    return np.where(np.signbit(x.reshape(-1)), pick | np.uint8(0x80), pick).reshape(x.shape)
+
+
+def _quantize_scale_480(c):
+    c = np.asarray(c, dtype=np.float32)
+    amax = np.float32(np.abs(c).max())
+    s = np.float32(amax / np.float32(480.0)) if amax > 0 else np.float32(1.0)
+    q = np.clip(c / s, np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    return _orig["e4m3_round_codes"](q.astype(np.float64)), s
+
+
+def _appended_off_by_one(h, w_dkv, w_kr, seq_lens, q_per_seq, theta=10000.0):
+    out = []
+    for b, ln in enumerate(np.asarray(seq_lens)):
+        for i in range(q_per_seq):
+            p = int(ln) - q_per_seq + i + 1
+            if p < 0:
+                continue
+            r = b * q_per_seq + i
+            out.append((b, p, M.down_project(h[r:r + 1], w_dkv)[0],
+                        M.rope_rotate(M.down_project(h[r:r + 1], w_kr)[0], p, theta)))
+    return out
+
+
 MUTANTS = {
+    "down_project": [_down_project_drops_last],
+    "rope_rotate": [_rope_half_split, _rope_wrong_sign],
+    "rope_angles": [_rope_angles_full_width],
+    "e4m3_round_codes": [_e4m3_ties_up, _e4m3_truncate],
+    "quantize_latent": [_quantize_scale_480],
+    "appended_tokens": [_appended_off_by_one],
     "reconstruct_keys": [_keys_without_rope, _keys_transposed_weight],
     "reconstruct_values": [_values_skip_projection],
     "scores": [_scores_wrong_scale, _scores_sign],
