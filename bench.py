@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip timing the cache append")
+    ap.add_argument("--append-d-model", type=int, default=5120,
+                    help="hidden width of the tokens the cache append projects (not on the pages)")
     ap.add_argument("--warm", action="store_true", help="also time steps without cache eviction")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a HIP graph of the four calls (checked bit for bit "
@@ -167,7 +170,7 @@ def main():
         return
     import mla_inputs as MI
     from mla_latent_kv_17_amd import mla_decode
-    from mla_latent_kv_17_amd.runner import DecodeStep, DeviceInputs
+    from mla_latent_kv_17_amd.runner import CacheAppend, DecodeStep, DeviceInputs
 
     wl = MI.WORKLOADS[args.workload]
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
@@ -273,6 +276,32 @@ def main():
         torch.cuda.synchronize()
         graph_ms = np.array([a.elapsed_time(b) for a, b in gev])
 
+    # the cache append (the step before the decode path, not part of it):
+    # c = W_DKV h and the rotated position key of the B*S_q new tokens,
+    # written into their page rows; each launch timed alone after an eviction
+    append = None
+    if not args.no_append:
+        app = CacheAppend(dev, MI.generate_append(wl, d_model=args.append_d_model))
+        for _ in range(3):
+            app.run()
+        aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for e0, e1 in aev:
+            do_flush()
+            e0.record()
+            app.run()
+            e1.record()
+        torch.cuda.synchronize()
+        app_us = float(np.median([a.elapsed_time(b) for a, b in aev])) * 1e3
+        T = wl.batch * wl.q_per_seq
+        wbytes = 2 if wl.w_dtype == "bf16" else 4
+        app_bytes = (576 + T) * args.append_d_model * wbytes + T * per_tok
+        append = {"kernels": "append_proj_mfma + append_finish" if wl.w_dtype == "bf16"
+                  else "append_proj_f32 + append_finish", "tokens": T, "d_model": args.append_d_model,
+                  "us": app_us, "algorithmic_bytes": app_bytes,
+                  "achieved_gbps": app_bytes / (app_us * 1e-6) / 1e9,
+                  "frac_hbm": app_bytes / (app_us * 1e-6) / HBM_PEAK,
+                  "timing": "median of 20 launches, each after an eviction read, HIP events around the two launches"}
+
     eager_ms_per_step = float(step_ms.mean())
     ms_per_step = eager_ms_per_step
     traffic = measured_traffic(wl.name)
@@ -324,6 +353,7 @@ def main():
         "step_tflops": (decode_flops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
         "warm_ms_per_step": warm_ms,
         "wall_s_timed_loop_incl_eviction": wall,
+        "cache_append": append,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -53,8 +53,8 @@ extern "C" {
 #endif
 
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
- * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv */
-#define MLA_ABI_VERSION 4
+ * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append */
+#define MLA_ABI_VERSION 5
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -189,6 +189,40 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
 int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
                        const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, float* lse,
                        void* stream);
+
+/* Cache append: the step that writes the S_q newest tokens of each sequence
+ * into the paged cache before mla_decode reads them (same page, section 1,
+ * "Store a latent, rebuild the keys and values": the down-projection
+ * c_t = W_DKV h_t is where compression happens, and a separate 64-wide key
+ * carries the position, because RoPE cannot pass through the absorbed
+ * projections).  For token i of sequence b at position p = len_b - S_q + i
+ * (skipped if p < 0), with h its hidden state:
+ *   c_t    = W_DKV h                                   (512 values)
+ *   k^R_t  = RoPE_p(W_KR h): pairs (2j, 2j+1) rotated by the angle
+ *            p * rope_theta^(-2j/64), j = 0..31        (64 values)
+ * and the token's cache row (kv's page table at position p) receives them:
+ *   F32 cache:  c and k^R as fp32;
+ *   BF16 cache: each rounded to nearest-even bf16;
+ *   FP8 cache:  scale = amax_j |c_j| / 448 (fp32; 1 if c is all zero), codes
+ *               = E4M3 of c_j / scale (fp32 division, nearest-even, clamped
+ *               to +-448), k^R as bf16.
+ * No other cache row is touched.
+ * h:     [batch*q_per_seq][d_model], in_dtype (BF16 with a BF16 or FP8 cache,
+ *        F32 with an F32 cache)
+ * w_dkv: [d_latent][d_model], w_kr: [d_rope][d_model], in_dtype
+ * kv:    the cache, written through its latent / rope / scale pointers
+ *        (seq_lens: lengths including the new tokens)
+ * d_model: a multiple of 64, 64 .. 65536
+ * workspace: device memory of at least mla_cache_append_workspace_size() bytes
+ *        (16-byte aligned; fp32 partial sums, contents on return unspecified)
+ * Products are exact, sums fp32 over d_model; the rotation is computed in
+ * fp64 from the fp32 sums. */
+int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                     int32_t in_dtype, float rope_theta, const mla_paged_kv* kv, void* workspace,
+                     int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_cache_append needs for these sizes (host-only). */
+int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64_t* bytes);
 
 /* A launch-shape helper: the num_splits mla_decode should use so that the
  * device's compute units are filled, given the longest sequence length the

@@ -26,7 +26,8 @@ D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 
 # the C entry points this binding exposes (also checked by the tests)
 EXPORTS = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_decode",
-           "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits"]
+           "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits",
+           "mla_cache_append", "mla_cache_append_workspace_size"]
 
 
 class MlaDims(ctypes.Structure):
@@ -84,6 +85,8 @@ def _load():
         "mla_out_uv": ([dp, f32p, vp, i32, vp, i32, vp], ctypes.c_int),
         "mla_combine_out_uv": ([dp, i32, f32p, f32p, vp, i32, vp, i32, f32p, vp], ctypes.c_int),
         "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+        "mla_cache_append": ([dp, i32, vp, vp, vp, i32, ctypes.c_float, kvp, vp, ctypes.c_int64, vp], ctypes.c_int),
+        "mla_cache_append_workspace_size": ([dp, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -194,3 +197,22 @@ def mla_decode_num_splits(dims: MlaDims, max_seq_len: int) -> int:
     _check("mla_decode_num_splits", _lib.mla_decode_num_splits(ctypes.byref(dims), int(max_seq_len),
                                                                ctypes.byref(out)))
     return int(out.value)
+
+
+def mla_cache_append_workspace_size(dims: MlaDims, d_model: int) -> int:
+    """Bytes of workspace mla_cache_append needs."""
+    out = ctypes.c_int64(0)
+    _check("mla_cache_append_workspace_size",
+           _lib.mla_cache_append_workspace_size(ctypes.byref(dims), int(d_model), ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_cache_append(dims: MlaDims, d_model: int, h, w_dkv, w_kr, cache: PagedCache, workspace,
+                     rope_theta: float = 10000.0, stream=None):
+    """Write c = W_DKV h and k^R = RoPE_p(W_KR h) of the S_q newest tokens of each
+    sequence (position p = len - S_q + i) into the paged cache."""
+    _check("mla_cache_append", _lib.mla_cache_append(ctypes.byref(dims), int(d_model), _ptr(h), _ptr(w_dkv),
+                                                     _ptr(w_kr), _dtype_code(h), float(rope_theta),
+                                                     ctypes.byref(cache.kv), _ptr(workspace),
+                                                     int(workspace.numel() * workspace.element_size()),
+                                                     _stream(stream)))

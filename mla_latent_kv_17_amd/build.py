@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["api.hip", "decode.hip", "absorb.hip", "combine.hip", "out_uv.hip"]
+SOURCES = ["api.hip", "decode.hip", "absorb.hip", "combine.hip", "out_uv.hip", "append.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -271,6 +271,93 @@ int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_
   return st;
 }
 
+namespace {
+
+int append_chunks(int32_t d_model) { return (d_model + mla::kAppendChunk - 1) / mla::kAppendChunk; }
+
+}  // namespace
+
+int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bytes) return MLA_ERR_NULL;
+  if (d_model < 64 || d_model > 65536 || d_model % 64) return MLA_ERR_SHAPE;
+  *bytes = (int64_t)append_chunks(d_model) * dims->batch * dims->q_per_seq * mla::kAppendCols * 4;
+  return MLA_OK;
+}
+
+int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                     int32_t in_dtype, float rope_theta, const mla_paged_kv* kv, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!kv || !h || !w_dkv || !w_kr || !workspace) return MLA_ERR_NULL;
+  if (!kv->latent || !kv->rope || !kv->block_table || !kv->seq_lens) return MLA_ERR_NULL;
+  if (d_model < 64 || d_model > 65536 || d_model % 64) return MLA_ERR_SHAPE;
+  if (!(rope_theta > 0.f) || !isfinite(rope_theta)) return MLA_ERR_SHAPE;
+  if (kv->block_size != kBlock || kv->num_blocks < 1 || kv->max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  const int32_t ld = kv->latent_dtype, rd = kv->rope_dtype;
+  int fmt;  // 0 = f32, 1 = bf16, 2 = fp8
+  if (in_dtype == MLA_F32 && ld == MLA_F32 && rd == MLA_F32) fmt = 0;
+  else if (in_dtype == MLA_BF16 && ld == MLA_BF16 && rd == MLA_BF16) fmt = 1;
+  else if (in_dtype == MLA_BF16 && ld == MLA_FP8_E4M3 && rd == MLA_BF16) fmt = 2;
+  else return MLA_ERR_DTYPE;
+  if (fmt == 2 && !kv->scale) return MLA_ERR_NULL;
+  if (fmt != 2 && kv->scale) return MLA_ERR_DTYPE;
+  if (kv->latent_row_stride < kDL || kv->rope_row_stride < kDR || kv->latent_block_stride < 0 ||
+      kv->rope_block_stride < 0 || (fmt == 2 && kv->scale_block_stride < kBlock))
+    return MLA_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(workspace)) return MLA_ERR_ALIGN;
+  const int tokens = dims->batch * dims->q_per_seq;
+  if (tokens == 0) return MLA_OK;
+  const int chunks = fmt == 0 ? 1 : append_chunks(d_model);
+  if (workspace_bytes < (int64_t)chunks * tokens * mla::kAppendCols * 4) return MLA_ERR_SHAPE;
+  if (check_mode()) {
+    st = check_paging(dims->batch, kv, (hipStream_t)stream);
+    if (st) return st;
+  }
+  const int64_t les = elem_size(ld), res = elem_size(rd);
+  mla::AppendArgs a;
+  a.h = h;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.part = (float*)workspace;
+  a.latent = (uint8_t*)kv->latent;
+  a.rope = (uint8_t*)kv->rope;
+  a.scale = (float*)kv->scale;
+  a.lat_bs = kv->latent_block_stride * les;
+  a.lat_rs = kv->latent_row_stride * les;
+  a.rope_bs = kv->rope_block_stride * res;
+  a.rope_rs = kv->rope_row_stride * res;
+  a.scale_bs = kv->scale_block_stride;
+  a.block_table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.tokens = tokens;
+  a.sq = dims->q_per_seq;
+  a.d_model = d_model;
+  a.chunks = chunks;
+  a.max_blocks = kv->max_blocks_per_seq;
+  a.log2_theta = log2((double)rope_theta);
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == 0) {
+    if (tokens > 65535) return MLA_ERR_SHAPE;
+    st = launch("mla::append_proj_f32", (const void*)mla::append_proj_f32, dim3(mla::kAppendCols / 4, tokens),
+                dim3(256), a, s);
+  } else {
+    const dim3 grid(mla::kAppendCols / 64, chunks, (tokens + 31) / 32);
+    if (grid.z > 65535) return MLA_ERR_SHAPE;
+    st = launch("mla::append_proj_mfma", (const void*)mla::append_proj_mfma, grid, dim3(256), a, s);
+  }
+  if (st) return st;
+  if (fmt == 0)
+    st = launch("mla::append_finish<f32>", (const void*)mla::append_finish<0>, dim3(tokens), dim3(256), a, s);
+  else if (fmt == 1)
+    st = launch("mla::append_finish<bf16>", (const void*)mla::append_finish<1>, dim3(tokens), dim3(256), a, s);
+  else
+    st = launch("mla::append_finish<fp8>", (const void*)mla::append_finish<2>, dim3(tokens), dim3(256), a, s);
+  return st;
+}
+
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits) {
   int st = check_dims(dims);
   if (st) return st;

@@ -1,0 +1,210 @@
+// Cache append: the S_q newest tokens of each sequence enter the paged cache.
+//
+// deepforge.srivtx.xyz "DeepSeek-V2", section 1, "Store a latent, rebuild the
+// keys and values" and its formula box: the cache holds, per token per layer,
+// the down-projected latent c_t = W_DKV h_t (512 wide) and one 64-wide key
+// that carries the position (RoPE cannot pass through the absorbed
+// projections, so it is kept apart from the latent).  Here that key is
+// k^R_t = RoPE_p(W_KR h_t) at the token's position p: pairs (2j, 2j+1) turned
+// by the angle p * theta^(-2j/64).
+//
+// Two launches:
+//  * append_proj_mfma (bf16 inputs): X = h W^T with W = [W_DKV; W_KR]
+//    (576 x d_model), a [tokens x 576] product over K = d_model on the matrix
+//    cores (v_mfma_f32_32x32x16_bf16, exact products, fp32 sums).
+//    Workgroup = (64 output columns, 512-wide chunk of d_model, 32 tokens):
+//    it stages its W and h row slices in LDS with fully coalesced loads (a
+//    wave's load is 1 KB of one row; the operands' own lane layout would
+//    touch 32 rows per load), each wave multiplies a quarter of the chunk,
+//    and the four partial tiles sum through LDS into the chunk's fp32
+//    partial sums in the caller's workspace.  The weights are the traffic
+//    (576 x d_model x 2 bytes) and are read once; the small h is read once
+//    per column tile.
+//  * append_finish (one workgroup per token): the chunk sums, the rotation
+//    (angles and sin/cos in fp64, so large positions keep their precision),
+//    then the cache encoding and the write into the token's page row.
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+
+__global__ void __launch_bounds__(256) append_proj_mfma(const AppendArgs a) {
+  constexpr int kPad = 33;          // LDS row stride (floats) of the partial tiles
+  constexpr int kRow = 1024 + 16;   // LDS row stride (bytes) of the staged operands
+  __shared__ __attribute__((aligned(16))) uint8_t ws[64 * kRow];  // W rows n0 .. n0+63, this chunk
+  __shared__ __attribute__((aligned(16))) uint8_t hs[32 * kRow];  // h rows m0 .. m0+31, this chunk
+  __shared__ float red[4][2][32 * kPad];
+  const int n0 = blockIdx.x * 64, chunk = blockIdx.y, m0 = blockIdx.z * 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, n32 = lane & 31;
+  const int k_lo = chunk * kAppendChunk;
+  const int klen = min(kAppendChunk, a.d_model - k_lo);  // a multiple of 64
+  // ---- staging: a wave's load is 1 KB of one row (64 lanes x 16 bytes);
+  // bytes past the chunk's end (a short last chunk) and rows past the last
+  // token stage zeros.  Every load is issued before the first store.
+  const int cb = lane * 16;  // byte of the row slice this lane moves
+  const bool in_k = cb < 2 * klen;
+  u32x4 wv[16], hv[8];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int n = n0 + 4 * i + wave;
+    const uint16_t* row = n < 512 ? (const uint16_t*)a.w_dkv + (int64_t)n * a.d_model
+                                  : (const uint16_t*)a.w_kr + (int64_t)(n - 512) * a.d_model;
+    wv[i] = *(const u32x4*)((const uint8_t*)(row + k_lo) + (in_k ? cb : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = m0 + 4 * i + wave;
+    hv[i] = *(const u32x4*)((const uint8_t*)((const uint16_t*)a.h + (int64_t)(r < a.tokens ? r : 0) * a.d_model + k_lo) +
+                            (in_k ? cb : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    *(MLA_LDS u32x4*)((MLA_LDS uint8_t*)ws + (4 * i + wave) * kRow + cb) = in_k ? wv[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool live = in_k && m0 + 4 * i + wave < a.tokens;
+    *(MLA_LDS u32x4*)((MLA_LDS uint8_t*)hs + (4 * i + wave) * kRow + cb) = live ? hv[i] : u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+  // ---- products: wave w takes k-steps 8w .. 8w+7 of the chunk (16 k each):
+  // A = h rows (token n32, k + 8g .. +7), B = W rows (column 32 nt + n32, same k)
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int kb = (16 * (8 * wave + j) + 8 * g) * 2;
+    const bf16x8 av = *(const MLA_LDS bf16x8*)((const MLA_LDS uint8_t*)hs + n32 * kRow + kb);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bf16x8 bv = *(const MLA_LDS bf16x8*)((const MLA_LDS uint8_t*)ws + (32 * nt + n32) * kRow + kb);
+      acc[nt] = mfma32x32x16(av, bv, acc[nt]);
+    }
+  }
+  // D lane l, register i: token (i/4)*8 + 4g + i%4 of the tile, column n32 of the 32-column block
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wave][nt][((i >> 2) * 8 + 4 * g + (i & 3)) * kPad + n32] = acc[nt][i];
+  __syncthreads();
+  float* part = a.part + (int64_t)chunk * a.tokens * kAppendCols;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = i * 256 + tid;
+    const int row = idx >> 6, d = idx & 63, nt = d >> 5, n = d & 31;
+    const float v = red[0][nt][row * kPad + n] + red[1][nt][row * kPad + n] + red[2][nt][row * kPad + n] +
+                    red[3][nt][row * kPad + n];
+    if (m0 + row < a.tokens) part[(int64_t)(m0 + row) * kAppendCols + n0 + d] = v;
+  }
+}
+
+// fp32 inputs: wave w of workgroup x computes column 4x + w of one token
+// (grid y): its 64 lanes stride along d_model, then a shuffle sum.
+__global__ void __launch_bounds__(256) append_proj_f32(const AppendArgs a) {
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), r = blockIdx.y, lane = threadIdx.x & 63;
+  const float* h = (const float*)a.h + (int64_t)r * a.d_model;
+  const float* w = n < 512 ? (const float*)a.w_dkv + (int64_t)n * a.d_model
+                           : (const float*)a.w_kr + (int64_t)(n - 512) * a.d_model;
+  float acc = 0.f;
+  for (int k = lane; k < a.d_model; k += 64) acc = fmaf(h[k], w[k], acc);
+  acc = wave_sum(acc);
+  if (lane == 0) a.part[(int64_t)r * kAppendCols + n] = acc;
+}
+
+namespace {
+
+// OCP E4M3FN code of a finite float with |x| <= 448, nearest with ties to
+// even, from the format's definition: at or above 2^-6 the float's exponent
+// and top three mantissa bits rounded as one field (a carry moves into the
+// exponent) and re-biased from 127 to 7; below 2^-6 the nearest-even count
+// of 2^-9.  The sign goes to bit 7.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  uint32_t code;
+  if (ax >= 0.015625f) {
+    const uint32_t b = __float_as_uint(ax);
+    code = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)rintf(ax * 512.0f);
+  }
+  return sign | code;
+}
+
+}  // namespace
+
+template <int kFmt>
+__global__ void __launch_bounds__(256) append_finish(const AppendArgs a) {
+  __shared__ float x[kAppendCols];
+  __shared__ float wmax[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  // the token's position and page row (read first: their latency overlaps
+  // the chunk sums; a token without a position reads entry 0 and leaves)
+  const int b = r / a.sq, i = r - b * a.sq;
+  const int p = a.seq_lens[b] - a.sq + i;
+  const int64_t blk = a.block_table[(int64_t)b * a.max_blocks + (max(p, 0) >> 6)];
+  const int row = p & 63;
+  // the chunk sums (they do not depend on the token's position), chunk
+  // order fixed, the loads of eight chunks for all of a thread's columns in
+  // flight at a time with no branch between them
+  const int64_t cstride = (int64_t)a.tokens * kAppendCols;
+  const float* pp = a.part + (int64_t)r * kAppendCols;
+  float sum[3] = {0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.chunks; c0 += 8) {
+    float v[3][8];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int n = min(tid + 256 * u, kAppendCols - 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[u][k] = pp[min(c0 + k, a.chunks - 1) * cstride + n];
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum[u] += c0 + k < a.chunks ? v[u][k] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+    if (tid + 256 * u < kAppendCols) x[tid + 256 * u] = sum[u];
+  if (p < 0) return;  // uniform: the whole workgroup leaves before any barrier
+  __syncthreads();
+  if (tid < 32) {
+    // pair j = tid of the RoPE key: angle p * theta^(-2j/64)
+    const double ang = (double)p * exp2(-(double)(2 * tid) / 64.0 * a.log2_theta);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const double x0 = x[512 + 2 * tid], x1 = x[512 + 2 * tid + 1];
+    x[512 + 2 * tid] = (float)(x0 * cs - x1 * sn);
+    x[512 + 2 * tid + 1] = (float)(x0 * sn + x1 * cs);
+  }
+  __syncthreads();
+  uint8_t* lrow = a.latent + blk * a.lat_bs + (int64_t)row * a.lat_rs;
+  uint8_t* rrow = a.rope + blk * a.rope_bs + (int64_t)row * a.rope_rs;
+  if (kFmt == 0) {
+    for (int n = tid; n < 512; n += 256) ((float*)lrow)[n] = x[n];
+    if (tid < 64) ((float*)rrow)[tid] = x[512 + tid];
+  } else if (kFmt == 1) {
+    for (int n = tid; n < 512; n += 256) ((uint16_t*)lrow)[n] = f32_to_bf16_bits(x[n]);
+    if (tid < 64) ((uint16_t*)rrow)[tid] = f32_to_bf16_bits(x[512 + tid]);
+  } else {
+    // per-token scale amax / 448 (1 for an all-zero latent), codes of c / scale
+    float m = fmaxf(fabsf(x[tid]), fabsf(x[tid + 256]));
+    m = wave_max(m);
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    for (int n = tid; n < 512; n += 256) {
+      const float q = fminf(fmaxf(x[n] / sc, -448.0f), 448.0f);
+      lrow[n] = (uint8_t)e4m3_code(q);
+    }
+    if (tid == 0) a.scale[blk * a.scale_bs + row] = sc;
+    if (tid < 64) ((uint16_t*)rrow)[tid] = f32_to_bf16_bits(x[512 + tid]);
+  }
+}
+
+template __global__ void append_finish<0>(const AppendArgs);
+template __global__ void append_finish<1>(const AppendArgs);
+template __global__ void append_finish<2>(const AppendArgs);
+
+}  // namespace mla

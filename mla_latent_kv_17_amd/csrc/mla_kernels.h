@@ -64,4 +64,29 @@ __global__ void merge_out_uv_mfma(const OutUvArgs a);  // the same with the chun
 template <bool kMerge>
 __global__ void out_uv_f32(const OutUvArgs a);   // fp32 weights
 
+// Cache append (c_t = W_DKV h_t, k^R_t = RoPE_p(W_KR h_t), written to the
+// paged cache).  Projections in two steps: fp32 partial sums over 512-wide
+// chunks of d_model into the caller's workspace, then per token the chunk
+// sums, the rotation, the encoding and the paged write.
+constexpr int kAppendChunk = 512;
+constexpr int kAppendCols = 576;  // W_DKV rows, then W_KR rows
+struct AppendArgs {
+  const void* h;      // [tokens][d_model]
+  const void* w_dkv;  // [512][d_model]
+  const void* w_kr;   // [64][d_model]
+  float* part;        // [chunks][tokens][576]
+  uint8_t* latent;    // cache latent rows (byte strides below)
+  uint8_t* rope;      // cache RoPE-key rows
+  float* scale;       // fp8: per-token scales
+  int64_t lat_bs, lat_rs, rope_bs, rope_rs, scale_bs;  // bytes; scale_bs in floats
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int tokens, sq, d_model, chunks, max_blocks;
+  double log2_theta;  // log2(rope_theta)
+};
+__global__ void append_proj_mfma(const AppendArgs a);  // bf16 inputs
+__global__ void append_proj_f32(const AppendArgs a);   // fp32 inputs
+template <int kFmt>  // 0 fp32, 1 bf16, 2 fp8 cache
+__global__ void append_finish(const AppendArgs a);
+
 }  // namespace mla

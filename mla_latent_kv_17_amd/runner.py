@@ -16,8 +16,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PagedCache, make_dims, mla_absorb_q, mla_combine_out_uv, mla_decode, mla_decode_num_splits,
-               mla_out_uv, mla_split_combine)
+from . import (PagedCache, make_dims, mla_absorb_q, mla_cache_append, mla_cache_append_workspace_size,
+               mla_combine_out_uv, mla_decode, mla_decode_num_splits, mla_out_uv, mla_split_combine)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -143,3 +143,25 @@ class DecodeStep:
         self.combine(stream)
         self.project(stream)
         return self.out
+
+
+class CacheAppend:
+    """Device copies of the append inputs (h, W_DKV, W_KR) and the append's
+    workspace; run() writes the S_q new tokens of every sequence into the
+    device cache of `dev` (mla_cache_append)."""
+
+    def __init__(self, dev: DeviceInputs, app):
+        self.dev = dev
+        self.d_model, self.rope_theta = app.d_model, app.rope_theta
+        device = dev.q_nope.device
+        kind = dev.wl.w_dtype
+        self.h = _dev(app.h, kind, device)
+        self.w_dkv = _dev(app.w_dkv, kind, device)
+        self.w_kr = _dev(app.w_kr, kind, device)
+        n = mla_cache_append_workspace_size(dev.dims, app.d_model)
+        self.workspace = torch.empty(max(n // 4, 4), dtype=torch.float32, device=device)
+
+    def run(self, stream=None):
+        mla_cache_append(self.dev.dims, self.d_model, self.h, self.w_dkv, self.w_kr, self.dev.cache,
+                         self.workspace, self.rope_theta, stream)
+

@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 8, syms
+    assert len(syms) == 10, syms
     lib = ctypes.CDLL(M.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 4
+    assert M.abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -89,3 +89,32 @@ def test_other_entry_points_validation():
     out = ctypes.c_int32(0)
     assert L.mla_decode_num_splits(ctypes.byref(d), 100, None) == M.MLA_ERR_NULL
     assert L.mla_decode_num_splits(ctypes.byref(d), -1, ctypes.byref(out)) == M.MLA_ERR_SHAPE
+
+
+def test_cache_append_validation():
+    d = M.make_dims(2, 1, 128)
+    L = M._lib
+    n = ctypes.c_int64(0)
+    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 5120, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 10 * 2 * 576 * 4
+    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 100, ctypes.byref(n)) == M.MLA_ERR_SHAPE
+    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 5120, None) == M.MLA_ERR_NULL
+
+    def call(d_model=640, h=0x1000, dt=M.MLA_BF16, theta=10000.0, kv=None, ws=0x9000, wsb=1 << 20):
+        kv = kv if kv is not None else _kv()
+        return L.mla_cache_append(ctypes.byref(d), d_model, h, 0x2000, 0x3000, dt, theta, ctypes.byref(kv), ws,
+                                  wsb, None)
+    assert call(h=0) == M.MLA_ERR_NULL
+    assert call(ws=0) == M.MLA_ERR_NULL
+    assert call(d_model=96) == M.MLA_ERR_SHAPE
+    assert call(d_model=65536 + 64) == M.MLA_ERR_SHAPE
+    assert call(theta=0.0) == M.MLA_ERR_SHAPE
+    assert call(theta=float("inf")) == M.MLA_ERR_SHAPE
+    assert call(dt=M.MLA_F32) == M.MLA_ERR_DTYPE                      # fp32 inputs need an fp32 cache
+    assert call(kv=_kv(ldt=M.MLA_FP8_E4M3)) == M.MLA_ERR_NULL          # fp8 needs a scale
+    assert call(h=0x1008) == M.MLA_ERR_ALIGN
+    assert call(wsb=2 * 2 * 576 * 4 - 4) == M.MLA_ERR_SHAPE             # 640 wide: two chunks
+    assert call(kv=_kv(bs=32)) == M.MLA_ERR_SHAPE
+    assert L.mla_cache_append(ctypes.byref(M.make_dims(0, 1, 128)), 640, 0x1000, 0x2000, 0x3000, M.MLA_BF16,
+                              10000.0, ctypes.byref(_kv()), 0x9000, 0, None) == M.MLA_OK  # nothing to do
+
