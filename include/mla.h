@@ -40,7 +40,8 @@
  *    a block id among a sequence's first ceil(len / block_size) entries is
  *    outside [0, num_blocks); MLA_ERR_DEVICE if the copy fails.
  *  - Supported sizes: d_latent = 512, d_rope = 64, d_head = 128,
- *    block_size = 64, 1 <= q_per_seq <= 2; anything else is MLA_ERR_SHAPE.
+ *    block_size = 64, 1 <= q_per_seq <= MLA_MAX_Q_PER_SEQ; anything else is
+ *    MLA_ERR_SHAPE.
  *  - Thread-safe: the library holds no mutable global state.
  */
 #ifndef MLA_H_
@@ -53,8 +54,9 @@ extern "C" {
 #endif
 
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
- * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append */
-#define MLA_ABI_VERSION 5
+ * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append;
+ * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2) */
+#define MLA_ABI_VERSION 6
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -74,11 +76,18 @@ typedef enum mla_status {
 } mla_status;
 
 #define MLA_MAX_SPLITS 1024
+/* Query tokens per sequence in one call (multi-token decode: speculative
+ * tokens, short prefill chunks).  The absorbed form costs 2 (576 + 512)
+ * flops per (query, token, head) against 2 (128 x 512) x 2 per (token, head)
+ * plus 2 (192 + 128) per (query, token, head) for rebuilding K and V
+ * explicitly: the absorbed form is the cheaper one below about 171 query
+ * tokens per sequence, so it is the only form here. */
+#define MLA_MAX_Q_PER_SEQ 128
 
 /* Static description of one decode batch. */
 typedef struct mla_dims {
   int32_t batch;       /* B: sequences                                       */
-  int32_t q_per_seq;   /* S_q: query tokens per sequence (1 or 2)            */
+  int32_t q_per_seq;   /* S_q: query tokens per sequence (1..128)            */
   int32_t heads;       /* H: attention heads (1..1024)                       */
   int32_t d_latent;    /* 512                                                */
   int32_t d_rope;      /* 64                                                 */

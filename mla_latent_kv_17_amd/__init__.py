@@ -22,6 +22,7 @@ MLA_OK = 0
 MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_ALIGN = -1, -2, -3, -4
 MLA_ERR_SPLITS, MLA_ERR_LAUNCH, MLA_ERR_DEVICE = -5, -6, -7
 MLA_MAX_SPLITS = 1024
+MLA_MAX_Q_PER_SEQ = 128
 D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 
 # the C entry points this binding exposes (also checked by the tests)

@@ -57,7 +57,7 @@ int check_paging(int32_t batch, const mla_paged_kv* kv, hipStream_t s) {
 
 int check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_NULL;
-  if (d->batch < 0 || d->heads < 1 || d->heads > 1024 || d->q_per_seq < 1 || d->q_per_seq > 2)
+  if (d->batch < 0 || d->heads < 1 || d->heads > 1024 || d->q_per_seq < 1 || d->q_per_seq > MLA_MAX_Q_PER_SEQ)
     return MLA_ERR_SHAPE;
   if (d->d_latent != kDL || d->d_rope != kDR || d->d_head != kDH) return MLA_ERR_SHAPE;
   if (!isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;

@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 5
+    assert M.abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -56,7 +56,9 @@ def test_decode_validation():
     assert _call_decode(d, _kv(scale=0x50000)) == M.MLA_ERR_DTYPE               # scale only with fp8
     assert _call_decode(d, _kv(latent=0x10008)) == M.MLA_ERR_ALIGN
     assert _call_decode(d, _kv(), q=0x1004) == M.MLA_ERR_ALIGN
-    bad = M.make_dims(2, 3, 128)
+    bad = M.make_dims(2, 129, 128)
+    assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
+    bad = M.make_dims(2, 0, 128)
     assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
     bad = M.MlaDims(2, 1, 128, 256, 64, 128, 0.1)
     assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE

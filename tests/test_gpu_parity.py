@@ -63,3 +63,30 @@ def test_deterministic():
     b = run_gpu(inp)
     for x, y in zip(a[:3], b[:3]):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+# multi-token decode: S_q query tokens per sequence, each seeing the cache up
+# to its own position (query i sees len - (S_q - 1 - i) tokens; the first
+# queries of a sequence shorter than S_q see none)
+MULTI = {
+    "bf16_sq5": MI.small_variants()["bf16_small_paged"].scaled(name="bf16_sq5", q_per_seq=5, seed=2201),
+    "bf16_sq16_split": MI.small_variants()["bf16_small_split"].scaled(name="bf16_sq16_split", q_per_seq=16,
+                                                                      heads=16, seed=2202),
+    "fp8_sq7": MI.small_variants()["fp8_small_sq2"].scaled(name="fp8_sq7", q_per_seq=7, lens=(3, 70, 200),
+                                                           len_range=None, seed=2203),
+    "fp32_sq3": MI.small_variants()["fp32_b1_h16_t1k"].scaled(name="fp32_sq3", q_per_seq=3, seq_len=130,
+                                                              seed=2204),
+}
+
+
+@pytest.mark.parametrize("name", list(MULTI))
+def test_multi_token_vs_oracle(name):
+    wl = MULTI[name]
+    inp = MI.generate(wl)
+    out, o_lat, lse, _ = run_gpu(inp)
+    o_ref, lse_ref = O.explicit_decode(inp)
+    check(f"{name}/o", out, o_ref, wl.cache_dtype)
+    none = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), none)
+    assert np.max(np.abs(lse[~none] - lse_ref[~none])) < 1e-2
+    assert (out[none] == 0).all()
