@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip timing the cache append")
+    ap.add_argument("--q-per-seq", type=int, default=0,
+                    help="query tokens per sequence instead of the workload's (multi-token decode)")
     ap.add_argument("--append-d-model", type=int, default=5120,
                     help="hidden width of the tokens the cache append projects (not on the pages)")
     ap.add_argument("--warm", action="store_true", help="also time steps without cache eviction")
@@ -173,6 +175,8 @@ def main():
     from mla_latent_kv_17_amd.runner import CacheAppend, DecodeStep, DeviceInputs
 
     wl = MI.WORKLOADS[args.workload]
+    if args.q_per_seq:  # multi-token decode on the workload's cache (context figure, not a configuration)
+        wl = wl.scaled(name=f"{wl.name}_sq{args.q_per_seq}", q_per_seq=args.q_per_seq)
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
     inp = MI.generate(wl)
     dev = DeviceInputs(inp)
