@@ -47,6 +47,44 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def measured_peaks(torch, device="cuda"):
+    """What this part reaches in practice, from the probes in libmla_peaks.so:
+    a streaming read of 2 GiB (beyond the 256 MB Infinity Cache) and
+    independent bf16 32x32x16 matrix products on every CU.  Best of five
+    runs each, HIP events."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mla_latent_kv_17_amd", "libmla_peaks.so"))
+    lib.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.mla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    blocks = 4096
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=device)
+
+    def best(fn, reps=5):
+        fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times)
+
+    t_read = best(lambda: lib.mla_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream))
+    iters = 4096
+    mfma_blocks = 2048
+    t_mfma = best(lambda: lib.mla_probe_mfma(sink.data_ptr(), mfma_blocks, iters, stream))
+    flops = mfma_blocks * 4 * iters * 8 * 2 * 32 * 32 * 16
+    del buf, sink
+    return {"hbm_read_gbps": nbytes / t_read / 1e9, "mfma_bf16_tflops": flops / t_mfma / 1e12,
+            "probes": "2 GiB streaming read, 4096 blocks each reading its own contiguous share; "
+                      "8 independent bf16 32x32x16 products per wave, 2048 x 4 waves"}
+
+
 def measured_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs,
     or None for another workload than theirs, or when the decode kernel
@@ -140,6 +178,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip timing the cache append")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--q-per-seq", type=int, default=0,
                     help="query tokens per sequence instead of the workload's (multi-token decode)")
     ap.add_argument("--append-d-model", type=int, default=5120,
@@ -306,6 +345,8 @@ def main():
                   "frac_hbm": app_bytes / (app_us * 1e-6) / HBM_PEAK,
                   "timing": "median of 20 launches, each after an eviction read, HIP events around the two launches"}
 
+    peaks = None if args.no_peaks else measured_peaks(torch)
+
     eager_ms_per_step = float(step_ms.mean())
     ms_per_step = eager_ms_per_step
     traffic = measured_traffic(wl.name)
@@ -320,6 +361,12 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": cache_bytes / (dec_avg * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": cache_bytes / (dec_avg * 1e-3) / HBM_PEAK}
+    # the same rate against what the probes reach on this part
+    frac_measured = None
+    if peaks is not None and roof["bound"] == "hbm":
+        frac_measured = roof["achieved"] / peaks["hbm_read_gbps"]
+    elif peaks is not None and roof["bound"] == "mfma":
+        frac_measured = roof["achieved"] / peaks["mfma_bf16_tflops"]
     out = {
         "metric": METRIC,
         "value": kv_tokens / (ms_per_step * 1e-3),
@@ -338,7 +385,7 @@ def main():
                    "block_size": 64, "cache_dtype": wl.cache_dtype, "num_splits": step.num_splits,
                    "steps_timed": "absorb_q + decode + the split merge fused into out_uv (combine_out_uv; split_combine "
                                   "+ out_uv above 8 chunks, out_uv alone for one chunk), caches evicted before each"},
-        "roofline": {**roof, "traffic": traffic,
+        "roofline": {**roof, "frac_of_measured": frac_measured, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                                      "calibrated on a 256 MiB copy)",
                      "kernel": DECODE_KERNEL[wl.cache_dtype], "launch_ms": dec_avg,
@@ -358,6 +405,7 @@ def main():
         "warm_ms_per_step": warm_ms,
         "wall_s_timed_loop_incl_eviction": wall,
         "cache_append": append,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
