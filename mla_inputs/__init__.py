@@ -363,6 +363,37 @@ def generate_append(wl: Workload, d_model: int = APPEND_D_MODEL, seed: Optional[
                         w_kr=_encode(w_kr, wl.w_dtype), rope_theta=10000.0)
 
 
+GATE_EXPERTS, GATE_TOP_K = 160, 6
+
+
+@dataclasses.dataclass
+class GateInputs:
+    u: np.ndarray   # [tokens][d_model]     hidden states entering the MoE layer
+    e: np.ndarray   # [n_experts][d_model]  routed experts' centroids
+    top_k: int
+
+
+def generate_gate(tokens: int, d_model: int = APPEND_D_MODEL, n_experts: int = GATE_EXPERTS,
+                  top_k: int = GATE_TOP_K, dtype: str = "bf16", seed: int = 0, one_hot: bool = False,
+                  twins: bool = False) -> GateInputs:
+    """Draws u ~ N(0, 1) and the centroids ~ N(0, std 1/sqrt(d_model)), so the
+    affinities u^T e_i come out near unit variance; encoded as `dtype` (bf16
+    or f32).  Draw order: u, e, from seed + 700.  With `one_hot`, row t of u
+    is the unit vector e_((7t + 3) mod d_model): each affinity is then one
+    centroid entry, exact in every precision.  With `twins`, centroid 2j+1
+    is a copy of centroid 2j, so every affinity has an equal partner and
+    every selection meets ties."""
+    rng = np.random.default_rng(seed + 700)
+    u = rng.standard_normal((tokens, d_model), dtype=np.float32)
+    e = rng.standard_normal((n_experts, d_model), dtype=np.float32) * np.float32(1.0 / math.sqrt(d_model))
+    if one_hot:
+        u = np.zeros((tokens, d_model), dtype=np.float32)
+        u[np.arange(tokens), (7 * np.arange(tokens) + 3) % d_model] = 1.0
+    if twins:
+        e[1::2] = e[0:n_experts - n_experts % 2:2]
+    return GateInputs(u=_encode(u, dtype), e=_encode(e, dtype), top_k=top_k)
+
+
 def depaged(inp: Inputs) -> Inputs:
     """Same logical cache, rewritten as a contiguous pool with an identity
     page table (sequence b owns blocks b*max_blocks ...).  Used to check that

@@ -19,6 +19,12 @@ Sources (the pages this follows; the short names are used below):
   W_UV into the output side ("absorption").
 * [DF-snippet]     same page, section 1, the two cache-size helpers and the
   ratio they print for 128 heads x 128, 60 layers, 8192 context, 2 bytes.
+* [DF-moe]         same page, section 1, part "Make the feed-forward layer
+  sparse" and its formula box "Top-K routed MoE layer": the affinity of
+  token u and expert centroid e_i is u^T e_i, s_i is its softmax over the
+  routed experts, and g_i = s_i for the K_r largest s_i and 0 otherwise
+  (160 routed experts, 6 active per token, 2 shared experts that every
+  token uses and that need no gate).
 * [CA-takeaways]   crackai.dev "DeepSeek-V2" card, "Key Takeaways for
   Interviews": MHA caches 2 x n_heads x d_head, GQA 2 x n_groups x d_head, MLA
   d_latent plus the small RoPE part, per token per layer.
@@ -36,7 +42,10 @@ len - (S_q - 1 - i) cached tokens (its own included).  For the append: the
 position key is k^R = RoPE_p(W_KR h) with the textbook rotation (pairs
 (2j, 2j+1) turned by p * theta^(-2j/64), theta = 10000); the S_q new tokens
 of a sequence sit at positions len - S_q + i; an fp8 cache row holds E4M3
-codes of c / s with s = max |c| / 448.
+codes of c / s with s = max |c| / 448.  For the MoE gate: the softmax runs
+over the routed experts' affinities only; g_i is s_i itself (the formula does
+not renormalise the K_r kept scores); the kept experts are listed by
+decreasing s, and of equal scores the lower expert index ranks first.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 facts fixed outside this file -- numbers the pages print, closed forms, a
@@ -63,6 +72,7 @@ __all__ = [
     "default_softmax_scale", "absorb_queries", "project_output",
     "down_project", "rope_angles", "rope_rotate", "e4m3_values", "e4m3_round_codes",
     "quantize_latent", "appended_tokens",
+    "expert_affinities", "gate_softmax", "top_k", "moe_gate", "gate_dense",
 ]
 
 
@@ -440,3 +450,47 @@ def appended_tokens(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, seq_lens
             out.append((b, p, c_all[r], rope_rotate(k_all[r], p, theta)))
     return out
 
+
+
+# ----------------------------------------------------------------------------
+# MoE gate ([DF-moe]: s_i = softmax_i(u^T e_i); g_i = s_i for the K_r largest
+# s_i, else 0)
+# ----------------------------------------------------------------------------
+
+def expert_affinities(u: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """u^T e_i for every token (rows of u) and every expert centroid (rows of
+    e), in fp64: a [tokens x experts] array."""
+    return np.asarray(u, dtype=np.float64) @ np.asarray(e, dtype=np.float64).T
+
+
+def gate_softmax(a: np.ndarray) -> np.ndarray:
+    """s_i = exp(a_i) / sum_j exp(a_j) over the last axis (the largest
+    affinity subtracted first, which leaves the quotient unchanged)."""
+    a = np.asarray(a, dtype=np.float64)
+    z = np.exp(a - a.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def top_k(s: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest entries of each row, largest first; of equal
+    entries the lower index comes first (a stable sort of -s)."""
+    s = np.asarray(s, dtype=np.float64)
+    return np.argsort(-s, axis=-1, kind="stable")[..., :k]
+
+
+def moe_gate(u: np.ndarray, e: np.ndarray, k: int):
+    """The routed gate of each token: (idx [tokens x k] int64, the kept
+    experts by decreasing score; g [tokens x k], their gate values g_i = s_i;
+    s [tokens x experts], every score)."""
+    s = gate_softmax(expert_affinities(u, e))
+    idx = top_k(s, k)
+    return idx, np.take_along_axis(s, idx, axis=-1), s
+
+
+def gate_dense(u: np.ndarray, e: np.ndarray, k: int) -> np.ndarray:
+    """g over all experts as the formula writes it: s_i where expert i is
+    among the k kept, 0 elsewhere ([tokens x experts])."""
+    idx, g, s = moe_gate(u, e, k)
+    out = np.zeros_like(s)
+    np.put_along_axis(out, idx, g, axis=-1)
+    return out

@@ -446,8 +446,94 @@ def check_append_positions():
     assert np.allclose(c, w_dkv @ h[3], rtol=0, atol=1e-12) and np.allclose(kr, w_kr @ h[3], rtol=0, atol=1e-12)
 
 
+def check_gate_worked_example():
+    """[DF-moe] by hand: affinities (0, ln 2, ln 3) give s = (1/6, 1/3, 1/2);
+    with K_r = 2 the kept experts are 2 then 1 with g = (1/2, 1/3), expert 0
+    gets g = 0; and a hand product u^T e_i."""
+    e = np.log(np.array([[1.0], [2.0], [3.0]]))
+    idx, g, s = O.moe_gate(np.array([[1.0]]), e, 2)
+    assert np.allclose(s, [[1 / 6, 1 / 3, 1 / 2]], rtol=0, atol=1e-15)
+    assert idx.tolist() == [[2, 1]]
+    assert np.allclose(g, [[0.5, 1 / 3]], rtol=0, atol=1e-15)
+    assert np.allclose(O.gate_dense(np.array([[1.0]]), e, 2), [[0.0, 1 / 3, 0.5]], rtol=0, atol=1e-15)
+    # u = (2, 1) against centroids (1, 2), (3, 4), (-1, 0): 4, 10, -2
+    a = O.expert_affinities(np.array([[2.0, 1.0]]), np.array([[1.0, 2.0], [3.0, 4.0], [-1.0, 0.0]]))
+    assert np.array_equal(a, [[4.0, 10.0, -2.0]])
+    rng = np.random.default_rng(31)
+    ee = rng.standard_normal((160, 96))
+    for m in (0, 95):                      # a one-hot token reads one coordinate of every centroid
+        u = np.zeros((1, 96))
+        u[0, m] = 1.0
+        assert np.array_equal(O.expert_affinities(u, ee)[0], ee[:, m])
+
+
+def check_gate_softmax():
+    """The scores are a softmax: agreement with scipy's routine, invariance
+    to a common shift of the affinities, and the sum of all 160 scores 1."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(32)
+    a = rng.standard_normal((5, 160)) * 4
+    s = O.gate_softmax(a)
+    assert np.allclose(s, softmax(a, axis=-1), rtol=1e-13, atol=0)
+    assert np.allclose(O.gate_softmax(a + 700.0), s, rtol=1e-12, atol=0)
+    assert np.allclose(s.sum(axis=-1), 1.0, rtol=0, atol=1e-14)
+
+
+def _rank_ok(s, idx, k):
+    """Brute force, pure Python: idx lists k distinct experts by decreasing
+    score (equal scores by increasing index), and every expert left out
+    ranks below every one kept."""
+    n = len(s)
+    idx = [int(i) for i in idx]
+    if len(idx) != k or len(set(idx)) != k:
+        return False
+    before = lambda i, j: s[i] > s[j] or (s[i] == s[j] and i < j)  # noqa: E731
+    if any(not before(idx[t], idx[t + 1]) for t in range(k - 1)):
+        return False
+    return all(before(i, j) for i in idx for j in range(n) if j not in idx)
+
+
+def check_gate_top_k():
+    """TopK keeps the K_r largest scores: hand cases with ties (the lower
+    index first), brute force over random rows with planted ties, and
+    K_r = N keeping every expert with g summing to 1."""
+    s = np.array([[0.2, 0.3, 0.3, 0.2]])
+    assert O.top_k(s, 2).tolist() == [[1, 2]]
+    assert O.top_k(s, 3).tolist() == [[1, 2, 0]]
+    assert O.top_k(np.array([[0.1, 0.4, 0.2, 0.3]]), 4).tolist() == [[1, 3, 2, 0]]
+    rng = np.random.default_rng(33)
+    for _ in range(40):
+        row = np.round(rng.standard_normal(24), 1)          # many equal values
+        for k in (1, 6, 24):
+            assert _rank_ok(row, O.top_k(row[None], k)[0], k), (row, k)
+    u, e = rng.standard_normal((3, 32)), rng.standard_normal((160, 32))
+    idx, g, s = O.moe_gate(u, e, 160)
+    assert all(sorted(r.tolist()) == list(range(160)) for r in idx)
+    assert np.allclose(g.sum(axis=-1), 1.0, rtol=0, atol=1e-13)
+
+
+def check_gate_deepseek_shape():
+    """160 routed experts, 6 kept: exactly 6 nonzero gate values per token,
+    each the token's score of that expert, every one at least as large as
+    every score left out, and their sum below 1 (no renormalisation)."""
+    rng = np.random.default_rng(34)
+    u, e = rng.standard_normal((8, 64)), rng.standard_normal((160, 64)) / 8
+    gd = O.gate_dense(u, e, 6)
+    idx, g, s = O.moe_gate(u, e, 6)
+    sp = O.gate_softmax(O.expert_affinities(u, e))
+    for t in range(8):
+        nz = np.flatnonzero(gd[t])
+        assert sorted(nz.tolist()) == sorted(idx[t].tolist()) and len(nz) == 6
+        assert np.array_equal(gd[t][nz], sp[t][nz])
+        assert gd[t][nz].min() >= np.delete(sp[t], nz).max()
+        assert gd[t].sum() < 1.0
+        assert _rank_ok(sp[t].tolist(), idx[t], 6)
+        assert np.array_equal(g[t], sp[t][idx[t]])
+
+
 ALL_CHECKS = [check_cache_arithmetic, check_decode_tables, check_softmax,
               check_textbook_reduction, check_closed_forms, check_brute_force_exact,
               check_paging_invariance, check_causal_two_tokens, check_split_combine,
               check_absorb_project_identities, check_append_projection, check_rope,
-              check_e4m3_encoding, check_fp8_row, check_append_positions]
+              check_e4m3_encoding, check_fp8_row, check_append_positions,
+              check_gate_worked_example, check_gate_softmax, check_gate_top_k, check_gate_deepseek_shape]

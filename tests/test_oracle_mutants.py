@@ -201,6 +201,54 @@ def _appended_off_by_one(h, w_dkv, w_kr, seq_lens, q_per_seq, theta=10000.0):
     return out
 
 
+def _affinity_reversed_dim(u, e):
+    return np.asarray(u, dtype=np.float64) @ np.asarray(e, dtype=np.float64)[:, ::-1].T
+
+
+def _gate_softmax_no_norm(a):
+    a = np.asarray(a, dtype=np.float64)
+    return np.exp(a - a.max(axis=-1, keepdims=True))
+
+
+def _gate_softmax_wrong_axis(a):
+    a = np.asarray(a, dtype=np.float64)
+    z = np.exp(a - a.max(axis=0, keepdims=True))
+    return z / z.sum(axis=0, keepdims=True)
+
+
+def _top_k_ascending(s, k):
+    return np.argsort(np.asarray(s), axis=-1, kind="stable")[..., :k]
+
+
+def _top_k_ties_high(s, k):
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[-1]
+    return (n - 1 - np.argsort(-s[..., ::-1], axis=-1, kind="stable"))[..., :k]
+
+
+def _top_k_unsorted(s, k):
+    s = np.asarray(s, dtype=np.float64)
+    return np.sort(np.argsort(-s, axis=-1, kind="stable")[..., :k], axis=-1)
+
+
+def _moe_gate_renormalised(u, e, k):
+    s = M.gate_softmax(M.expert_affinities(u, e))
+    idx = M.top_k(s, k)
+    g = np.take_along_axis(s, idx, axis=-1)
+    return idx, g / g.sum(axis=-1, keepdims=True), s
+
+
+def _moe_gate_raw_affinity(u, e, k):
+    a = M.expert_affinities(u, e)
+    s = M.gate_softmax(a)
+    idx = M.top_k(s, k)
+    return idx, np.take_along_axis(a, idx, axis=-1), s
+
+
+def _gate_dense_keeps_all(u, e, k):
+    return M.gate_softmax(M.expert_affinities(u, e))
+
+
 MUTANTS = {
     "down_project": [_down_project_drops_last],
     "rope_rotate": [_rope_half_split, _rope_wrong_sign],
@@ -223,6 +271,11 @@ MUTANTS = {
     "cache_numbers_per_token_layer": [_cache_mha_one_vector],
     "absorb_queries": [_absorb_first_head],
     "project_output": [_project_first_head, _project_drops_last_column],
+    "expert_affinities": [_affinity_reversed_dim],
+    "gate_softmax": [_gate_softmax_no_norm, _gate_softmax_wrong_axis],
+    "top_k": [_top_k_ascending, _top_k_ties_high, _top_k_unsorted],
+    "moe_gate": [_moe_gate_renormalised, _moe_gate_raw_affinity],
+    "gate_dense": [_gate_dense_keeps_all],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]
