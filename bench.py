@@ -179,6 +179,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip timing the cache append")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--no-gate", action="store_true", help="skip timing the MoE gate")
+    ap.add_argument("--gate-tokens", type=int, nargs="*", default=None,
+                    help="token counts at which to time the MoE gate (default: the step's tokens and 4096)")
     ap.add_argument("--q-per-seq", type=int, default=0,
                     help="query tokens per sequence instead of the workload's (multi-token decode)")
     ap.add_argument("--append-d-model", type=int, default=5120,
@@ -211,7 +214,7 @@ def main():
         return
     import mla_inputs as MI
     from mla_latent_kv_17_amd import mla_decode
-    from mla_latent_kv_17_amd.runner import CacheAppend, DecodeStep, DeviceInputs
+    from mla_latent_kv_17_amd.runner import CacheAppend, DecodeStep, DeviceInputs, MoeGate
 
     wl = MI.WORKLOADS[args.workload]
     if args.q_per_seq:  # multi-token decode on the workload's cache (context figure, not a configuration)
@@ -345,6 +348,35 @@ def main():
                   "frac_hbm": app_bytes / (app_us * 1e-6) / HBM_PEAK,
                   "timing": "median of 20 launches, each after an eviction read, HIP events around the two launches"}
 
+    # the MoE gate of DeepSeek-V2's routed experts (160 centroids of width
+    # 5120, top 6), a second workload beside the attention path: at the
+    # step's token count and at a prefill-sized 4096 tokens
+    gate = None
+    if not args.no_gate:
+        gate_runs = []
+        for T in (args.gate_tokens if args.gate_tokens is not None else [wl.batch * wl.q_per_seq, 4096]):
+            g = MoeGate(MI.generate_gate(T, d_model=MI.APPEND_D_MODEL), "bf16", torch.device("cuda", 0))
+            for _ in range(3):
+                g.run()
+            gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for e0, e1 in gev:
+                do_flush()
+                e0.record()
+                g.run()
+                e1.record()
+            torch.cuda.synchronize()
+            g_us = float(np.median([a.elapsed_time(b) for a, b in gev])) * 1e3
+            d, n, k = MI.APPEND_D_MODEL, MI.GATE_EXPERTS, MI.GATE_TOP_K
+            g_bytes = (T + n) * d * 2 + T * k * 8
+            gate_runs.append({"tokens": T, "us": g_us, "algorithmic_bytes": g_bytes,
+                              "achieved_gbps": g_bytes / (g_us * 1e-6) / 1e9,
+                              "frac_hbm": g_bytes / (g_us * 1e-6) / HBM_PEAK,
+                              "tflops": 2.0 * T * n * d / (g_us * 1e-6) / 1e12})
+            del g
+        gate = {"kernels": "gate_proj_mfma + gate_finish", "d_model": MI.APPEND_D_MODEL,
+                "n_experts": MI.GATE_EXPERTS, "top_k": MI.GATE_TOP_K, "dtype": "bf16", "runs": gate_runs,
+                "timing": "median of 20 launches, each after an eviction read, HIP events around the two launches"}
+
     peaks = None if args.no_peaks else measured_peaks(torch)
 
     eager_ms_per_step = float(step_ms.mean())
@@ -405,6 +437,7 @@ def main():
         "warm_ms_per_step": warm_ms,
         "wall_s_timed_loop_incl_eviction": wall,
         "cache_append": append,
+        "moe_gate": gate,
         "measured_peaks": peaks,
     }
     if not args.no_cpu:

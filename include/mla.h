@@ -55,8 +55,8 @@ extern "C" {
 
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
  * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append;
- * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2) */
-#define MLA_ABI_VERSION 6
+ * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2); 7: adds mla_moe_gate */
+#define MLA_ABI_VERSION 7
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -232,6 +232,42 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
 
 /* Bytes of workspace mla_cache_append needs for these sizes (host-only). */
 int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64_t* bytes);
+
+/* MoE gate: the routed experts each token uses and their gate values
+ * (deepforge.srivtx.xyz "DeepSeek-V2", section 1, "Make the feed-forward
+ * layer sparse" and its formula box "Top-K routed MoE layer"; DeepSeek-V2
+ * routes over 160 experts and keeps 6, and its 2 shared experts take every
+ * token without a gate).  For token t with hidden state u (row t of u) and
+ * expert centroids e_i (rows of e):
+ *   a_i = u^T e_i                      (exact products, fp32 sums over d_model)
+ *   s_i = exp(a_i - max_j a_j) / sum_j exp(a_j - max_j a_j)    over the n_experts
+ *   idx[t][0..top_k-1]: the top_k experts of largest s_i, largest first; the
+ *        order compares the fp32 a_i (the softmax keeps it), and of equal a_i
+ *        the lower expert index comes first
+ *   weight[t][k] = s_(idx[t][k]): g_i = s_i, not renormalised over the kept
+ *        experts (every expert not listed has g_i = 0)
+ *   scores[t][i] = s_i if scores is not NULL.
+ * u:      [tokens][d_model], e: [n_experts][d_model], both in_dtype (BF16 or
+ *         F32), 16-byte aligned
+ * idx:    [tokens][top_k] int32; weight: [tokens][top_k] fp32;
+ *         scores: [tokens][n_experts] fp32 or NULL; caller-owned device memory
+ * tokens: 0 .. 2097152 (fp32 inputs: 0 .. 65535); 0 launches nothing, and then
+ *         the pointers are not read (NULL allowed) once the sizes are valid
+ * d_model: a multiple of 64, 64 .. 65536; n_experts: 1 .. 256;
+ * top_k: 1 .. min(n_experts, 16)
+ * workspace: device memory of at least mla_moe_gate_workspace_size() bytes
+ *         (16-byte aligned; fp32 partial sums, contents on return unspecified)
+ * The affinities must be finite (a NaN or infinite one leaves the selection
+ * unspecified).  Errors: MLA_ERR_NULL (a required pointer), MLA_ERR_SHAPE
+ * (sizes, short workspace), MLA_ERR_DTYPE, MLA_ERR_ALIGN; nothing is
+ * launched on an error. */
+int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top_k, const void* u, const void* e,
+                 int32_t in_dtype, int32_t* idx, float* weight, float* scores, void* workspace,
+                 int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_moe_gate needs for these sizes (host-only). */
+int mla_moe_gate_workspace_size(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype,
+                                int64_t* bytes);
 
 /* A launch-shape helper: the num_splits mla_decode should use so that the
  * device's compute units are filled, given the longest sequence length the

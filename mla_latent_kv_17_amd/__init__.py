@@ -28,7 +28,9 @@ D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 # the C entry points this binding exposes (also checked by the tests)
 EXPORTS = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_decode",
            "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits",
-           "mla_cache_append", "mla_cache_append_workspace_size"]
+           "mla_cache_append", "mla_cache_append_workspace_size", "mla_moe_gate",
+           "mla_moe_gate_workspace_size"]
+MLA_GATE_MAX_EXPERTS, MLA_GATE_MAX_TOP_K = 256, 16
 
 
 class MlaDims(ctypes.Structure):
@@ -88,6 +90,8 @@ def _load():
         "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
         "mla_cache_append": ([dp, i32, vp, vp, vp, i32, ctypes.c_float, kvp, vp, ctypes.c_int64, vp], ctypes.c_int),
         "mla_cache_append_workspace_size": ([dp, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+        "mla_moe_gate": ([i32, i32, i32, i32, vp, vp, i32, vp, f32p, f32p, vp, ctypes.c_int64, vp], ctypes.c_int),
+        "mla_moe_gate_workspace_size": ([i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -217,3 +221,26 @@ def mla_cache_append(dims: MlaDims, d_model: int, h, w_dkv, w_kr, cache: PagedCa
                                                      ctypes.byref(cache.kv), _ptr(workspace),
                                                      int(workspace.numel() * workspace.element_size()),
                                                      _stream(stream)))
+
+
+def mla_moe_gate_workspace_size(tokens: int, d_model: int, n_experts: int, in_dtype: int) -> int:
+    """Bytes of workspace mla_moe_gate needs."""
+    out = ctypes.c_int64(0)
+    _check("mla_moe_gate_workspace_size",
+           _lib.mla_moe_gate_workspace_size(int(tokens), int(d_model), int(n_experts), int(in_dtype),
+                                            ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_moe_gate(u, e, top_k: int, idx, weight, workspace, scores=None, stream=None):
+    """The routed experts of each token (rows of u [tokens][d_model]) over the
+    centroids e [n_experts][d_model]: idx [tokens][top_k] int32 (largest score
+    first), weight [tokens][top_k] fp32 = their softmax scores, and every
+    score into scores [tokens][n_experts] if given."""
+    tokens, d_model = u.shape
+    if e.dtype != u.dtype or e.dim() != 2 or e.shape[1] != d_model:
+        raise ValueError(f"centroids {tuple(e.shape)} {e.dtype} do not match tokens {tuple(u.shape)} {u.dtype}")
+    _check("mla_moe_gate", _lib.mla_moe_gate(int(tokens), int(d_model), int(e.shape[0]), int(top_k), _ptr(u),
+                                             _ptr(e), _dtype_code(u), _ptr(idx), _ptr(weight), _ptr(scores),
+                                             _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                             _stream(stream)))

@@ -358,6 +358,76 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
   return st;
 }
 
+namespace {
+
+constexpr int32_t kGateMaxTokens = 65535 * 32;
+
+// 0 on success; the chunk count of the affinity partial sums in *chunks.
+int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype, int* chunks) {
+  if (tokens < 0 || d_model < 64 || d_model > 65536 || d_model % 64 || n_experts < 1 ||
+      n_experts > mla::kGateMaxExperts)
+    return MLA_ERR_SHAPE;
+  if (in_dtype == MLA_BF16) {
+    if (tokens > kGateMaxTokens) return MLA_ERR_SHAPE;
+    *chunks = (d_model + mla::kAppendChunk - 1) / mla::kAppendChunk;
+  } else if (in_dtype == MLA_F32) {
+    if (tokens > 65535) return MLA_ERR_SHAPE;
+    *chunks = 1;
+  } else {
+    return MLA_ERR_DTYPE;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+int mla_moe_gate_workspace_size(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype,
+                                int64_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL;
+  int chunks = 0;
+  const int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks);
+  if (st) return st;
+  *bytes = (int64_t)chunks * tokens * n_experts * 4;
+  return MLA_OK;
+}
+
+int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top_k, const void* u, const void* e,
+                 int32_t in_dtype, int32_t* idx, float* weight, float* scores, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+  int chunks = 0;
+  int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks);
+  if (st) return st;
+  if (top_k < 1 || top_k > n_experts || top_k > mla::kGateMaxTopK) return MLA_ERR_SHAPE;
+  if (tokens == 0) return MLA_OK;  // no token: nothing read or written, pointers unused
+  if (!u || !e || !idx || !weight || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(u) || !aligned16(e) || !aligned16(workspace) || ((uintptr_t)idx & 3u) ||
+      ((uintptr_t)weight & 3u) || ((uintptr_t)scores & 3u))
+    return MLA_ERR_ALIGN;
+  if (workspace_bytes < (int64_t)chunks * tokens * n_experts * 4) return MLA_ERR_SHAPE;
+  mla::GateArgs a;
+  a.u = u;
+  a.e = e;
+  a.part = (float*)workspace;
+  a.idx = idx;
+  a.weight = weight;
+  a.scores = scores;
+  a.tokens = tokens;
+  a.d_model = d_model;
+  a.n_experts = n_experts;
+  a.top_k = top_k;
+  a.chunks = chunks;
+  hipStream_t s = (hipStream_t)stream;
+  if (in_dtype == MLA_F32) {
+    st = launch("mla::gate_proj_f32", (const void*)mla::gate_proj_f32, dim3((n_experts + 3) / 4, tokens), dim3(256),
+                a, s);
+  } else {
+    const dim3 grid((n_experts + 63) / 64, chunks, (tokens + 31) / 32);
+    st = launch("mla::gate_proj_mfma", (const void*)mla::gate_proj_mfma, grid, dim3(256), a, s);
+  }
+  if (st) return st;
+  return launch("mla::gate_finish", (const void*)mla::gate_finish, dim3((tokens + 3) / 4), dim3(256), a, s);
+}
+
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits) {
   int st = check_dims(dims);
   if (st) return st;

@@ -10,14 +10,10 @@
 //
 // Two launches:
 //  * append_proj_mfma (bf16 inputs): X = h W^T with W = [W_DKV; W_KR]
-//    (576 x d_model), a [tokens x 576] product over K = d_model on the matrix
-//    cores (v_mfma_f32_32x32x16_bf16, exact products, fp32 sums).
-//    Workgroup = (64 output columns, 512-wide chunk of d_model, 32 tokens):
-//    it stages its W and h row slices in LDS with fully coalesced loads (a
-//    wave's load is 1 KB of one row; the operands' own lane layout would
-//    touch 32 rows per load), each wave multiplies a quarter of the chunk,
-//    and the four partial tiles sum through LDS into the chunk's fp32
-//    partial sums in the caller's workspace.  The weights are the traffic
+//    (576 x d_model), a [tokens x 576] product over K = d_model, one
+//    workgroup per (64 output columns, 512-wide chunk of d_model, 32 tokens)
+//    (proj_chunk_bf16: LDS-staged coalesced rows, matrix cores, fp32 chunk
+//    partials into the caller's workspace).  The weights are the traffic
 //    (576 x d_model x 2 bytes) and are read once; the small h is read once
 //    per column tile.
 //  * append_finish (one workgroup per token): the chunk sums, the rotation
@@ -25,76 +21,21 @@
 //    then the cache encoding and the write into the token's page row.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "proj_chunk.h"
 
 namespace mla {
 
+static_assert(kAppendChunk == kProjChunk, "the append's chunk is the projection routine's");
+
 __global__ void __launch_bounds__(256) append_proj_mfma(const AppendArgs a) {
-  constexpr int kPad = 33;          // LDS row stride (floats) of the partial tiles
-  constexpr int kRow = 1024 + 16;   // LDS row stride (bytes) of the staged operands
-  __shared__ __attribute__((aligned(16))) uint8_t ws[64 * kRow];  // W rows n0 .. n0+63, this chunk
-  __shared__ __attribute__((aligned(16))) uint8_t hs[32 * kRow];  // h rows m0 .. m0+31, this chunk
-  __shared__ float red[4][2][32 * kPad];
-  const int n0 = blockIdx.x * 64, chunk = blockIdx.y, m0 = blockIdx.z * 32;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 5, n32 = lane & 31;
-  const int k_lo = chunk * kAppendChunk;
-  const int klen = min(kAppendChunk, a.d_model - k_lo);  // a multiple of 64
-  // ---- staging: a wave's load is 1 KB of one row (64 lanes x 16 bytes);
-  // bytes past the chunk's end (a short last chunk) and rows past the last
-  // token stage zeros.  Every load is issued before the first store.
-  const int cb = lane * 16;  // byte of the row slice this lane moves
-  const bool in_k = cb < 2 * klen;
-  u32x4 wv[16], hv[8];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int n = n0 + 4 * i + wave;
-    const uint16_t* row = n < 512 ? (const uint16_t*)a.w_dkv + (int64_t)n * a.d_model
-                                  : (const uint16_t*)a.w_kr + (int64_t)(n - 512) * a.d_model;
-    wv[i] = *(const u32x4*)((const uint8_t*)(row + k_lo) + (in_k ? cb : 0));
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = m0 + 4 * i + wave;
-    hv[i] = *(const u32x4*)((const uint8_t*)((const uint16_t*)a.h + (int64_t)(r < a.tokens ? r : 0) * a.d_model + k_lo) +
-                            (in_k ? cb : 0));
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    *(MLA_LDS u32x4*)((MLA_LDS uint8_t*)ws + (4 * i + wave) * kRow + cb) = in_k ? wv[i] : u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool live = in_k && m0 + 4 * i + wave < a.tokens;
-    *(MLA_LDS u32x4*)((MLA_LDS uint8_t*)hs + (4 * i + wave) * kRow + cb) = live ? hv[i] : u32x4{0, 0, 0, 0};
-  }
-  __syncthreads();
-  // ---- products: wave w takes k-steps 8w .. 8w+7 of the chunk (16 k each):
-  // A = h rows (token n32, k + 8g .. +7), B = W rows (column 32 nt + n32, same k)
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int kb = (16 * (8 * wave + j) + 8 * g) * 2;
-    const bf16x8 av = *(const MLA_LDS bf16x8*)((const MLA_LDS uint8_t*)hs + n32 * kRow + kb);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const bf16x8 bv = *(const MLA_LDS bf16x8*)((const MLA_LDS uint8_t*)ws + (32 * nt + n32) * kRow + kb);
-      acc[nt] = mfma32x32x16(av, bv, acc[nt]);
-    }
-  }
-  // D lane l, register i: token (i/4)*8 + 4g + i%4 of the tile, column n32 of the 32-column block
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) red[wave][nt][((i >> 2) * 8 + 4 * g + (i & 3)) * kPad + n32] = acc[nt][i];
-  __syncthreads();
-  float* part = a.part + (int64_t)chunk * a.tokens * kAppendCols;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = i * 256 + tid;
-    const int row = idx >> 6, d = idx & 63, nt = d >> 5, n = d & 31;
-    const float v = red[0][nt][row * kPad + n] + red[1][nt][row * kPad + n] + red[2][nt][row * kPad + n] +
-                    red[3][nt][row * kPad + n];
-    if (m0 + row < a.tokens) part[(int64_t)(m0 + row) * kAppendCols + n0 + d] = v;
-  }
+  const uint16_t* w_dkv = (const uint16_t*)a.w_dkv;
+  const uint16_t* w_kr = (const uint16_t*)a.w_kr;
+  const int64_t dm = a.d_model;
+  auto wrow = [&](int n) __attribute__((always_inline)) -> const uint16_t* {
+    return n < 512 ? w_dkv + n * dm : w_kr + (n - 512) * dm;  // W_DKV rows, then W_KR rows
+  };
+  proj_chunk_bf16((const uint16_t*)a.h, a.tokens, a.d_model, kAppendCols, wrow, blockIdx.x * 64, blockIdx.y,
+                  blockIdx.z * 32, a.part, kAppendCols);
 }
 
 // fp32 inputs: wave w of workgroup x computes column 4x + w of one token

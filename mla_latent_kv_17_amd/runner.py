@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 from . import (PagedCache, make_dims, mla_absorb_q, mla_cache_append, mla_cache_append_workspace_size,
-               mla_combine_out_uv, mla_decode, mla_decode_num_splits, mla_out_uv, mla_split_combine)
+               mla_combine_out_uv, mla_decode, mla_decode_num_splits, mla_moe_gate, mla_moe_gate_workspace_size,
+               mla_out_uv, mla_split_combine, MLA_BF16, MLA_F32)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -165,3 +166,25 @@ class CacheAppend:
         mla_cache_append(self.dev.dims, self.d_model, self.h, self.w_dkv, self.w_kr, self.dev.cache,
                          self.workspace, self.rope_theta, stream)
 
+
+
+class MoeGate:
+    """Device copies of the gate inputs (tokens u, centroids e), its outputs
+    and workspace; run() selects the top_k experts of every token
+    (mla_moe_gate)."""
+
+    def __init__(self, gi, kind: str = "bf16", device=None, with_scores: bool = False):
+        device = device or torch.device("cuda", 0)
+        self.u = _dev(gi.u, kind, device)
+        self.e = _dev(gi.e, kind, device)
+        self.top_k = gi.top_k
+        tokens, d_model = gi.u.shape
+        n = gi.e.shape[0]
+        self.idx = torch.empty((tokens, gi.top_k), dtype=torch.int32, device=device)
+        self.weight = torch.empty((tokens, gi.top_k), dtype=torch.float32, device=device)
+        self.scores = torch.empty((tokens, n), dtype=torch.float32, device=device) if with_scores else None
+        ws = mla_moe_gate_workspace_size(tokens, d_model, n, MLA_BF16 if kind == "bf16" else MLA_F32)
+        self.workspace = torch.empty(max(ws // 4, 4), dtype=torch.float32, device=device)
+
+    def run(self, stream=None):
+        mla_moe_gate(self.u, self.e, self.top_k, self.idx, self.weight, self.workspace, self.scores, stream)

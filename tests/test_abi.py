@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 12, syms
     lib = ctypes.CDLL(M.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 6
+    assert M.abi_version() == 7
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -120,3 +120,39 @@ def test_cache_append_validation():
     assert L.mla_cache_append(ctypes.byref(M.make_dims(0, 1, 128)), 640, 0x1000, 0x2000, 0x3000, M.MLA_BF16,
                               10000.0, ctypes.byref(_kv()), 0x9000, 0, None) == M.MLA_OK  # nothing to do
 
+
+
+def test_moe_gate_validation():
+    L = M._lib
+    n = ctypes.c_int64(0)
+    assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 10 * 32 * 160 * 4
+    assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_F32, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 32 * 160 * 4
+    assert L.mla_moe_gate_workspace_size(32, 5120, 257, M.MLA_BF16, ctypes.byref(n)) == M.MLA_ERR_SHAPE
+    assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_FP8_E4M3, ctypes.byref(n)) == M.MLA_ERR_DTYPE
+    assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_BF16, None) == M.MLA_ERR_NULL
+
+    def call(T=32, D=640, N=160, K=6, u=0x1000, e=0x2000, dt=M.MLA_BF16, idx=0x3000, w=0x4000, sc=None,
+             ws=0x9000, wsb=1 << 20):
+        return L.mla_moe_gate(T, D, N, K, u, e, dt, idx, w, sc, ws, wsb, None)
+    assert call(u=0) == M.MLA_ERR_NULL
+    assert call(idx=0) == M.MLA_ERR_NULL
+    assert call(ws=0) == M.MLA_ERR_NULL
+    assert call(D=100) == M.MLA_ERR_SHAPE
+    assert call(D=65536 + 64) == M.MLA_ERR_SHAPE
+    assert call(N=0) == M.MLA_ERR_SHAPE
+    assert call(N=257) == M.MLA_ERR_SHAPE
+    assert call(K=0) == M.MLA_ERR_SHAPE
+    assert call(K=17, N=160) == M.MLA_ERR_SHAPE
+    assert call(K=5, N=4) == M.MLA_ERR_SHAPE
+    assert call(T=-1) == M.MLA_ERR_SHAPE
+    assert call(T=65536, dt=M.MLA_F32) == M.MLA_ERR_SHAPE
+    assert call(dt=M.MLA_FP8_E4M3) == M.MLA_ERR_DTYPE
+    assert call(u=0x1008) == M.MLA_ERR_ALIGN
+    assert call(w=0x4002) == M.MLA_ERR_ALIGN
+    assert call(sc=0x5001) == M.MLA_ERR_ALIGN
+    assert call(wsb=2 * 32 * 160 * 4 - 4) == M.MLA_ERR_SHAPE          # 640 wide: two chunks
+    assert call(T=0, wsb=0) == M.MLA_OK                                 # nothing to do
+    assert call(T=0, u=0, idx=0, w=0, ws=0, wsb=0) == M.MLA_OK          # ... and no pointer read
+    assert call(T=0, K=0) == M.MLA_ERR_SHAPE                            # sizes still checked
