@@ -11,6 +11,7 @@
 
 #include "mla.h"
 #include "mla_kernels.h"
+#include "gate_kernels.h"
 
 namespace {
 
@@ -369,7 +370,7 @@ int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dt
     return MLA_ERR_SHAPE;
   if (in_dtype == MLA_BF16) {
     if (tokens > kGateMaxTokens) return MLA_ERR_SHAPE;
-    *chunks = (d_model + mla::kAppendChunk - 1) / mla::kAppendChunk;
+    *chunks = (d_model + mla::kGateChunk - 1) / mla::kGateChunk;
   } else if (in_dtype == MLA_F32) {
     if (tokens > 65535) return MLA_ERR_SHAPE;
     *chunks = 1;

@@ -21,12 +21,13 @@
 //    affinities never tie through the rounding of exp.  Equal affinities
 //    rank the lower expert index first.
 #include "mla_device.h"
-#include "mla_kernels.h"
+#include "gate_kernels.h"
 #include "proj_chunk.h"
 
 namespace mla {
 
 static_assert(kGateMaxExperts == 4 * 64, "four experts per lane");
+static_assert(kGateChunk == kProjChunk, "the gate's chunk is the projection routine's");
 
 __global__ void __launch_bounds__(256) gate_proj_mfma(const GateArgs a) {
   const uint16_t* e = (const uint16_t*)a.e;

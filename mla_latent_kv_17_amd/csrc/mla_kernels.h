@@ -89,23 +89,4 @@ __global__ void append_proj_f32(const AppendArgs a);   // fp32 inputs
 template <int kFmt>  // 0 fp32, 1 bf16, 2 fp8 cache
 __global__ void append_finish(const AppendArgs a);
 
-// MoE gate (s_i = softmax over the routed experts of u^T e_i; the top_k
-// largest kept, g_i = s_i).  Affinities in two steps as in the append: fp32
-// partial sums over 512-wide chunks of d_model into the caller's workspace,
-// then per token the chunk sums, the softmax and the selection.
-constexpr int kGateMaxExperts = 256;
-constexpr int kGateMaxTopK = 16;
-struct GateArgs {
-  const void* u;   // [tokens][d_model]
-  const void* e;   // [n_experts][d_model] expert centroids
-  float* part;     // [chunks][tokens][n_experts]
-  int32_t* idx;    // [tokens][top_k]
-  float* weight;   // [tokens][top_k]
-  float* scores;   // [tokens][n_experts] or null
-  int tokens, d_model, n_experts, top_k, chunks;
-};
-__global__ void gate_proj_mfma(const GateArgs a);  // bf16 inputs
-__global__ void gate_proj_f32(const GateArgs a);   // fp32 inputs
-__global__ void gate_finish(const GateArgs a);
-
 }  // namespace mla
