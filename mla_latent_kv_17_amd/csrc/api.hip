@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "mla.h"
@@ -363,16 +364,29 @@ namespace {
 
 constexpr int32_t kGateMaxTokens = 65535 * 32;
 
-// 0 on success; the chunk count of the affinity partial sums in *chunks.
-int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype, int* chunks) {
+// 0 on success.  The d_model slices of the affinity partial sums: their
+// count in *chunks and width in *kslice (a multiple of 64; the last slice
+// shorter).  bf16 inputs from kGateTallMinTokens tokens on take the tall
+// kernel, with slices cut so that about 512 workgroups (two per compute
+// unit) fill the device, none narrower than 512 unless d_model is; fewer
+// tokens take 512-wide slices; fp32 inputs one slice.
+int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype, int* chunks, int* kslice) {
   if (tokens < 0 || d_model < 64 || d_model > 65536 || d_model % 64 || n_experts < 1 ||
       n_experts > mla::kGateMaxExperts)
     return MLA_ERR_SHAPE;
   if (in_dtype == MLA_BF16) {
     if (tokens > kGateMaxTokens) return MLA_ERR_SHAPE;
-    *chunks = (d_model + mla::kGateChunk - 1) / mla::kGateChunk;
+    int ks = mla::kGateChunk;
+    if (tokens >= mla::kGateTallMinTokens) {
+      const int tiles = (tokens + mla::kGateTallM - 1) / mla::kGateTallM;
+      const int want = std::max(1, std::min((512 + tiles - 1) / tiles, d_model / mla::kGateChunk));
+      ks = ((d_model + want - 1) / want + 63) / 64 * 64;
+    }
+    *kslice = ks;
+    *chunks = (d_model + ks - 1) / ks;
   } else if (in_dtype == MLA_F32) {
     if (tokens > 65535) return MLA_ERR_SHAPE;
+    *kslice = d_model;
     *chunks = 1;
   } else {
     return MLA_ERR_DTYPE;
@@ -385,8 +399,8 @@ int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dt
 int mla_moe_gate_workspace_size(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype,
                                 int64_t* bytes) {
   if (!bytes) return MLA_ERR_NULL;
-  int chunks = 0;
-  const int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks);
+  int chunks = 0, kslice = 0;
+  const int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks, &kslice);
   if (st) return st;
   *bytes = (int64_t)chunks * tokens * n_experts * 4;
   return MLA_OK;
@@ -395,8 +409,8 @@ int mla_moe_gate_workspace_size(int32_t tokens, int32_t d_model, int32_t n_exper
 int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top_k, const void* u, const void* e,
                  int32_t in_dtype, int32_t* idx, float* weight, float* scores, void* workspace,
                  int64_t workspace_bytes, void* stream) {
-  int chunks = 0;
-  int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks);
+  int chunks = 0, kslice = 0;
+  int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks, &kslice);
   if (st) return st;
   if (top_k < 1 || top_k > n_experts || top_k > mla::kGateMaxTopK) return MLA_ERR_SHAPE;
   if (tokens == 0) return MLA_OK;  // no token: nothing read or written, pointers unused
@@ -417,10 +431,21 @@ int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top
   a.n_experts = n_experts;
   a.top_k = top_k;
   a.chunks = chunks;
+  a.kslice = kslice;
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == MLA_F32) {
     st = launch("mla::gate_proj_f32", (const void*)mla::gate_proj_f32, dim3((n_experts + 3) / 4, tokens), dim3(256),
                 a, s);
+  } else if (tokens >= mla::kGateTallMinTokens) {
+    const dim3 grid(chunks, (tokens + mla::kGateTallM - 1) / mla::kGateTallM);
+    const void* k = nullptr;
+    switch (((n_experts + 31) / 32 + 1) / 2) {
+      case 1: k = (const void*)mla::gate_proj_tall<1>; break;
+      case 2: k = (const void*)mla::gate_proj_tall<2>; break;
+      case 3: k = (const void*)mla::gate_proj_tall<3>; break;
+      default: k = (const void*)mla::gate_proj_tall<4>; break;
+    }
+    st = launch("mla::gate_proj_tall", k, grid, dim3(256), a, s);
   } else {
     const dim3 grid((n_experts + 63) / 64, chunks, (tokens + 31) / 32);
     st = launch("mla::gate_proj_mfma", (const void*)mla::gate_proj_mfma, grid, dim3(256), a, s);

@@ -22,9 +22,15 @@ struct GateArgs {
   int32_t* idx;    // [tokens][top_k]
   float* weight;   // [tokens][top_k]
   float* scores;   // [tokens][n_experts] or null
-  int tokens, d_model, n_experts, top_k, chunks;
+  int tokens, d_model, n_experts, top_k;
+  int chunks;  // partial sums per token: d_model slices of kslice (the last shorter)
+  int kslice;  // a multiple of 64
 };
-__global__ void gate_proj_mfma(const GateArgs a);  // bf16 inputs
+constexpr int kGateTallM = 64;         // tokens per workgroup of gate_proj_tall
+constexpr int kGateTallMinTokens = 512;  // from this many tokens on, gate_proj_tall
+__global__ void gate_proj_mfma(const GateArgs a);  // bf16 inputs, few tokens
+template <int kTilesPerWave>  // ceil(ceil(n_experts / 32) / 2)
+__global__ void gate_proj_tall(const GateArgs a);  // bf16 inputs, many tokens
 __global__ void gate_proj_f32(const GateArgs a);   // fp32 inputs
 __global__ void gate_finish(const GateArgs a);
 

@@ -129,6 +129,11 @@ def test_moe_gate_validation():
     assert n.value == 10 * 32 * 160 * 4
     assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_F32, ctypes.byref(n)) == M.MLA_OK
     assert n.value == 32 * 160 * 4
+    # from 512 tokens on: slices cut for about 512 workgroups of 64 tokens (4096 tokens: 8 slices of 640)
+    assert L.mla_moe_gate_workspace_size(4096, 5120, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 8 * 4096 * 160 * 4
+    assert L.mla_moe_gate_workspace_size(600, 640, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 1 * 600 * 160 * 4
     assert L.mla_moe_gate_workspace_size(32, 5120, 257, M.MLA_BF16, ctypes.byref(n)) == M.MLA_ERR_SHAPE
     assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_FP8_E4M3, ctypes.byref(n)) == M.MLA_ERR_DTYPE
     assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_BF16, None) == M.MLA_ERR_NULL

@@ -116,6 +116,11 @@ CASES = {
     "bf16_max": (33, 1024, 256, 16, "bf16"),
     "bf16_one_expert": (5, 64, 1, 1, "bf16"),
     "bf16_keep_all": (9, 192, 24, 16, "bf16"),
+    # from 512 tokens on the tall projection kernel (64 tokens x every expert per workgroup)
+    "bf16_tall_ragged": (600, 640, 160, 6, "bf16"),
+    "bf16_tall_max": (531, 1024, 256, 16, "bf16"),
+    "bf16_tall_few_experts": (517, 5120, 20, 4, "bf16"),
+    "bf16_tall_n100": (1000, 1536, 100, 8, "bf16"),
     "f32_small": (11, 192, 64, 8, "f32"),
     "f32_deepseek": (6, 5120, 160, 6, "f32"),
 }
@@ -135,12 +140,11 @@ def test_gate_vs_oracle(name):
 
 
 @pytest.mark.parametrize("twins", [False, True], ids=["distinct", "twins"])
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_gate_one_hot_exact(dt, twins):
+@pytest.mark.parametrize("dt,tokens", [("bf16", 40), ("bf16", 576), ("f32", 7)])
+def test_gate_one_hot_exact(dt, tokens, twins):
     """Exact affinities: the selection (ties included) equals the oracle's."""
-    print(f"[case] gate one-hot {dt} twins={twins}", flush=True)
-    gi = MI.generate_gate(40 if dt == "bf16" else 7, d_model=640, n_experts=160, top_k=6, dtype=dt, seed=3,
-                          one_hot=True, twins=twins)
+    print(f"[case] gate one-hot {dt} tokens={tokens} twins={twins}", flush=True)
+    gi = MI.generate_gate(tokens, d_model=640, n_experts=160, top_k=6, dtype=dt, seed=3, one_hot=True, twins=twins)
     idx, w, sc = _run(gi, dt)
     u, e = _decode(gi.u, dt), _decode(gi.e, dt)
     _check_selection(f"gate one-hot {dt} twins={twins}", idx, u, e, 6, exact=True)
