@@ -367,7 +367,7 @@ constexpr int32_t kGateMaxTokens = 65535 * 32;
 // 0 on success.  The d_model slices of the affinity partial sums: their
 // count in *chunks and width in *kslice (a multiple of 64; the last slice
 // shorter).  bf16 inputs from kGateTallMinTokens tokens on take the tall
-// kernel, with slices cut so that about 512 workgroups (two per compute
+// kernel, with slices cut so that about 256 workgroups (one per compute
 // unit) fill the device, none narrower than 512 unless d_model is; fewer
 // tokens take 512-wide slices; fp32 inputs one slice.
 int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype, int* chunks, int* kslice) {
@@ -379,7 +379,7 @@ int gate_shape(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dt
     int ks = mla::kGateChunk;
     if (tokens >= mla::kGateTallMinTokens) {
       const int tiles = (tokens + mla::kGateTallM - 1) / mla::kGateTallM;
-      const int want = std::max(1, std::min((512 + tiles - 1) / tiles, d_model / mla::kGateChunk));
+      const int want = std::max(1, std::min((256 + tiles - 1) / tiles, d_model / mla::kGateChunk));
       ks = ((d_model + want - 1) / want + 63) / 64 * 64;
     }
     *kslice = ks;
@@ -402,7 +402,7 @@ int mla_moe_gate_workspace_size(int32_t tokens, int32_t d_model, int32_t n_exper
   int chunks = 0, kslice = 0;
   const int st = gate_shape(tokens, d_model, n_experts, in_dtype, &chunks, &kslice);
   if (st) return st;
-  *bytes = (int64_t)chunks * tokens * n_experts * 4;
+  *bytes = (int64_t)chunks * tokens * ((n_experts + 3) / 4 * 4) * 4;
   return MLA_OK;
 }
 
@@ -418,7 +418,8 @@ int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top
   if (!aligned16(u) || !aligned16(e) || !aligned16(workspace) || ((uintptr_t)idx & 3u) ||
       ((uintptr_t)weight & 3u) || ((uintptr_t)scores & 3u))
     return MLA_ERR_ALIGN;
-  if (workspace_bytes < (int64_t)chunks * tokens * n_experts * 4) return MLA_ERR_SHAPE;
+  const int part_stride = (n_experts + 3) / 4 * 4;
+  if (workspace_bytes < (int64_t)chunks * tokens * part_stride * 4) return MLA_ERR_SHAPE;
   mla::GateArgs a;
   a.u = u;
   a.e = e;
@@ -432,26 +433,30 @@ int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top
   a.top_k = top_k;
   a.chunks = chunks;
   a.kslice = kslice;
+  a.part_stride = part_stride;
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == MLA_F32) {
     st = launch("mla::gate_proj_f32", (const void*)mla::gate_proj_f32, dim3((n_experts + 3) / 4, tokens), dim3(256),
                 a, s);
   } else if (tokens >= mla::kGateTallMinTokens) {
     const dim3 grid(chunks, (tokens + mla::kGateTallM - 1) / mla::kGateTallM);
-    const void* k = nullptr;
-    switch (((n_experts + 31) / 32 + 1) / 2) {
-      case 1: k = (const void*)mla::gate_proj_tall<1>; break;
-      case 2: k = (const void*)mla::gate_proj_tall<2>; break;
-      case 3: k = (const void*)mla::gate_proj_tall<3>; break;
-      default: k = (const void*)mla::gate_proj_tall<4>; break;
-    }
+    const void* const tall[8] = {(const void*)mla::gate_proj_tall<1>, (const void*)mla::gate_proj_tall<2>,
+                                 (const void*)mla::gate_proj_tall<3>, (const void*)mla::gate_proj_tall<4>,
+                                 (const void*)mla::gate_proj_tall<5>, (const void*)mla::gate_proj_tall<6>,
+                                 (const void*)mla::gate_proj_tall<7>, (const void*)mla::gate_proj_tall<8>};
+    const void* k = tall[(n_experts + 31) / 32 - 1];
     st = launch("mla::gate_proj_tall", k, grid, dim3(256), a, s);
   } else {
     const dim3 grid((n_experts + 63) / 64, chunks, (tokens + 31) / 32);
     st = launch("mla::gate_proj_mfma", (const void*)mla::gate_proj_mfma, grid, dim3(256), a, s);
   }
   if (st) return st;
-  return launch("mla::gate_finish", (const void*)mla::gate_finish, dim3((tokens + 3) / 4), dim3(256), a, s);
+  if (tokens <= mla::kGateWideFinishMaxTokens)  // 64 lanes and up to 4 experts per lane per token
+    return launch("mla::gate_finish<1, 64>", (const void*)mla::gate_finish<1, 64>, dim3((tokens + 3) / 4),
+                  dim3(256), a, s);
+  const void* const finish[4] = {(const void*)mla::gate_finish<1, 16>, (const void*)mla::gate_finish<2, 16>,
+                                 (const void*)mla::gate_finish<3, 16>, (const void*)mla::gate_finish<4, 16>};
+  return launch("mla::gate_finish", finish[(n_experts + 63) / 64 - 1], dim3((tokens + 15) / 16), dim3(256), a, s);
 }
 
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits) {

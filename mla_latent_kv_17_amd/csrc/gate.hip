@@ -14,19 +14,22 @@
 //    - gate_proj_mfma (few tokens): one workgroup per (64 experts, 512-wide
 //      slice, 32 tokens) through proj_chunk_bf16, so that even one token
 //      tile spreads the centroid read (the traffic) over many CUs;
-//    - gate_proj_tall (many tokens): one workgroup per (64 tokens, slice of
+//    - gate_proj_tall (many tokens): one workgroup per (128 tokens, slice of
 //      d_model) covering every expert, looping over its slice in 64-wide
-//      stages staged through LDS, so that each token row is read once and
-//      the partial sums stay few; the centroids (n_experts x d_model, 1.6 MB
-//      for DeepSeek-V2) are re-read from L2.
-//  * gate_finish: one wave per token.  Lane l owns experts l, l+64, l+128,
-//    l+192: the slice sums, the softmax (max, exp, sum across the wave),
-//    then top_k rounds of a wave argmax.  The selection compares the fp32
+//      stages staged through LDS, so that each token row is read once, each
+//      centroid row staged serves 128 tokens, and the partial sums stay
+//      few; the centroids (n_experts x d_model, 1.6 MB for DeepSeek-V2) are
+//      re-read from L2.
+//  * gate_finish: 16 lanes per token (many tokens) or 64 (few), each lane
+//    owning a run of 4 to 16 experts (16-byte loads per slice): the slice
+//    sums, the softmax (max, exp, sum across the token's lanes), then top_k
+//    rounds of an argmax over 64-bit keys (the affinity's ordered bits, then
+//    the complemented index).  The selection compares the fp32
 //    affinities, not the rounded scores: the softmax is strictly increasing
 //    in each affinity, so the order is the scores' order, and two distinct
 //    affinities never tie through the rounding of exp.  Equal affinities
-//    rank the lower expert index first.  Cross-lane steps use DPP moves
-//    within rows of 16 lanes and four lane reads across the rows.
+//    rank the lower expert index first.  Cross-lane steps are DPP moves
+//    within rows of 16 lanes, plus one lane read per row for 64 lanes.
 #include "mla_device.h"
 #include "gate_kernels.h"
 #include "proj_chunk.h"
@@ -34,6 +37,7 @@
 namespace mla {
 
 static_assert(kGateMaxExperts == 4 * 64, "four experts per lane");
+static_assert(kGateTallM == 4 * 32, "one 32-token tile per wave");
 static_assert(kGateChunk == kProjChunk, "the gate's chunk is the projection routine's");
 
 __global__ void __launch_bounds__(256) gate_proj_mfma(const GateArgs a) {
@@ -41,28 +45,33 @@ __global__ void __launch_bounds__(256) gate_proj_mfma(const GateArgs a) {
   const int64_t dm = a.d_model;
   auto wrow = [&](int n) __attribute__((always_inline)) -> const uint16_t* { return e + n * dm; };
   proj_chunk_bf16((const uint16_t*)a.u, a.tokens, a.d_model, a.n_experts, wrow, blockIdx.x * 64, blockIdx.y,
-                  blockIdx.z * 32, a.part, a.n_experts);
+                  blockIdx.z * 32, a.part, a.part_stride);
 }
 
 // Many tokens: workgroup (slice x, token tile y) computes the affinities of
-// tokens 64y .. 64y+63 with every expert over d_model slice x.  Per 64-wide
-// stage the 64 token rows and the centroid rows (2 * kTilesPerWave * 32, the
-// ones past n_experts zero) are loaded as 128-byte rows, 8 rows per wave
-// load, into one of two LDS buffers (rows padded to 144 bytes so that the
-// operand reads, 8 rows per pass at one column, hit distinct banks); the
-// loads of the next two stages are in flight while one is multiplied.  Wave w
-// owns token tile (w & 1) and expert tiles (w >> 1) * kTilesPerWave + j,
-// accumulating over all four 16-wide k-steps of a stage.
-template <int kTilesPerWave>
+// tokens 128y .. 128y+127 with every expert over d_model slice x.  Per
+// 64-wide stage the 128 token rows and the 32 * kNT centroid rows (rows past
+// the last token or expert repeat it; their results are never stored) are
+// loaded as 128-byte rows, 8 rows per wave load, into one of two LDS
+// buffers (rows padded to 144 bytes so that the operand reads, 8 rows per
+// pass at one column, hit distinct banks); the loads of the next two stages
+// are in flight while one is multiplied.  Wave w owns token tile w (32
+// tokens) against all kNT expert tiles, so each staged centroid row serves
+// 128 tokens.  The results leave through LDS: each wave writes its tile
+// there and stores rows of 16-byte pieces.
+template <int kNT>
 __global__ void __launch_bounds__(256) gate_proj_tall(const GateArgs a) {
   constexpr int kRow = 144;
-  constexpr int kER = 2 * kTilesPerWave * 32;  // staged centroid rows
-  constexpr int kLoads = (kGateTallM + kER) / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t us[2][kGateTallM * kRow];
-  __shared__ __attribute__((aligned(16))) uint8_t es[2][kER * kRow];
+  constexpr int kER = 32 * kNT;                            // staged centroid rows
+  constexpr int kLoads = (kGateTallM + kER) / 32;          // wave loads per lane per stage
+  constexpr int kBuf = (kGateTallM + kER) * kRow;          // one stage buffer
+  constexpr int kOutRow = 128 * 4 + 16;                    // output staging row: 128 fp32 + pad
+  constexpr int kOutWave = 32 * kOutRow;                   // one wave's output staging
+  constexpr int kLds = 2 * kBuf > 4 * kOutWave ? 2 * kBuf : 4 * kOutWave;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, n32 = lane & 31, sub = lane >> 3, piece = lane & 7;
-  const int T = a.tokens, N = a.n_experts, NT = (N + 31) / 32;
+  const int T = a.tokens, N = a.n_experts;
   const int m0 = blockIdx.y * kGateTallM;
   const int k_lo = blockIdx.x * a.kslice;
   const int stages = (min(a.d_model, k_lo + a.kslice) - k_lo) / 64;
@@ -83,62 +92,80 @@ __global__ void __launch_bounds__(256) gate_proj_tall(const GateArgs a) {
   auto store = [&](const u32x4 (&v)[kLoads], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int r = 32 * i + 8 * wave + sub;
-      const bool live = i < kGateTallM / 32 ? m0 + r < T : r - kGateTallM < N;
-      uint8_t* dst = i < kGateTallM / 32 ? &us[b][r * kRow] : &es[b][(r - kGateTallM) * kRow];
-      *(MLA_LDS u32x4*)(dst + 16 * piece) = live ? v[i] : u32x4{0, 0, 0, 0};
+      const int r = 32 * i + 8 * wave + sub;  // u rows, then e rows: one row index space
+      *(MLA_LDS u32x4*)&lds[b * kBuf + r * kRow + 16 * piece] = v[i];
     }
   };
-  const int mt = wave & 1, nt0 = (wave >> 1) * kTilesPerWave;
-  f32x16 acc[kTilesPerWave];
+  f32x16 acc[kNT];
 #pragma unroll
-  for (int j = 0; j < kTilesPerWave; ++j) acc[j] = f32x16{};
+  for (int j = 0; j < kNT; ++j) acc[j] = f32x16{};
   auto compute = [&](int b) __attribute__((always_inline)) {
+    const uint8_t* buf = &lds[b * kBuf];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb = 32 * ks + 16 * g;
-      const bf16x8 av = *(const MLA_LDS bf16x8*)&us[b][(32 * mt + n32) * kRow + kb];
+      const bf16x8 av = *(const MLA_LDS bf16x8*)&buf[(32 * wave + n32) * kRow + kb];
 #pragma unroll
-      for (int j = 0; j < kTilesPerWave; ++j)
-        if (nt0 + j < NT) {
-          const bf16x8 bv = *(const MLA_LDS bf16x8*)&es[b][(32 * (nt0 + j) + n32) * kRow + kb];
-          acc[j] = mfma32x32x16(av, bv, acc[j]);
-        }
+      for (int j = 0; j < kNT; ++j) {
+        const bf16x8 bv = *(const MLA_LDS bf16x8*)&buf[(kGateTallM + 32 * j + n32) * kRow + kb];
+        acc[j] = mfma32x32x16(av, bv, acc[j]);
+      }
     }
   };
   // stage s sits in LDS buffer s & 1 while it is multiplied; stage s + 1 is
   // stored into the other buffer after that (its readers, stage s - 1, are
-  // past the barrier), and the freed register set starts loading stage s + 3
+  // past the barrier), and the freed register set starts loading stage
+  // s + 3.  Loads and stores are unconditional (stage numbers clamped to the
+  // last; a store past the last stage lands in a buffer nobody reads again),
+  // so the loop body is straight-line and each store waits only for its own
+  // register set.
+  const int last = stages - 1;
   load(va, 0);
   store(va, 0);
-  if (stages > 1) load(va, 1);
-  if (stages > 2) load(vb, 2);
+  load(va, min(1, last));
+  load(vb, min(2, last));
   __syncthreads();
-  for (int st = 0; st < stages; st += 2) {
+  int st = 0;
+  for (; st + 1 < stages; st += 2) {
     compute(0);
-    if (st + 1 < stages) {
-      store(va, 1);
-      if (st + 3 < stages) load(va, st + 3);
-    }
+    store(va, 1);
+    load(va, min(st + 3, last));
     __syncthreads();
-    if (st + 1 >= stages) break;
     compute(1);
-    if (st + 2 < stages) {
-      store(vb, 0);
-      if (st + 4 < stages) load(vb, st + 4);
-    }
+    store(vb, 0);
+    load(vb, min(st + 4, last));
     __syncthreads();
   }
-  // D lane l, register i: token (i/4)*8 + 4g + i%4 of the wave's tile, expert n32 of tile nt0 + j
-  float* pc = a.part + (int64_t)blockIdx.x * T * N;
+  if (st < stages) compute(0);  // an odd stage count: the last stage is in buffer 0
+  __syncthreads();              // every wave is done with the stage buffers
+  // out: up to four expert tiles (128 columns) at a time through the wave's
+  // own LDS area.  D lane l, register i: token (i/4)*8 + 4g + i%4 of the
+  // wave's tile, expert n32 of the tile
+  uint8_t* ow = &lds[wave * kOutWave];
+  const int ps = a.part_stride;
+  float* pc = a.part + (int64_t)blockIdx.x * T * ps;
+  const int t0 = m0 + 32 * wave;
 #pragma unroll
-  for (int j = 0; j < kTilesPerWave; ++j) {
-    const int n = 32 * (nt0 + j) + n32;
+  for (int p = 0; p < kNT; p += 4) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = m0 + 32 * mt + (i >> 2) * 8 + 4 * g + (i & 3);
-      if (t < T && n < N) pc[(int64_t)t * N + n] = acc[j][i];
+    for (int j = p; j < p + 4 && j < kNT; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *(MLA_LDS float*)&ow[((i >> 2) * 8 + 4 * g + (i & 3)) * kOutRow + 4 * (32 * (j - p) + n32)] = acc[j][i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 32 rows x 128 columns: lane l takes 16-byte piece l % 32 of rows 2q + l / 32
+    const int cols = min(128, ps - 128 * (p / 4));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = 2 * q + (lane >> 5), c = 4 * (lane & 31);
+      const f32x4 v = *(const MLA_LDS f32x4*)&ow[r * kOutRow + 4 * c];
+      if (t0 + r < T && c < cols) *(f32x4*)&pc[(int64_t)(t0 + r) * ps + 128 * (p / 4) + c] = v;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -146,6 +173,10 @@ template __global__ void gate_proj_tall<1>(const GateArgs);
 template __global__ void gate_proj_tall<2>(const GateArgs);
 template __global__ void gate_proj_tall<3>(const GateArgs);
 template __global__ void gate_proj_tall<4>(const GateArgs);
+template __global__ void gate_proj_tall<5>(const GateArgs);
+template __global__ void gate_proj_tall<6>(const GateArgs);
+template __global__ void gate_proj_tall<7>(const GateArgs);
+template __global__ void gate_proj_tall<8>(const GateArgs);
 
 // fp32 inputs: wave w of workgroup x computes expert 4x + w of one token
 // (grid y): its 64 lanes stride along d_model, then a shuffle sum.
@@ -157,13 +188,10 @@ __global__ void __launch_bounds__(256) gate_proj_f32(const GateArgs a) {
   float acc = 0.f;
   for (int k = lane; k < a.d_model; k += 64) acc = fmaf(u[k], e[k], acc);
   acc = wave_sum(acc);
-  if (lane == 0) a.part[(int64_t)r * a.n_experts + n] = acc;
+  if (lane == 0) a.part[(int64_t)r * a.part_stride + n] = acc;
 }
 
 namespace {
-
-// (v, i) ranks before (w, j): larger value, or equal value and lower index.
-__device__ __forceinline__ bool ranks_before(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
 // Lane moves within rows of 16 lanes (every lane has a source in these
 // patterns): swap neighbours, swap pairs, mirror within 8, mirror within 16.
@@ -178,133 +206,169 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(dpp<kCtrl>(__float_as_int(v)));
 }
 
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Every lane receives the maximum / the sum over the wave (fixed order).
-__device__ __forceinline__ float wave_max_dpp(float v) {
+// Every lane of a row of 16 lanes receives the row's maximum / sum (fixed
+// order).
+__device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp<kDppXor1>(v));
   v = fmaxf(v, dpp<kDppXor2>(v));
   v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppMirror>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+  return fmaxf(v, dpp<kDppMirror>(v));
 }
-__device__ __forceinline__ float wave_sum_dpp(float v) {
+__device__ __forceinline__ float row_sum(float v) {
   v += dpp<kDppXor1>(v);
   v += dpp<kDppXor2>(v);
   v += dpp<kDppHalfMirror>(v);
-  v += dpp<kDppMirror>(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+  return v + dpp<kDppMirror>(v);
 }
 
 template <int kCtrl>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = dpp<kCtrl>(v);
-  const int oi = dpp<kCtrl>(i);
-  if (ranks_before(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)dpp<kCtrl>((int)(uint32_t)v), hi = (uint32_t)dpp<kCtrl>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// The row's largest key, returned to every lane of the row.
+__device__ __forceinline__ uint64_t row_max64(uint64_t v) {
+  v = max64(v, dpp64<kDppXor1>(v));
+  v = max64(v, dpp64<kDppXor2>(v));
+  v = max64(v, dpp64<kDppHalfMirror>(v));
+  return max64(v, dpp64<kDppMirror>(v));
 }
 
-// The wave's first-ranked (value, index) pair, returned to every lane.
-__device__ __forceinline__ int wave_argmax(float v, int i) {
-  argmax_step<kDppXor1>(v, i);
-  argmax_step<kDppXor2>(v, i);
-  argmax_step<kDppHalfMirror>(v, i);
-  argmax_step<kDppMirror>(v, i);
-  float bv = lane_f(v, 0);
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) {
-    const float rv = lane_f(v, r);
-    const int ri = __builtin_amdgcn_readlane(i, r);
-    if (ranks_before(rv, ri, bv, bi)) {
-      bv = rv;
-      bi = ri;
-    }
-  }
-  return bi;
+// The same over the whole wave: the four rows' results combined from lanes
+// 0, 16, 32 and 48 (returned to every lane).
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_rows(float v) {
+  v = row_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v = row_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ uint64_t lane64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max64_rows(uint64_t v) {
+  v = row_max64(v);
+  return max64(max64(lane64(v, 0), lane64(v, 16)), max64(lane64(v, 32), lane64(v, 48)));
+}
+
+// A key whose unsigned order is the ranking of (affinity, expert): the
+// affinity's bits made monotone in its value (-0 taken as +0), then the
+// complement of the index, so that of equal affinities the lower index is
+// the larger key.  Every key of a finite affinity exceeds 0.
+__device__ __forceinline__ uint64_t rank_key(float x, int i) {
+  const uint32_t b = __float_as_uint(x + 0.0f);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (0xFFFFFFFFu - (uint32_t)i);
 }
 
 }  // namespace
 
+// kL lanes per token (16: four tokens per wave, one per row; 64: one token
+// per wave); lane j of a token owns the S = 4 * kS4 experts from S * j on
+// (16-byte loads per slice from rows padded to a multiple of 4).
+// Reductions by DPP moves within rows, and for 64 lanes the four rows'
+// results read from one lane each.  Sixteen lanes per token spend fewer
+// instructions per token (many tokens); 64 lanes give each lane fewer
+// experts and so a shorter chain (few tokens).
+template <int kS4, int kL>
 __global__ void __launch_bounds__(256) gate_finish(const GateArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.tokens) return;  // uniform per wave; no barrier in this kernel
-  const int N = a.n_experts;
-  // the slice sums, slice order fixed, sixteen slices' loads for all four
-  // of a lane's experts in flight at a time with no branch between them
-  const int64_t cstride = (int64_t)a.tokens * N;
-  const float* pp = a.part + (int64_t)t * N;
-  float x[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < a.chunks; c0 += 16) {
-    float v[4][16];
+  static_assert(kL == 16 || kL == 64, "a row or a wave per token");
+  constexpr int S = 4 * kS4, kTpw = 64 / kL;
+  const int lane = threadIdx.x & 63, j = lane % kL;
+  const int w0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kTpw;  // the wave's first token
+  if (w0 >= a.tokens) return;  // uniform per wave; no barrier in this kernel
+  const int t = w0 + lane / kL;
+  const int tc = min(t, a.tokens - 1);  // rows past the last token compute on it and write nothing
+  const int N = a.n_experts, ps = a.part_stride;
+  const int e0 = S * j;
+  auto vmax = [](float v) __attribute__((always_inline)) { return kL == 16 ? row_max(v) : wave_max_rows(v); };
+  auto vsum = [](float v) __attribute__((always_inline)) { return kL == 16 ? row_sum(v) : wave_sum_rows(v); };
+  auto kmax = [](uint64_t v) __attribute__((always_inline)) { return kL == 16 ? row_max64(v) : wave_max64_rows(v); };
+  // the slice sums in slice order, eight slices' loads in flight at a time
+  // with no branch between them
+  const int64_t cstride = (int64_t)a.tokens * ps;
+  const float* pp = a.part + (int64_t)tc * ps;
+  f32x4 x[kS4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int n = min(lane + 64 * u, N - 1);
+  for (int q = 0; q < kS4; ++q) x[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.chunks; c0 += 8) {
+    f32x4 v[8][kS4];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[u][k] = pp[min(c0 + k, a.chunks - 1) * cstride + n];
-    }
+    for (int k = 0; k < 8; ++k)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int q = 0; q < kS4; ++q)
+        v[k][q] = *(const f32x4*)(pp + min(c0 + k, a.chunks - 1) * cstride + min(e0 + 4 * q, ps - 4));
 #pragma unroll
-      for (int k = 0; k < 16; ++k) x[u] += c0 + k < a.chunks ? v[u][k] : 0.f;
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int q = 0; q < kS4; ++q)
+        if (c0 + k < a.chunks) x[q] += v[k][q];
   }
-  bool live[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) live[u] = lane + 64 * u < N;
   // softmax over the routed experts
   float m = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (live[u]) m = fmaxf(m, x[u]);
-  m = wave_max_dpp(m);
-  float z[4], zs = 0.f;
+  for (int i = 0; i < S; ++i)
+    if (e0 + i < N) m = fmaxf(m, x[i / 4][i % 4]);
+  m = vmax(m);
+  float sc[S], zs = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    z[u] = live[u] ? expf(x[u] - m) : 0.f;
-    zs += z[u];
+  for (int i = 0; i < S; ++i) {
+    sc[i] = e0 + i < N ? expf(x[i / 4][i % 4] - m) : 0.f;
+    zs += sc[i];
   }
-  zs = wave_sum_dpp(zs);
+  zs = vsum(zs);
   const float inv = 1.0f / zs;
-  float s[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) s[u] = z[u] * inv;
-  if (a.scores) {
+  for (int i = 0; i < S; ++i) sc[i] *= inv;
+  const bool tok = t < a.tokens;
+  if (a.scores && tok) {
     float* so = a.scores + (int64_t)t * N;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (live[u]) so[lane + 64 * u] = s[u];
+    for (int i = 0; i < S; ++i)
+      if (e0 + i < N) so[e0 + i] = sc[i];
   }
-  // top_k rounds: the lane's best remaining expert, then the wave's
-  bool taken[4] = {!live[0], !live[1], !live[2], !live[3]};
+  // top_k rounds: the token's largest key; its owner clears it, writes the
+  // expert and its score, and finds its next largest key
+  uint64_t key[S], best = 0;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    key[i] = e0 + i < N ? rank_key(x[i / 4][i % 4], e0 + i) : 0;
+    best = max64(best, key[i]);
+  }
   for (int k = 0; k < a.top_k; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    const uint64_t r = kmax(best);
+    const int bi = (int)(0xFFFFFFFFu - (uint32_t)r);
+    if (bi - e0 >= 0 && bi - e0 < S) {
+      float w = 0.f;
+      best = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (!taken[u] && ranks_before(x[u], lane + 64 * u, bv, bi)) {
-        bv = x[u];
-        bi = lane + 64 * u;
-      }
-    bi = wave_argmax(bv, bi);
-    // every lane now holds the winner bi; its owner marks it and writes it
-    if ((bi & 63) == lane) {
-      const int u = bi >> 6;
-      float w = s[0];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q == u) {
-          taken[q] = true;
-          w = s[q];
+      for (int i = 0; i < S; ++i) {
+        if (e0 + i == bi) {
+          w = sc[i];
+          key[i] = 0;
         }
-      a.idx[(int64_t)t * a.top_k + k] = bi;
-      a.weight[(int64_t)t * a.top_k + k] = w;
+        best = max64(best, key[i]);
+      }
+      if (tok) {
+        a.idx[(int64_t)t * a.top_k + k] = bi;
+        a.weight[(int64_t)t * a.top_k + k] = w;
+      }
     }
   }
 }
+
+template __global__ void gate_finish<1, 16>(const GateArgs);
+template __global__ void gate_finish<2, 16>(const GateArgs);
+template __global__ void gate_finish<3, 16>(const GateArgs);
+template __global__ void gate_finish<4, 16>(const GateArgs);
+template __global__ void gate_finish<1, 64>(const GateArgs);
 
 }  // namespace mla

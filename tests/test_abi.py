@@ -129,11 +129,16 @@ def test_moe_gate_validation():
     assert n.value == 10 * 32 * 160 * 4
     assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_F32, ctypes.byref(n)) == M.MLA_OK
     assert n.value == 32 * 160 * 4
-    # from 512 tokens on: slices cut for about 512 workgroups of 64 tokens (4096 tokens: 8 slices of 640)
+    # from 768 tokens on: slices cut for about 256 workgroups of 128 tokens (4096 tokens: 8 slices of 640)
     assert L.mla_moe_gate_workspace_size(4096, 5120, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
     assert n.value == 8 * 4096 * 160 * 4
-    assert L.mla_moe_gate_workspace_size(600, 640, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
-    assert n.value == 1 * 600 * 160 * 4
+    # partial rows padded to a multiple of 4 experts
+    assert L.mla_moe_gate_workspace_size(800, 640, 101, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 1 * 800 * 104 * 4
+    assert L.mla_moe_gate_workspace_size(800, 640, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 1 * 800 * 160 * 4
+    assert L.mla_moe_gate_workspace_size(700, 640, 160, M.MLA_BF16, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 2 * 700 * 160 * 4                                 # below 768 tokens: 512-wide slices
     assert L.mla_moe_gate_workspace_size(32, 5120, 257, M.MLA_BF16, ctypes.byref(n)) == M.MLA_ERR_SHAPE
     assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_FP8_E4M3, ctypes.byref(n)) == M.MLA_ERR_DTYPE
     assert L.mla_moe_gate_workspace_size(32, 5120, 160, M.MLA_BF16, None) == M.MLA_ERR_NULL

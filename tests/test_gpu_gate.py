@@ -116,11 +116,14 @@ CASES = {
     "bf16_max": (33, 1024, 256, 16, "bf16"),
     "bf16_one_expert": (5, 64, 1, 1, "bf16"),
     "bf16_keep_all": (9, 192, 24, 16, "bf16"),
-    # from 512 tokens on the tall projection kernel (64 tokens x every expert per workgroup)
-    "bf16_tall_ragged": (600, 640, 160, 6, "bf16"),
-    "bf16_tall_max": (531, 1024, 256, 16, "bf16"),
-    "bf16_tall_few_experts": (517, 5120, 20, 4, "bf16"),
+    # from 768 tokens on the tall projection kernel (128 tokens x every expert per workgroup);
+    # from 2048 tokens on four tokens per wave in the finish
+    "bf16_tall_ragged": (800, 640, 160, 6, "bf16"),
+    "bf16_tall_max": (771, 1024, 256, 16, "bf16"),
+    "bf16_tall_few_experts": (777, 5120, 20, 4, "bf16"),
     "bf16_tall_n100": (1000, 1536, 100, 8, "bf16"),
+    "bf16_rows_n101": (2100, 640, 101, 5, "bf16"),
+    "bf16_rows_n250": (2053, 640, 250, 7, "bf16"),
     "f32_small": (11, 192, 64, 8, "f32"),
     "f32_deepseek": (6, 5120, 160, 6, "f32"),
 }
@@ -140,7 +143,7 @@ def test_gate_vs_oracle(name):
 
 
 @pytest.mark.parametrize("twins", [False, True], ids=["distinct", "twins"])
-@pytest.mark.parametrize("dt,tokens", [("bf16", 40), ("bf16", 576), ("f32", 7)])
+@pytest.mark.parametrize("dt,tokens", [("bf16", 40), ("bf16", 800), ("bf16", 2050), ("f32", 7)])
 def test_gate_one_hot_exact(dt, tokens, twins):
     """Exact affinities: the selection (ties included) equals the oracle's."""
     print(f"[case] gate one-hot {dt} tokens={tokens} twins={twins}", flush=True)
