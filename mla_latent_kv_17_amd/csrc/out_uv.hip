@@ -145,7 +145,15 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
   }
   const int c = tid & 127, r0 = tid >> 7;
   for (int m0 = 0; m0 < a.rows; m0 += 32) {
-    // ---- loads: first chunks' partial rows, then the lse of row m0 + tid / 8
+    // ---- loads: the lse of row m0 + tid / 8 first (unconditional, clamped
+    // indices), then the first chunks' partial rows: the weights wait only
+    // for the former, the partial rows stay in flight meanwhile
+    const int lr = tid >> 3, lj = tid & 7, r = m0 + lr;
+    const float* lp = a.lse_part + prow(min(r, a.rows - 1));
+    float lv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lv[k] = lp[(int64_t)min(lj + 8 * k, ns - 1) * rs];
+    asm volatile("" ::: "memory");  // keep the lse loads ahead of the partial rows
     const float* vrow[16];  // chunk 0 of the thread's rows (clamped to a real row)
 #pragma unroll
     for (int i = 0; i < 16; ++i) vrow[i] = a.o_part + prow(min(m0 + r0 + 2 * i, a.rows - 1)) * 512 + 4 * c;
@@ -156,14 +164,13 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v0[jj][i] = *(const f32x4*)(vrow[i] + so);
     }
-    const int lr = tid >> 3, lj = tid & 7, r = m0 + lr;
-    const float* lp = a.lse_part + prow(min(r, a.rows - 1));
-    float lv[8];
+    // (an empty use of every lse value here keeps its load where it is, ahead
+    // of the partial rows, instead of being moved into the branch below)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int sk = lj + 8 * k;
-      lv[k] = (r < a.rows && sk < ns) ? lp[sk * rs] : -__builtin_inff();
-    }
+    for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(lv[k]));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (!(r < a.rows && lj + 8 * k < ns)) lv[k] = -__builtin_inff();
     // ---- merge weights of row lr (8 lanes per row)
     float m = -__builtin_inff();
 #pragma unroll
@@ -193,20 +200,23 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
       rowinv[lr] = inv;
       if (a.lse && half == 0 && r < a.rows) a.lse[(int64_t)r * a.heads + h] = z > 0.f ? m + logf(z) : -__builtin_inff();
     }
-    __syncthreads();
-    // ---- merged tile in registers; a chunk past the end, or one whose weight
-    // is 0 (it saw no token: its data may be anything), is dropped
+    // LDS-only barrier: the weights are visible, the partial rows' loads stay
+    // in flight (a full barrier would wait for every outstanding load)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // ---- merged tile in registers, chunk by chunk as the rows land; a chunk
+    // past the end, or one whose weight is 0 (it saw no token: its data may
+    // be anything), is dropped
     f32x4 acc[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc[i] = f32x4{};
+    for (int i = 0; i < 16; ++i) acc[i] = f32x4{};
 #pragma unroll
-      for (int jj = 0; jj < kF; ++jj) {
+    for (int jj = 0; jj < kF; ++jj)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
         const float e = jj < ns ? wt[r0 + 2 * i][jj] : 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[i][k] += e > 0.f ? e * v0[jj][i][k] : 0.f;
+        for (int k = 0; k < 4; ++k) acc[i][k] = e > 0.f ? fmaf(e, v0[jj][i][k], acc[i][k]) : acc[i][k];
       }
-    }
     for (int s0 = kF; s0 < ns; s0 += 2) {
       if (s0 % kW == 0) {  // weights of chunks s0 .. s0 + kW - 1 from the rows' max and sum
         __syncthreads();
