@@ -197,6 +197,8 @@ decode_mfma_bf16(const DecodeArgs a) {
   constexpr int kQBase = 2 * kTileBytes;          // queries are staged over tiles 2, 3 (+ P)
   constexpr int kXOff = kBuf * kTileBytes + 2 * kPBytes;
   static_assert(kQBase + 64 * kQStride * 16 <= kXOff, "query staging must fit before the exchange area");
+  constexpr int kORow = 512 * 4 + 16;             // staged output row (epilogue)
+  static_assert(64 * kORow <= kBuf * kTileBytes, "the output staging must fit in the tile ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280];
   MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)&smem[0];
   MLA_LDS uint8_t* const pbuf = tiles + kBuf * kTileBytes;
@@ -625,26 +627,38 @@ decode_mfma_bf16(const DecodeArgs a) {
       wg_barrier();  // new reference
     }
 
-    // ---- epilogue: normalise by the row sums and write this chunk's o_lat
+    // ---- epilogue: normalise by the row sums and stage this chunk's o_lat
+    // in the tile ring (free now: every copy has landed, no tile is read),
+    // rows of 512 fp32 plus 16 bytes of pad
     wg_barrier();  // row sums
-    float* obase = a.o + slot * (int64_t)rows * 512;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int r = nt * 32 + n32;
-      const int row = row_base + r;
       const float lt = xl[r] + xl[64 + r];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* orow = obase + (int64_t)row * 512 + v * 128;
+      MLA_LDS uint8_t* orow = tiles + r * kORow + v * 512;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 o = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
                            oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
-          if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = o;
+          *(MLA_LDS f32x4*)(orow + (mt * 32 + j * 8 + 4 * g) * 4) = o;
         }
-        sched_fence();
       }
+    }
+  }
+  // all eight waves write the staged rows: a wave's store covers 1 KB of a
+  // row (the accumulator layout would write 32 rows x 32 bytes per store)
+  wg_barrier();
+  {
+    float* obase = a.o + slot * (int64_t)rows * 512;
+    const int c16 = tid & 127;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = (tid >> 7) + 4 * k;
+      const f32x4 o = *(const MLA_LDS f32x4*)(tiles + r * kORow + c16 * 16);
+      if (row_base + r < rows) *(f32x4*)(obase + (int64_t)(row_base + r) * 512 + 4 * c16) = o;
     }
   }
 }
@@ -668,6 +682,8 @@ decode_mfma_fp8(const DecodeArgs a) {
   constexpr int kQBase = 2 * kTileBytes;          // queries are staged over tiles 2, 3 (+ P)
   constexpr int kXOff = kBuf * kTileBytes + 2 * kPBytes;
   static_assert(kQBase + 64 * kQStride * 16 <= kXOff, "query staging must fit before the exchange area");
+  constexpr int kORow = 512 * 4 + 16;             // staged output row (epilogue)
+  static_assert(64 * kORow <= kBuf * kTileBytes, "the output staging must fit in the tile ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280 + kBuf * 128];
   MLA_LDS uint8_t* const tiles = (MLA_LDS uint8_t*)&smem[0];
   MLA_LDS uint8_t* const pbuf = tiles + kBuf * kTileBytes;
@@ -1135,26 +1151,38 @@ decode_mfma_fp8(const DecodeArgs a) {
       wg_barrier();  // new reference
     }
 
-    // ---- epilogue: normalise by the row sums and write this chunk's o_lat
+    // ---- epilogue: normalise by the row sums and stage this chunk's o_lat
+    // in the tile ring (free now: every copy has landed, no tile is read),
+    // rows of 512 fp32 plus 16 bytes of pad
     wg_barrier();  // row sums
-    float* obase = a.o + slot * (int64_t)rows * 512;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int r = nt * 32 + n32;
-      const int row = row_base + r;
       const float lt = xl[r] + xl[64 + r];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* orow = obase + (int64_t)row * 512 + v * 128;
+      MLA_LDS uint8_t* orow = tiles + r * kORow + v * 512;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 o = {oacc[mt][nt][4 * j] * inv, oacc[mt][nt][4 * j + 1] * inv,
                            oacc[mt][nt][4 * j + 2] * inv, oacc[mt][nt][4 * j + 3] * inv};
-          if (row < rows) *(f32x4*)(orow + mt * 32 + j * 8 + 4 * g) = o;
+          *(MLA_LDS f32x4*)(orow + (mt * 32 + j * 8 + 4 * g) * 4) = o;
         }
-        sched_fence();
       }
+    }
+  }
+  // all eight waves write the staged rows: a wave's store covers 1 KB of a
+  // row (the accumulator layout would write 32 rows x 32 bytes per store)
+  wg_barrier();
+  {
+    float* obase = a.o + slot * (int64_t)rows * 512;
+    const int c16 = tid & 127;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = (tid >> 7) + 4 * k;
+      const f32x4 o = *(const MLA_LDS f32x4*)(tiles + r * kORow + c16 * 16);
+      if (row_base + r < rows) *(f32x4*)(obase + (int64_t)(row_base + r) * 512 + 4 * c16) = o;
     }
   }
 }
