@@ -25,18 +25,12 @@
 
 namespace mla {
 
-// Zero bytes standing in for cache rows past a sequence's length: their tile
-// rows must hold zeros (not whatever is in memory) because the value product
-// multiplies them by p = 0.
-__device__ __attribute__((aligned(1024))) const uint32_t g_zero_row[256] = {0};
-
 namespace {
 
 constexpr int kTileTok = 32;                    // tokens per LDS tile
 constexpr int kLatBytes = kTileTok * 64 * 16;   // latent part: 32 rows x 64 chunks of 16 B
 constexpr int kRopeBytes = kTileTok * 8 * 16;   // RoPE part:   32 rows x 8 chunks
 constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 36,864
-constexpr int kStageBytes = kTileTok * 512;     // fp8 latent codes of one tile
 constexpr int kRowsPerWg = 64;
 constexpr float kRefSlack = 64.0f;              // log2 headroom above a row's reference max
 
@@ -118,10 +112,6 @@ __device__ __forceinline__ void dma16xy(const void* base, uint32_t lc, uint32_t 
       : "v"(lc), "s"(x16), "v"(lrow), "s"(row), "s"(base), "s"(lds_base)
       : "memory");
 }
-
-// A wait the compiler sees (it updates its own counter model): all vector
-// memory loads issued so far have completed.
-__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Scalar (constant address space) load of a wave-uniform int: tracked by
 // lgkmcnt, so it never waits on the outstanding HBM -> LDS copies.
