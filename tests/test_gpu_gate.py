@@ -124,6 +124,8 @@ CASES = {
     "bf16_tall_n100": (1000, 1536, 100, 8, "bf16"),
     "bf16_rows_n101": (2100, 640, 101, 5, "bf16"),
     "bf16_rows_n250": (2053, 640, 250, 7, "bf16"),
+    "bf16_rows_one_expert": (2050, 128, 1, 1, "bf16"),
+    "bf16_rows_n3": (2049, 192, 3, 2, "bf16"),
     "f32_small": (11, 192, 64, 8, "f32"),
     "f32_deepseek": (6, 5120, 160, 6, "f32"),
 }
