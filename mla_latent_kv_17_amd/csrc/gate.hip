@@ -292,22 +292,24 @@ __global__ void __launch_bounds__(256) gate_finish(const GateArgs a) {
   auto vmax = [](float v) __attribute__((always_inline)) { return kL == 16 ? row_max(v) : wave_max_rows(v); };
   auto vsum = [](float v) __attribute__((always_inline)) { return kL == 16 ? row_sum(v) : wave_sum_rows(v); };
   auto kmax = [](uint64_t v) __attribute__((always_inline)) { return kL == 16 ? row_max64(v) : wave_max64_rows(v); };
-  // the slice sums in slice order, eight slices' loads in flight at a time
-  // with no branch between them
+  // the slice sums in slice order, kRound slices' loads in flight at a time
+  // with no branch between them (16 with one run of 4 experts per lane: a
+  // 5120-wide d_model in one round of loads)
+  constexpr int kRound = kS4 == 1 ? 16 : 8;
   const int64_t cstride = (int64_t)a.tokens * ps;
   const float* pp = a.part + (int64_t)tc * ps;
   f32x4 x[kS4];
 #pragma unroll
   for (int q = 0; q < kS4; ++q) x[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < a.chunks; c0 += 8) {
-    f32x4 v[8][kS4];
+  for (int c0 = 0; c0 < a.chunks; c0 += kRound) {
+    f32x4 v[kRound][kS4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < kRound; ++k)
 #pragma unroll
       for (int q = 0; q < kS4; ++q)
         v[k][q] = *(const f32x4*)(pp + min(c0 + k, a.chunks - 1) * cstride + min(e0 + 4 * q, ps - 4));
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < kRound; ++k)
 #pragma unroll
       for (int q = 0; q < kS4; ++q)
         if (c0 + k < a.chunks) x[q] += v[k][q];
