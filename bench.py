@@ -198,8 +198,8 @@ def main():
                     help="total size of the cache copies the decode timing rotates over")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(batch sharding needs no exchange and is described in the design notes)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (the decode shards by "
+              f"sequence with no exchange between GPUs, so the one-GPU rate is the per-GPU rate)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

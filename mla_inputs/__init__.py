@@ -9,8 +9,9 @@ and the HIP path can use it without sharing any of the method.
 Shapes follow the DeepSeek-V2 explainer (deepforge "DeepSeek-V2", section 1,
 "Store a latent, rebuild the keys and values"): per token per layer the cache
 holds a 512-wide latent c_t plus a 64-wide decoupled RoPE key k^R_t; heads are
-128 wide.  The five workloads below are the synthetic configurations the build
-is measured on; their value distributions are stated in each docstring field.
+128 wide.  The five workloads below are the synthetic configurations the
+library is measured on; their value distributions are stated in each docstring
+field.
 
 Storage formats (all little-endian, row-major):
 
