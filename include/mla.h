@@ -251,7 +251,7 @@ int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64
  *         F32), 16-byte aligned
  * idx:    [tokens][top_k] int32; weight: [tokens][top_k] fp32;
  *         scores: [tokens][n_experts] fp32 or NULL; caller-owned device memory
- * tokens: 0 .. 2097152 (fp32 inputs: 0 .. 65535); 0 launches nothing, and then
+ * tokens: 0 .. 2097120 (fp32 inputs: 0 .. 65535); 0 launches nothing, and then
  *         the pointers are not read (NULL allowed) once the sizes are valid
  * d_model: a multiple of 64, 64 .. 65536; n_experts: 1 .. 256;
  * top_k: 1 .. min(n_experts, 16)

@@ -158,6 +158,7 @@ def test_moe_gate_validation():
     assert call(K=5, N=4) == M.MLA_ERR_SHAPE
     assert call(T=-1) == M.MLA_ERR_SHAPE
     assert call(T=65536, dt=M.MLA_F32) == M.MLA_ERR_SHAPE
+    assert call(T=65535 * 32 + 1) == M.MLA_ERR_SHAPE                   # the largest bf16 token count is 2097120
     assert call(dt=M.MLA_FP8_E4M3) == M.MLA_ERR_DTYPE
     assert call(u=0x1008) == M.MLA_ERR_ALIGN
     assert call(w=0x4002) == M.MLA_ERR_ALIGN
