@@ -41,7 +41,11 @@
  *    outside [0, num_blocks); MLA_ERR_DEVICE if the copy fails.
  *  - Supported sizes: d_latent = 512, d_rope = 64, d_head = 128,
  *    block_size = 64, 1 <= q_per_seq <= MLA_MAX_Q_PER_SEQ; anything else is
- *    MLA_ERR_SHAPE.
+ *    MLA_ERR_SHAPE.  The fp32 paths launch one grid row per query row, so
+ *    there batch * q_per_seq is at most 65535 (mla_absorb_q, mla_out_uv and
+ *    mla_combine_out_uv with F32 data, mla_cache_append with an F32 cache);
+ *    mla_cache_append with bf16 inputs takes up to 65535 * 32 new tokens.
+ *    Larger calls return MLA_ERR_SHAPE.
  *  - Thread-safe: the library holds no mutable global state.
  */
 #ifndef MLA_H_
