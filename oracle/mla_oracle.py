@@ -67,7 +67,7 @@ __all__ = [
     "decode_bf16", "decode_e4m3", "decode_f32",
     "gather_sequence", "reconstruct_keys", "reconstruct_values", "query_vector",
     "visible_tokens", "scores", "softmax_lse", "mix_values",
-    "explicit_decode", "absorbed_decode", "split_ranges", "split_partials",
+    "explicit_decode", "absorbed_decode", "absorbed_decode_batched", "split_ranges", "split_partials",
     "combine_partials", "cache_numbers_per_token_layer", "cache_bytes",
     "default_softmax_scale", "absorb_queries", "project_output",
     "down_project", "rope_angles", "rope_rotate", "e4m3_values", "e4m3_round_codes",
@@ -94,14 +94,16 @@ def decode_f32(x: np.ndarray) -> np.ndarray:
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     """OCP E4M3FN bytes -> float64, from the format definition: sign bit 7,
     4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
-    subnormals m * 2^-9; 0x7F / 0xFF are NaN; there are no infinities."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    subnormals m * 2^-9; 0x7F / 0xFF are NaN; there are no infinities.  The
+    definition is evaluated once on the 256 byte values, which the codes then
+    index (a large cache decodes in one gather)."""
+    c = np.arange(256, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
     mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
     mag = np.where((e == 0xF) & (c & 0x7 == 0x7), np.nan, mag)
-    return sign * mag
+    return (sign * mag)[np.asarray(codes, dtype=np.uint8)]
 
 
 def _decoder(kind: str):
@@ -255,6 +257,54 @@ def absorbed_decode(inp, select=None, softmax_scale: Optional[float] = None):
                 q_lat[r, h], o_lat[r, h], lse[r, h] = ql, ol, l
                 o[r, h] = w_uv @ ol
     return q_lat, o_lat, lse, o
+
+
+def absorbed_decode_batched(inp, softmax_scale: Optional[float] = None, batches: Optional[Iterable[int]] = None):
+    """The absorbed form again, with every (query token, head) row of one
+    sequence in a single matrix product.  All heads read the same cached rows
+    ([DF-latent]: one c_t and one k^R_t per token), so the scores of the
+    sequence are the [len x S_q*H] product [C | K^R] [q_lat | q_rope]^T times
+    the scale; column (i, h) keeps its first len - (S_q - 1 - i) tokens; the
+    softmax runs down each column (max subtracted); o_lat = P^T C and
+    o[i][h] = W_UV[h] o_lat[i][h].  No blocking along the tokens.  It gives
+    every output of a full-size workload in seconds, so that a whole output
+    can be compared element by element.
+
+    Returns (o_lat [B*S_q][H][512], lse [B*S_q][H], o [B*S_q][H][128]) in
+    fp64; a column that sees no token gets o_lat = o = 0 and lse = -inf.  With
+    `batches`, only those sequences are computed (the other rows are NaN)."""
+    wl = inp.wl
+    B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
+    scale = inp.softmax_scale if softmax_scale is None else softmax_scale
+    dq = _decoder(wl.q_dtype)
+    dw = _decoder(wl.w_dtype)
+    w_uk = dw(inp.w_uk)                         # [H][128][512]
+    w_uv_t = dw(inp.w_uv).transpose(0, 2, 1)    # [H][512][128]
+    o_lat = np.full((B * Sq, H, D_LATENT), np.nan)
+    o = np.full((B * Sq, H, D_HEAD), np.nan)
+    lse = np.full((B * Sq, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        C, KR = gather_sequence(inp, b)
+        n = C.shape[0]
+        r0 = b * Sq
+        # q_lat[i][h] = W_UK[h]^T q_nope[i][h], as a batch over heads
+        qn = dq(inp.q_nope[r0:r0 + Sq]).transpose(1, 0, 2)          # [H][Sq][128]
+        ql = np.matmul(qn, w_uk).transpose(1, 0, 2).reshape(Sq * H, D_LATENT)
+        qr = dq(inp.q_rope[r0:r0 + Sq]).reshape(Sq * H, D_ROPE)
+        S = (C @ ql.T + KR @ qr.T) * scale                           # [n][Sq*H], column i*H + h
+        vis = np.repeat([visible_tokens(n, Sq, i) for i in range(Sq)], H)
+        S[np.arange(n)[:, None] >= vis[None, :]] = -np.inf
+        seen = vis > 0
+        m = np.where(seen, S.max(axis=0, initial=-np.inf), 0.0)
+        E = np.exp(S - m)
+        z = E.sum(axis=0)
+        P = E / np.where(seen, z, 1.0)
+        ol = P.T @ C                                                 # [Sq*H][512]
+        o_lat[r0:r0 + Sq] = ol.reshape(Sq, H, D_LATENT)
+        lse[r0:r0 + Sq] = np.where(seen, m + np.log(np.where(seen, z, 1.0)), -np.inf).reshape(Sq, H)
+        oo = np.matmul(ol.reshape(Sq, H, D_LATENT).transpose(1, 0, 2), w_uv_t)  # [H][Sq][128]
+        o[r0:r0 + Sq] = oo.transpose(1, 0, 2)
+    return o_lat, lse, o
 
 
 def absorb_queries(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:

@@ -268,6 +268,52 @@ def check_absorbed_equals_explicit(inp, select=None, tol=1e-12):
     assert np.max(np.abs(lse_a[m] - lse[m])) <= tol * max(1.0, np.abs(lse[m]).max())
 
 
+def check_batched_equals_explicit(inp, tol=1e-12):
+    """The batched absorbed form (every head and query token of a sequence in
+    one product) against the explicit definition: the same o and lse to
+    rounding; rows that see no token give o = o_lat = 0 and lse = -inf in
+    both."""
+    o, lse = O.explicit_decode(inp)
+    ol_b, lse_b, o_b = O.absorbed_decode_batched(inp)
+    seen = np.isfinite(lse)
+    assert np.array_equal(np.isneginf(lse_b), np.isneginf(lse))
+    assert not np.isnan(o_b).any() and not np.isnan(lse_b).any()
+    if seen.any():
+        assert rel_l2(o_b[seen], o[seen]) <= tol, rel_l2(o_b[seen], o[seen])
+        assert np.max(np.abs(lse_b[seen] - lse[seen])) <= tol * max(1.0, np.abs(lse[seen]).max())
+    assert (o_b[~seen] == 0).all() and (ol_b[~seen] == 0).all()
+    return ol_b
+
+
+def check_batched_absorbed():
+    """Batched absorbed form on paged inputs with three causal query tokens
+    and three heads (so a mix-up of the query and head axes shows), a
+    sequence shorter than S_q, an empty one and a page-aligned one; its
+    latent output equals the per-row absorbed form's, and with one head and
+    one query it reduces to the textbook softmax attention of a single row
+    written out by hand."""
+    inp = tiny_inputs([150, 2, 0, 64], heads=3, q_per_seq=3, seed=21)
+    ol_b = check_batched_equals_explicit(inp)
+    _, ol_a, lse_a, _ = O.absorbed_decode(inp)
+    seen = np.isfinite(lse_a)
+    assert rel_l2(ol_b[seen], ol_a[seen]) <= 1e-12
+    # one row by hand: s_t = (q_lat . c_t + q_rope . k^R_t) * scale
+    one = tiny_inputs([5], heads=1, q_per_seq=1, seed=22)
+    ol1, lse1, o1 = O.absorbed_decode_batched(one)
+    rows = one.latent[one.block_table[0, 0], :5].astype(np.float64)
+    ql = one.w_uk[0].astype(np.float64).T @ one.q_nope[0, 0].astype(np.float64)
+    s = [(sum(ql[j] * rows[t, j] for j in range(DL)) +
+          sum(float(one.q_rope[0, 0, j]) * rows[t, DL + j] for j in range(DR))) * one.softmax_scale
+         for t in range(5)]
+    w = [math.exp(x - max(s)) for x in s]
+    p = [x / sum(w) for x in w]
+    assert abs(lse1[0, 0] - (max(s) + math.log(sum(w)))) <= 1e-12
+    want = [sum(p[t] * rows[t, j] for t in range(5)) for j in range(DL)]
+    assert np.max(np.abs(ol1[0, 0] - np.array(want))) <= 1e-12
+    w_uv = one.w_uv[0].astype(np.float64)
+    assert np.max(np.abs(o1[0, 0] - w_uv @ np.array(want))) <= 1e-12
+
+
 def check_paging_invariance():
     inp = tiny_inputs([70, 200, 5], heads=2, seed=8, permute=True)
     flat = tiny_inputs([70, 200, 5], heads=2, seed=8, permute=True)
@@ -536,4 +582,5 @@ ALL_CHECKS = [check_cache_arithmetic, check_decode_tables, check_softmax,
               check_paging_invariance, check_causal_two_tokens, check_split_combine,
               check_absorb_project_identities, check_append_projection, check_rope,
               check_e4m3_encoding, check_fp8_row, check_append_positions,
-              check_gate_worked_example, check_gate_softmax, check_gate_top_k, check_gate_deepseek_shape]
+              check_gate_worked_example, check_gate_softmax, check_gate_top_k, check_gate_deepseek_shape,
+              check_batched_absorbed]

@@ -76,7 +76,21 @@ MULTI = {
                                                            len_range=None, seed=2203),
     "fp32_sq3": MI.small_variants()["fp32_b1_h16_t1k"].scaled(name="fp32_sq3", q_per_seq=3, seq_len=130,
                                                               seed=2204),
+    # the top of the supported range (MLA_MAX_Q_PER_SEQ = 128): a sequence
+    # shorter than S_q, splits on both sides of the fused-merge limit (8)
+    "bf16_sq128_split3": MI.small_variants()["bf16_small_paged"].scaled(
+        name="bf16_sq128_split3", q_per_seq=128, heads=16, batch=3, lens=(100, 300, 700), len_range=None,
+        num_splits=3, seed=2205),
+    "bf16_sq128_h128_split12": MI.small_variants()["bf16_small_paged"].scaled(
+        name="bf16_sq128_h128_split12", q_per_seq=128, heads=128, batch=2, lens=(90, 1500), len_range=None,
+        num_splits=12, seed=2206),
+    "fp8_sq65_split2": MI.small_variants()["fp8_small_sq2"].scaled(
+        name="fp8_sq65_split2", q_per_seq=65, heads=8, batch=4, lens=(40, 64, 65, 300), len_range=None,
+        num_splits=2, seed=2207),
 }
+# cases with many rows: the batched absorbed form of the oracle (pinned to
+# the explicit definition on the CPU) computes every row
+MULTI_BATCHED = {"bf16_sq128_h128_split12"}
 
 
 @pytest.mark.parametrize("name", list(MULTI))
@@ -84,7 +98,10 @@ def test_multi_token_vs_oracle(name):
     wl = MULTI[name]
     inp = MI.generate(wl)
     out, o_lat, lse, _ = run_gpu(inp)
-    o_ref, lse_ref = O.explicit_decode(inp)
+    if name in MULTI_BATCHED:
+        _, lse_ref, o_ref = O.absorbed_decode_batched(inp)
+    else:
+        o_ref, lse_ref = O.explicit_decode(inp)
     check(f"{name}/o", out, o_ref, wl.cache_dtype)
     none = np.isneginf(lse_ref)
     assert np.array_equal(np.isneginf(lse), none)

@@ -1,7 +1,9 @@
 """Plant plausible mistakes in the oracle (on the CPU) and require that the
 pin checks catch each one.  This shows the pins constrain every step: a
 dropped term, a wrong scale, an off-by-one mask, a wrong index or operand."""
+import inspect
 import math
+import textwrap
 
 import numpy as np
 import pytest
@@ -249,7 +251,35 @@ def _gate_dense_keeps_all(u, e, k):
     return M.gate_softmax(M.expert_affinities(u, e))
 
 
+def _mutated(name, label, old, new):
+    """A copy of oracle function `name` with one piece of its source replaced."""
+    src = textwrap.dedent(inspect.getsource(_orig[name]))
+    assert src.count(old) == 1, (name, old)
+    ns = dict(vars(M))
+    exec(compile(src.replace(old, new), f"<{label}>", "exec"), ns)
+    f = ns[name]
+    f.__name__ = label
+    return f
+
+
+_BATCHED_MUTANTS = [
+    _mutated("absorbed_decode_batched", "_batched_causal_reversed",
+             "visible_tokens(n, Sq, i) for i in range(Sq)", "visible_tokens(n, Sq, Sq - 1 - i) for i in range(Sq)"),
+    _mutated("absorbed_decode_batched", "_batched_query_head_axes_swapped",
+             "o_lat[r0:r0 + Sq] = ol.reshape(Sq, H, D_LATENT)",
+             "o_lat[r0:r0 + Sq] = ol.reshape(H, Sq, D_LATENT).transpose(1, 0, 2)"),
+    _mutated("absorbed_decode_batched", "_batched_rope_unscaled",
+             "S = (C @ ql.T + KR @ qr.T) * scale", "S = C @ ql.T * scale + KR @ qr.T"),
+    _mutated("absorbed_decode_batched", "_batched_wrong_head_weight",
+             "w_uv_t = dw(inp.w_uv).transpose(0, 2, 1)", "w_uv_t = dw(inp.w_uv)[::-1].transpose(0, 2, 1)"),
+    _mutated("absorbed_decode_batched", "_batched_lse_missing_max",
+             "m + np.log(np.where(seen, z, 1.0))", "np.log(np.where(seen, z, 1.0))"),
+    _mutated("absorbed_decode_batched", "_batched_mask_off_by_one",
+             "np.arange(n)[:, None] >= vis[None, :]", "np.arange(n)[:, None] > vis[None, :]"),
+]
+
 MUTANTS = {
+    "absorbed_decode_batched": _BATCHED_MUTANTS,
     "down_project": [_down_project_drops_last],
     "rope_rotate": [_rope_half_split, _rope_wrong_sign],
     "rope_angles": [_rope_angles_full_width],

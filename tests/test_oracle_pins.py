@@ -4,7 +4,7 @@ import pytest
 
 import mla_inputs as MI
 import oracle as O
-from oracle_pins import (ALL_CHECKS, check_absorbed_equals_explicit, rel_l2)
+from oracle_pins import (ALL_CHECKS, check_absorbed_equals_explicit, check_batched_equals_explicit, rel_l2)
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -16,6 +16,25 @@ def test_pin(check):
 def test_absorbed_equals_explicit_small(name):
     inp = MI.generate(MI.small_variants()[name])
     check_absorbed_equals_explicit(inp)
+
+
+@pytest.mark.parametrize("name", list(MI.small_variants()))
+def test_batched_equals_explicit_small(name):
+    inp = MI.generate(MI.small_variants()[name])
+    check_batched_equals_explicit(inp)
+
+
+def test_batched_equals_explicit_headline_sampled():
+    """Headline shape (H=128, T=4096): the batched form's rows equal the
+    explicit form's on sampled heads of both sequences."""
+    wl = MI.WORKLOADS[MI.HEADLINE].scaled(batch=2)
+    inp = MI.generate(wl)
+    sel = [(0, 0, 0), (0, 0, 64), (1, 0, 77), (1, 0, 127)]
+    o, lse = O.explicit_decode(inp, select=sel)
+    _, lse_b, o_b = O.absorbed_decode_batched(inp)
+    m = ~np.isnan(lse)
+    assert rel_l2(o_b[m], o[m]) <= 1e-12
+    assert np.max(np.abs(lse_b[m] - lse[m])) <= 1e-12 * np.abs(lse[m]).max()
 
 
 def test_absorbed_equals_explicit_headline_sampled():
