@@ -59,8 +59,9 @@ extern "C" {
 
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
  * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append;
- * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2); 7: adds mla_moe_gate */
-#define MLA_ABI_VERSION 7
+ * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2); 7: adds mla_moe_gate;
+ * 8: adds mla_source_hash */
+#define MLA_ABI_VERSION 8
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -139,6 +140,11 @@ const char* mla_status_str(int status);
 
 /* MLA_ABI_VERSION of the built library. */
 int mla_abi_version(void);
+
+/* 16 lowercase hex digits identifying the sources the library was built from
+ * (a hash over its kernel and header files, static storage).  Lets a caller
+ * refuse a library built from other sources than the ones it expects. */
+const char* mla_source_hash(void);
 
 /* Query absorption (formula box "MLA: compress once, reconstruct in attention":
  * k = W_UK c, folded into the query side):

@@ -26,7 +26,7 @@ MLA_MAX_Q_PER_SEQ = 128
 D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 
 # the C entry points this binding exposes (also checked by the tests)
-EXPORTS = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_decode",
+EXPORTS = ["mla_status_str", "mla_abi_version", "mla_source_hash", "mla_absorb_q", "mla_decode",
            "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits",
            "mla_cache_append", "mla_cache_append_workspace_size", "mla_moe_gate",
            "mla_moe_gate_workspace_size"]
@@ -82,6 +82,7 @@ def _load():
     sig = {
         "mla_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "mla_abi_version": ([], ctypes.c_int),
+        "mla_source_hash": ([], ctypes.c_char_p),
         "mla_absorb_q": ([dp, vp, vp, i32, vp, i32, vp], ctypes.c_int),
         "mla_decode": ([dp, vp, vp, i32, kvp, i32, f32p, f32p, vp], ctypes.c_int),
         "mla_split_combine": ([dp, i32, f32p, f32p, f32p, f32p, vp], ctypes.c_int),
@@ -97,7 +98,22 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    # a library built from other sources than the ones beside it is refused
+    built, want = lib.mla_source_hash().decode(), _build_script().source_hash()
+    if built != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources (hash {built}, sources {want}); "
+                          f"rebuild with `python mla_latent_kv_17_amd/build.py`")
     return lib
+
+
+def _build_script():
+    """build.py, loaded by path (it holds the source hash; importing it as a
+    submodule would import this package first)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_mla_build", os.path.join(_HERE, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 _lib = _load()
@@ -109,6 +125,11 @@ def status_str(status: int) -> str:
 
 def abi_version() -> int:
     return int(_lib.mla_abi_version())
+
+
+def source_hash() -> str:
+    """Hash of the sources the loaded library was built from."""
+    return _lib.mla_source_hash().decode()
 
 
 def _check(fn: str, status: int):

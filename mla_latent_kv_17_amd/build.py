@@ -6,10 +6,14 @@
 
 Each kernel source is compiled to an object with hipcc, then linked into
 ``mla_latent_kv_17_amd/libmla.so``.  Always rebuilds (the sources are small).
+The hash of the sources (``source_hash()``) is compiled into the library,
+which reports it through ``mla_source_hash()``: the binding refuses a library
+built from other sources than the ones beside it.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -31,6 +35,33 @@ FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over every kernel and header source
+    the library is built from (csrc/*.hip, csrc/*.h, include/*.h), by name
+    and content."""
+    h = hashlib.sha256()
+    files = []
+    for d, exts in ((CSRC, (".hip", ".h")), (os.path.join(ROOT, "include"), (".h",))):
+        files += sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(exts))
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
+def built_hash(lib: str = LIB) -> str | None:
+    """The source hash compiled into a built library (read from the file, so
+    the library need not be loaded), or None."""
+    if not os.path.exists(lib):
+        return None
+    with open(lib, "rb") as fh:
+        data = fh.read()
+    i = data.find(b"mla-source-hash:")
+    return data[i + 16:i + 32].decode("ascii", "replace") if i >= 0 else None
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -46,10 +77,11 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    stamp = f'-DMLA_SOURCE_HASH="{source_hash()}"'
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append(([HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        jobs.append(([HIPCC, *FLAGS, stamp, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj], obj))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
     tmp = LIB + ".tmp"

@@ -102,6 +102,16 @@ const char* mla_status_str(int status) {
 
 int mla_abi_version(void) { return MLA_ABI_VERSION; }
 
+// The build passes the hash of the sources; the prefix lets a build check
+// find it in the library file without loading it.
+#ifndef MLA_SOURCE_HASH
+#define MLA_SOURCE_HASH "0000000000000000"
+#endif
+static const char kSourceHash[] = "mla-source-hash:" MLA_SOURCE_HASH;
+static_assert(sizeof(kSourceHash) == 16 + 16 + 1, "the source hash is 16 hex digits");
+
+const char* mla_source_hash(void) { return kSourceHash + 16; }
+
 int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int32_t in_dtype,
                  void* q_lat, int32_t q_lat_dtype, void* stream) {
   int st = check_dims(dims);
@@ -288,12 +298,18 @@ int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64
   return MLA_OK;
 }
 
-int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
-                     int32_t in_dtype, float rope_theta, const mla_paged_kv* kv, void* workspace,
-                     int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The body of mla_cache_append: with `workspace` NULL it validates only and
+// stores the partial-sum bytes the call needs in *need (launching nothing).
+int cache_append_impl(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                      int32_t in_dtype, float rope_theta, const mla_paged_kv* kv, void* workspace,
+                      int64_t workspace_bytes, int64_t* need, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
-  if (!kv || !h || !w_dkv || !w_kr || !workspace) return MLA_ERR_NULL;
+  if (!kv || !h || !w_dkv || !w_kr || (!workspace && !need)) return MLA_ERR_NULL;
   if (!kv->latent || !kv->rope || !kv->block_table || !kv->seq_lens) return MLA_ERR_NULL;
   if (d_model < 64 || d_model > 65536 || d_model % 64) return MLA_ERR_SHAPE;
   if (!(rope_theta > 0.f) || !isfinite(rope_theta)) return MLA_ERR_SHAPE;
@@ -311,8 +327,12 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
     return MLA_ERR_SHAPE;
   if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(workspace)) return MLA_ERR_ALIGN;
   const int tokens = dims->batch * dims->q_per_seq;
-  if (tokens == 0) return MLA_OK;
   const int chunks = fmt == 0 ? 1 : append_chunks(d_model);
+  if (!workspace) {
+    *need = (int64_t)chunks * tokens * mla::kAppendCols * 4;
+    return MLA_OK;
+  }
+  if (tokens == 0) return MLA_OK;
   if (workspace_bytes < (int64_t)chunks * tokens * mla::kAppendCols * 4) return MLA_ERR_SHAPE;
   if (check_mode()) {
     st = check_paging(dims->batch, kv, (hipStream_t)stream);
@@ -358,6 +378,18 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
   else
     st = launch("mla::append_finish<fp8>", (const void*)mla::append_finish<2>, dim3(tokens), dim3(256), a, s);
   return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                     int32_t in_dtype, float rope_theta, const mla_paged_kv* kv, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+  if (!workspace) return MLA_ERR_NULL;
+  return cache_append_impl(dims, d_model, h, w_dkv, w_kr, in_dtype, rope_theta, kv, workspace, workspace_bytes,
+                           nullptr, stream);
 }
 
 namespace {

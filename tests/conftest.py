@@ -11,13 +11,15 @@ def pytest_configure(config):
 
 
 def _ensure_built():
-    """Build the HIP library in-tree when nothing is built yet."""
-    lib = os.path.join(ROOT, "mla_latent_kv_17_amd", "libmla.so")
-    if not os.path.exists(lib):
-        import importlib.util  # by path: importing the package needs the library
-        spec = importlib.util.spec_from_file_location("_mla_build", os.path.join(ROOT, "mla_latent_kv_17_amd", "build.py"))
-        mod = importlib.util.module_from_spec(spec)
-        spec.loader.exec_module(mod)
+    """Build the HIP library in-tree when nothing is built yet, or when the
+    built one carries the hash of other sources than the ones checked out (so
+    the tests never run a stale binary)."""
+    import importlib.util  # by path: importing the package needs the library
+    spec = importlib.util.spec_from_file_location("_mla_build", os.path.join(ROOT, "mla_latent_kv_17_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    if mod.built_hash() != mod.source_hash():
+        print(f"conftest: building {mod.LIB} (built {mod.built_hash()}, sources {mod.source_hash()})", flush=True)
         mod.build()
 
 

@@ -20,15 +20,25 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 13, syms
     lib = ctypes.CDLL(M.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
     assert sorted(M.EXPORTS) == syms
 
 
+def test_source_hash_matches_the_sources():
+    """The loaded library was built from the sources in the tree."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_mla_build", os.path.join(os.path.dirname(M.LIB_PATH), "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert re.fullmatch(r"[0-9a-f]{16}", M.source_hash())
+    assert M.source_hash() == mod.source_hash() == mod.built_hash()
+
+
 def test_version_and_status_strings():
-    assert M.abi_version() == 7
+    assert M.abi_version() == 8
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -119,7 +129,6 @@ def test_cache_append_validation():
     assert call(kv=_kv(bs=32)) == M.MLA_ERR_SHAPE
     assert L.mla_cache_append(ctypes.byref(M.make_dims(0, 1, 128)), 640, 0x1000, 0x2000, 0x3000, M.MLA_BF16,
                               10000.0, ctypes.byref(_kv()), 0x9000, 0, None) == M.MLA_OK  # nothing to do
-
 
 
 def test_moe_gate_validation():

@@ -24,6 +24,21 @@ def test_binding_fails_loudly_without_library(tmp_path):
     assert "ImportError" in r.stderr and "is not built" in r.stderr, r.stderr[-2000:]
 
 
+def test_binding_refuses_a_stale_library(tmp_path):
+    """A library built from other sources than the ones beside it (here: one
+    kernel source changed after the build) is refused at import."""
+    copy = tmp_path / "mla_latent_kv_17_amd"
+    shutil.copytree(PKG, copy, ignore=shutil.ignore_patterns("_build", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    with open(copy / "csrc" / "combine.hip", "a") as fh:
+        fh.write("\n// changed after the build\n")
+    env = dict(os.environ, PYTHONPATH=str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", "import mla_latent_kv_17_amd"], cwd=tmp_path, env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "built from other sources" in r.stderr, r.stderr[-2000:]
+
+
 def test_product_sources_never_import_the_oracle():
     pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle[\s.])", re.M)
     for dirpath, _, files in os.walk(PKG):
