@@ -46,7 +46,9 @@
  *    mla_combine_out_uv with F32 data, mla_cache_append with an F32 cache);
  *    mla_cache_append with bf16 inputs takes up to 65535 * 32 new tokens.
  *    Larger calls return MLA_ERR_SHAPE.
- *  - Thread-safe: the library holds no mutable global state.
+ *  - Thread-safe.  The library holds no mutable global state, with one
+ *    exception: mla_cache_append_static keeps a fixed device array per GPU
+ *    (its scratch) and that array's device address per device.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -60,8 +62,8 @@ extern "C" {
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
  * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append;
  * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2); 7: adds mla_moe_gate;
- * 8: adds mla_source_hash */
-#define MLA_ABI_VERSION 8
+ * 8: adds mla_source_hash; 9: adds mla_cache_append_static and MLA_ERR_SCRATCH */
+#define MLA_ABI_VERSION 9
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -77,7 +79,8 @@ typedef enum mla_status {
   MLA_ERR_ALIGN = -4,  /* a pointer or stride breaks the 16-byte alignment   */
   MLA_ERR_SPLITS = -5, /* num_splits < 1 or > MLA_MAX_SPLITS                 */
   MLA_ERR_LAUNCH = -6, /* the HIP runtime refused the launch                 */
-  MLA_ERR_DEVICE = -7  /* no usable gfx950 device is current                 */
+  MLA_ERR_DEVICE = -7, /* no usable gfx950 device is current                */
+  MLA_ERR_SCRATCH = -8 /* the call needs more than the static scratch holds  */
 } mla_status;
 
 #define MLA_MAX_SPLITS 1024
@@ -242,6 +245,28 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
 
 /* Bytes of workspace mla_cache_append needs for these sizes (host-only). */
 int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64_t* bytes);
+
+/* Device bytes of the scratch array mla_cache_append_static uses on each GPU. */
+#define MLA_STATIC_SCRATCH_BYTES (16 << 20)
+
+/* mla_cache_append for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments, kernels and results as mla_cache_append
+ * (bit-identical cache contents), with the fp32 partial sums kept in a fixed
+ * array of MLA_STATIC_SCRATCH_BYTES that the library holds on each GPU from
+ * its first call there until the process ends, instead of a workspace.
+ * No device memory is allocated or freed by the call.
+ * The partial sums need mla_cache_append_workspace_size() bytes; a call that
+ * needs more than MLA_STATIC_SCRATCH_BYTES (at d_model 5120: more than 728
+ * new tokens) returns MLA_ERR_SCRATCH and enqueues nothing.
+ * Every call on one GPU shares that GPU's array (each call overwrites every
+ * byte it reads before reading it): calls whose work overlaps on one GPU --
+ * on different streams, or from different threads without ordering -- race
+ * and give undefined results; calls ordered on one stream are safe.
+ * MLA_ERR_DEVICE if the array's device address cannot be obtained. */
+int mla_cache_append_static(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv,
+                            const void* w_kr, int32_t in_dtype, float rope_theta, const mla_paged_kv* kv,
+                            void* stream);
 
 /* MoE gate: the routed experts each token uses and their gate values
  * (deepforge.srivtx.xyz "DeepSeek-V2", section 1, "Make the feed-forward

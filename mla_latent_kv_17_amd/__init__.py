@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 MLA_OK = 0
 MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_ALIGN = -1, -2, -3, -4
-MLA_ERR_SPLITS, MLA_ERR_LAUNCH, MLA_ERR_DEVICE = -5, -6, -7
+MLA_ERR_SPLITS, MLA_ERR_LAUNCH, MLA_ERR_DEVICE, MLA_ERR_SCRATCH = -5, -6, -7, -8
+MLA_STATIC_SCRATCH_BYTES = 16 << 20
 MLA_MAX_SPLITS = 1024
 MLA_MAX_Q_PER_SEQ = 128
 D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
@@ -28,7 +29,7 @@ D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 # the C entry points this binding exposes (also checked by the tests)
 EXPORTS = ["mla_status_str", "mla_abi_version", "mla_source_hash", "mla_absorb_q", "mla_decode",
            "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits",
-           "mla_cache_append", "mla_cache_append_workspace_size", "mla_moe_gate",
+           "mla_cache_append", "mla_cache_append_workspace_size", "mla_cache_append_static", "mla_moe_gate",
            "mla_moe_gate_workspace_size"]
 MLA_GATE_MAX_EXPERTS, MLA_GATE_MAX_TOP_K = 256, 16
 
@@ -91,6 +92,7 @@ def _load():
         "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
         "mla_cache_append": ([dp, i32, vp, vp, vp, i32, ctypes.c_float, kvp, vp, ctypes.c_int64, vp], ctypes.c_int),
         "mla_cache_append_workspace_size": ([dp, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+        "mla_cache_append_static": ([dp, i32, vp, vp, vp, i32, ctypes.c_float, kvp, vp], ctypes.c_int),
         "mla_moe_gate": ([i32, i32, i32, i32, vp, vp, i32, vp, f32p, f32p, vp, ctypes.c_int64, vp], ctypes.c_int),
         "mla_moe_gate_workspace_size": ([i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     }
@@ -242,6 +244,17 @@ def mla_cache_append(dims: MlaDims, d_model: int, h, w_dkv, w_kr, cache: PagedCa
                                                      ctypes.byref(cache.kv), _ptr(workspace),
                                                      int(workspace.numel() * workspace.element_size()),
                                                      _stream(stream)))
+
+
+def mla_cache_append_static(dims: MlaDims, d_model: int, h, w_dkv, w_kr, cache: PagedCache,
+                            rope_theta: float = 10000.0, stream=None):
+    """mla_cache_append with the partial sums in the library's fixed per-GPU
+    scratch instead of a workspace (allocates nothing; calls that overlap on
+    one GPU race)."""
+    _check("mla_cache_append_static",
+           _lib.mla_cache_append_static(ctypes.byref(dims), int(d_model), _ptr(h), _ptr(w_dkv), _ptr(w_kr),
+                                        _dtype_code(h), float(rope_theta), ctypes.byref(cache.kv),
+                                        _stream(stream)))
 
 
 def mla_moe_gate_workspace_size(tokens: int, d_model: int, n_experts: int, in_dtype: int) -> int:

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "mla.h"
@@ -96,6 +97,7 @@ const char* mla_status_str(int status) {
     case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_splits out of range";
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: the HIP runtime refused the launch";
     case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable device";
+    case MLA_ERR_SCRATCH: return "MLA_ERR_SCRATCH: the call needs more than the library's static scratch holds";
     default: return "MLA_ERR_UNKNOWN";
   }
 }
@@ -302,8 +304,9 @@ int mla_cache_append_workspace_size(const mla_dims* dims, int32_t d_model, int64
 
 namespace {
 
-// The body of mla_cache_append: with `workspace` NULL it validates only and
-// stores the partial-sum bytes the call needs in *need (launching nothing).
+// The shared body of mla_cache_append and mla_cache_append_static: with
+// `workspace` NULL it validates only and stores the partial-sum bytes the
+// call needs in *need (launching nothing).
 int cache_append_impl(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
                       int32_t in_dtype, float rope_theta, const mla_paged_kv* kv, void* workspace,
                       int64_t workspace_bytes, int64_t* need, void* stream) {
@@ -380,6 +383,31 @@ int cache_append_impl(const mla_dims* dims, int32_t d_model, const void* h, cons
   return st;
 }
 
+// ---- the no-allocation variant's scratch: one array per GPU, in this
+// source's device code, for the fp32 chunk partial sums of the append.  Host
+// code never passes `scratch` itself (its host-side name is not a device
+// address): the device address is looked up once per device with that
+// device current and kept in g_scratch.
+constexpr int64_t kScratchBytes = MLA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_DEVICE;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +418,21 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
   if (!workspace) return MLA_ERR_NULL;
   return cache_append_impl(dims, d_model, h, w_dkv, w_kr, in_dtype, rope_theta, kv, workspace, workspace_bytes,
                            nullptr, stream);
+}
+
+int mla_cache_append_static(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv,
+                            const void* w_kr, int32_t in_dtype, float rope_theta, const mla_paged_kv* kv,
+                            void* stream) {
+  int64_t need = 0;
+  int st = cache_append_impl(dims, d_model, h, w_dkv, w_kr, in_dtype, rope_theta, kv, nullptr, 0, &need, stream);
+  if (st) return st;
+  if (need > kScratchBytes) return MLA_ERR_SCRATCH;
+  if (need == 0) return MLA_OK;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  return cache_append_impl(dims, d_model, h, w_dkv, w_kr, in_dtype, rope_theta, kv, ws, kScratchBytes, nullptr,
+                           stream);
 }
 
 namespace {

@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 14, syms
     lib = ctypes.CDLL(M.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
@@ -38,8 +38,8 @@ def test_source_hash_matches_the_sources():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 8
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    assert M.abi_version() == 9
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
 
@@ -129,6 +129,29 @@ def test_cache_append_validation():
     assert call(kv=_kv(bs=32)) == M.MLA_ERR_SHAPE
     assert L.mla_cache_append(ctypes.byref(M.make_dims(0, 1, 128)), 640, 0x1000, 0x2000, 0x3000, M.MLA_BF16,
                               10000.0, ctypes.byref(_kv()), 0x9000, 0, None) == M.MLA_OK  # nothing to do
+
+
+def test_cache_append_static_validation():
+    """The no-allocation append validates like mla_cache_append and refuses a
+    call whose partial sums exceed its fixed scratch before touching any
+    device (every call here returns before a launch)."""
+    L = M._lib
+
+    def call(batch=2, sq=1, d_model=640, h=0x1000, dt=M.MLA_BF16, kv=None):
+        kv = kv if kv is not None else _kv()
+        return L.mla_cache_append_static(ctypes.byref(M.make_dims(batch, sq, 128)), d_model, h, 0x2000, 0x3000, dt,
+                                         10000.0, ctypes.byref(kv), None)
+    assert call(h=0) == M.MLA_ERR_NULL
+    assert call(d_model=96) == M.MLA_ERR_SHAPE
+    assert call(dt=M.MLA_F32) == M.MLA_ERR_DTYPE
+    assert call(h=0x1008) == M.MLA_ERR_ALIGN
+    # d_model 5120: 10 chunks x 576 x 4 bytes per token; 728 tokens fit in 16 MiB, 729 do not
+    assert 728 * 10 * 576 * 4 <= M.MLA_STATIC_SCRATCH_BYTES < 729 * 10 * 576 * 4
+    assert call(batch=729, d_model=5120) == M.MLA_ERR_SCRATCH
+    assert call(batch=243, sq=3, d_model=5120) == M.MLA_ERR_SCRATCH
+    assert call(batch=0) == M.MLA_OK  # nothing to do, no device touched
+    assert "scratch" in M.status_str(M.MLA_ERR_SCRATCH)
+
 
 
 def test_moe_gate_validation():
