@@ -39,6 +39,10 @@
  *    MLA_ERR_SHAPE without launching if a length is negative or too long or
  *    a block id among a sequence's first ceil(len / block_size) entries is
  *    outside [0, num_blocks); MLA_ERR_DEVICE if the copy fails.
+ *  - mla_decode with a bf16 cache runs 64 query rows per workgroup, or 32
+ *    when 64-row workgroups would leave compute units idle (few sequence x
+ *    chunk units); MLA_DECODE_ROWS=64 or 32 in the environment at the call
+ *    fixes the choice (same results within rounding of the summation order).
  *  - Supported sizes: d_latent = 512, d_rope = 64, d_head = 128,
  *    block_size = 64, 1 <= q_per_seq <= MLA_MAX_Q_PER_SEQ; anything else is
  *    MLA_ERR_SHAPE.  The fp32 paths launch one grid row per query row, so

@@ -69,6 +69,29 @@ int check_dims(const mla_dims* d) {
   return MLA_OK;
 }
 
+// MLA_DECODE_ROWS=64 or 32 in the environment at the call fixes the bf16
+// decode's query rows per workgroup (otherwise chosen from the launch size).
+int forced_decode_rows() {
+  const char* e = getenv("MLA_DECODE_ROWS");
+  if (!e) return 0;
+  if (!strcmp(e, "64")) return 64;
+  if (!strcmp(e, "32")) return 32;
+  return 0;
+}
+
+// Compute units of the current device (0 if unknown; cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 // Launch through hipLaunchKernel so the status returned is this launch's own
 // (hipGetLastError would also report errors left by unrelated earlier calls).
 // With MLA_VERBOSE set in the environment a refused launch prints the HIP error.
@@ -197,7 +220,15 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   a.sq = dims->q_per_seq;
   a.heads = dims->heads;
   a.rows = rows;
-  a.row_blocks = (rows + mla::kDecodeRowsPerWg - 1) / mla::kDecodeRowsPerWg;
+  // bf16: 32-row workgroups when 64-row ones would leave compute units idle
+  // (few (sequence, chunk) units: a long context split into few chunks)
+  int rows_per_wg = mla::kDecodeRowsPerWg;
+  if (fmt == 1) {
+    const int forced = forced_decode_rows();
+    if (forced) rows_per_wg = forced;
+    else if (rows > 32 && units * ((rows + 63) / 64) < device_cus()) rows_per_wg = 32;
+  }
+  a.row_blocks = (rows + rows_per_wg - 1) / rows_per_wg;
   a.num_splits = num_splits;
   a.units = (int)units;
   a.max_blocks = kv->max_blocks_per_seq;
@@ -209,8 +240,12 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
     const int64_t padded = (units + 7) / 8 * 8;
     const int64_t grid = padded * a.row_blocks;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    if (fmt == 1)
-      st = launch("mla::decode_mfma_bf16", (const void*)mla::decode_mfma_bf16, dim3((unsigned)grid), dim3(512), a, s);
+    if (fmt == 1 && rows_per_wg == 32)
+      st = launch("mla::decode_mfma_bf16<32>", (const void*)mla::decode_mfma_bf16<32>, dim3((unsigned)grid), dim3(512),
+                  a, s);
+    else if (fmt == 1)
+      st = launch("mla::decode_mfma_bf16<64>", (const void*)mla::decode_mfma_bf16<64>, dim3((unsigned)grid), dim3(512),
+                  a, s);
     else
       st = launch("mla::decode_mfma_fp8", (const void*)mla::decode_mfma_fp8, dim3((unsigned)grid), dim3(512), a, s);
   } else {

@@ -31,7 +31,6 @@ constexpr int kTileTok = 32;                    // tokens per LDS tile
 constexpr int kLatBytes = kTileTok * 64 * 16;   // latent part: 32 rows x 64 chunks of 16 B
 constexpr int kRopeBytes = kTileTok * 8 * 16;   // RoPE part:   32 rows x 8 chunks
 constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 36,864
-constexpr int kRowsPerWg = 64;
 constexpr float kRefSlack = 64.0f;              // log2 headroom above a row's reference max
 
 // LDS tile layout (64 banks x 4 B): chunk q of latent row r sits at slot
@@ -161,8 +160,12 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
 
 }  // namespace
 
-// bf16 cache.  Workgroup = 8 waves = one (sequence, KV chunk, block of 64
-// query rows); the chunk is walked in 32-token tiles (half a cache page).
+// bf16 cache.  Workgroup = 8 waves = one (sequence, KV chunk, block of
+// kRows = 64 or 32 query rows); the chunk is walked in 32-token tiles (half
+// a cache page).  The description below is for 64 rows; with 32 rows each
+// score wave holds one 16-row block and each value wave one 32-row block
+// (half the products per tile, for launches with few (sequence, chunk)
+// units: four row blocks per unit fill twice as many compute units).
 // Two wave roles, one of each per SIMD:
 //   score waves 0..3: wave w computes S^T[16 tokens (half w&1)][32 rows
 //            (half w>>1)] with v_mfma_f32_16x16x32_bf16 over K = 576 (A = tile
@@ -179,14 +182,17 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
 // waves work on tile s, the value waves on tile s-1 (and refill their slices
 // of its buffer with tile s+3 once read), tiles s+1 .. s+3 are in flight;
 // one barrier per tile.
+template <int kRows>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_bf16(const DecodeArgs a) {
+  static_assert(kRows == 64 || kRows == 32, "64 or 32 query rows per workgroup");
+  constexpr int kRB = kRows / 32;                 // 16-row blocks per score wave, 32-row blocks per value wave
   constexpr int kBuf = 4;                         // tile ring
-  constexpr int kPBytes = 64 * 32 * 2;            // P of one tile: 64 rows x 32 tokens bf16
+  constexpr int kPBytes = kRows * 32 * 2;         // P of one tile: kRows rows x 32 tokens bf16
   constexpr int kQStride = 73;                    // staged query row: 72 chunks + 1 pad
   constexpr int kQBase = 2 * kTileBytes;          // queries are staged over tiles 2, 3 (+ P)
   constexpr int kXOff = kBuf * kTileBytes + 2 * kPBytes;
-  static_assert(kQBase + 64 * kQStride * 16 <= kXOff, "query staging must fit before the exchange area");
+  static_assert(kQBase + (kRows * kQStride + 63) / 64 * 1024 <= kXOff, "query staging must fit before the exchange area");
   constexpr int kORow = 512 * 4 + 16;             // staged output row (epilogue)
   static_assert(64 * kORow <= kBuf * kTileBytes, "the output staging must fit in the tile ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kXOff + 1280];
@@ -209,7 +215,7 @@ decode_mfma_bf16(const DecodeArgs a) {
   const int q4 = lane >> 4;       // k-quarter of a 16x16 operand / token quad of its result
   const int i16 = lane & 15;
   const int rows = a.rows;
-  const int row_base = wk.rb * kRowsPerWg;
+  const int row_base = wk.rb * kRows;
   const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
   const int ntiles = wk.ntiles;
   const uint32_t tiles_lds = lds_addr(tiles);
@@ -287,13 +293,15 @@ decode_mfma_bf16(const DecodeArgs a) {
     }
   };
 
-  // ---- prologue: stage the block's 64 query rows (q_lat | q_rope, 72 chunks
-  // of 16 bytes each, row stride 73 chunks) over tile buffers 2..3 with DMA,
+  // ---- prologue: stage the block's kRows query rows (q_lat | q_rope, 72
+  // chunks of 16 bytes each, row stride 73 chunks) over tile buffers 2..3
+  // with DMA (lanes past the last row copy a clamped row into the staging
+  // area's tail, which nothing reads),
   // start tiles 0 and 1; the score waves then pull their queries into
   // registers.
   {
     const int64_t qbase = (int64_t)wk.b * rows;
-    for (int i = wave; i < (64 * kQStride) / 64; i += 8) {
+    for (int i = wave; i < (kRows * kQStride + 63) / 64; i += 8) {
       const int sl = i * 64 + lane;
       const int r = sl / kQStride, c = sl - r * kQStride;
       const int qr = min(row_base + r, rows - 1);
@@ -331,10 +339,10 @@ decode_mfma_bf16(const DecodeArgs a) {
     // chunk ks + 16 q4 for ks < 16 (each lane quarter walks its own quarter of
     // the row: with the tile swizzle this order keeps the tile reads free of
     // bank conflicts, measured), RoPE chunk 4 (ks - 16) + q4 after
-    bf16x8 qf[2][18];
+    bf16x8 qf[kRB][18];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = 32 * rh + 16 * rb + i16;
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int r = (kRows / 2) * rh + 16 * rb + i16;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
         const int c = ks < 16 ? ks + 16 * q4 : 64 + 4 * (ks - 16) + q4;
@@ -357,8 +365,8 @@ decode_mfma_bf16(const DecodeArgs a) {
     int prow[2], hi_tok[2];
     uint32_t pwrite[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      prow[rb] = 32 * rh + 16 * rb + i16;
+    for (int rb = 0; rb < kRB; ++rb) {
+      prow[rb] = (kRows / 2) * rh + 16 * rb + i16;
       const int qrow = row_base + prow[rb];
       hi_tok[rb] = qrow < rows ? min(wk.tok1, wk.len - (a.sq - 1 - qrow / a.heads)) : 0;
       pwrite[rb] = (4 * prow[rb] + ((2 * th + (q4 & 1)) ^ ((prow[rb] >> 2) & 3))) * 16 + 8 * (q4 >> 1);
@@ -370,7 +378,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
     // scores of tile s: 18 k-steps, two 16x16x32 products each (one per row
     // block, same token operand).  `hook(ks)` runs after k-step ks.
-    f32x4 sacc[2];
+    f32x4 sacc[kRB];
     auto scores = [&](int s, auto hook) __attribute__((always_inline)) {
       const MLA_LDS uint8_t* tb = tiles + (s % kBuf) * kTileBytes;
       auto ldA = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
@@ -378,15 +386,15 @@ decode_mfma_bf16(const DecodeArgs a) {
         return *(const MLA_LDS bf16x8*)(tb + c1_rope[ks - 16]);
       };
       constexpr int kDepth = 4;
-      sacc[0] = f32x4{};
-      sacc[1] = f32x4{};
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) sacc[rb] = f32x4{};
       bf16x8 ar[kDepth];
 #pragma unroll
       for (int ks = 0; ks < kDepth; ++ks) ar[ks] = ldA(ks);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        sacc[0] = mfma16x16x32(ar[ks % kDepth], qf[0][ks], sacc[0]);
-        sacc[1] = mfma16x16x32(ar[ks % kDepth], qf[1][ks], sacc[1]);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) sacc[rb] = mfma16x16x32(ar[ks % kDepth], qf[rb][ks], sacc[rb]);
         if (ks + kDepth < 18) ar[ks % kDepth] = ldA(ks + kDepth);
         hook(ks);
         sched_fence();
@@ -398,7 +406,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     auto soft_scale = [&](int s) __attribute__((always_inline)) {
       const int tt = wk.tok0 + s * kTileTok + 16 * th + 4 * q4;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float x = sacc[rb][r] * a.scale_log2;
@@ -411,7 +419,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     // cannot matter next to the row's largest weight (>= 1 after the first tile)
     auto soft_finish = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         m_hi[rb] = fmaxf(m_hi[rb], mx[rb]);
         ovf |= mx[rb] > m_ref[rb] + kRefSlack;
         const float mu = m_ref[rb] == -__builtin_inff() ? 0.f : m_ref[rb];
@@ -427,7 +435,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
     for (int pass = 0; pass < 2; ++pass) {
       const bool first = pass == 0;
-      l_part[0] = l_part[1] = 0.f;
+      l_part[0] = l_part[1] = 0.f;  // entry 1 unused with one row block
       m_hi[0] = m_hi[1] = -__builtin_inff();
       ovf = false;
       if (!first) {
@@ -448,7 +456,7 @@ decode_mfma_bf16(const DecodeArgs a) {
           // each row's maximum over the whole first tile (both token halves);
           // a row left at -inf sees no token of this chunk
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
+          for (int rb = 0; rb < kRB; ++rb) {
             float m = fmaxf(mx[rb], __shfl_xor(mx[rb], 16, 64));
             m = fmaxf(m, __shfl_xor(m, 32, 64));
             if (q4 == 0) xm[th * 64 + prow[rb]] = m;
@@ -456,7 +464,7 @@ decode_mfma_bf16(const DecodeArgs a) {
           }
           wg_barrier();
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(mx[rb], xm[(th ^ 1) * 64 + prow[rb]]);
+          for (int rb = 0; rb < kRB; ++rb) m_ref[rb] = fmaxf(mx[rb], xm[(th ^ 1) * 64 + prow[rb]]);
         }
         soft_finish(0);
         wait_vmcnt<2>();  // tile 1 (tiles 2, 3 may still be in flight)
@@ -480,7 +488,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
       // ---- did any row overflow its reference?  (its partner lanes may not know)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         float m = fmaxf(m_hi[rb], __shfl_xor(m_hi[rb], 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
         m_hi[rb] = m;
@@ -494,13 +502,13 @@ decode_mfma_bf16(const DecodeArgs a) {
       const bool again = (xf[0] | xf[1] | xf[2] | xf[3]) != 0;
       if (!again || !first) break;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) m_ref[rb] = fmaxf(m_hi[rb], xm[(th ^ 1) * 64 + prow[rb]]);
+      for (int rb = 0; rb < kRB; ++rb) m_ref[rb] = fmaxf(m_hi[rb], xm[(th ^ 1) * 64 + prow[rb]]);
       wg_barrier();
     }
 
     // ---- row sums (4 token quads x 2 token halves) for the value waves; lse
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       float l = l_part[rb] + __shfl_xor(l_part[rb], 16, 64);
       l += __shfl_xor(l, 32, 64);
       if (q4 == 0) xl[th * 64 + prow[rb]] = l;
@@ -508,7 +516,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     wg_barrier();
     if (th == 0 && q4 == 0) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         const int qrow = row_base + prow[rb];
         const float lt = xl[prow[rb]] + xl[64 + prow[rb]];
         if (qrow < rows) a.lse[slot * rows + qrow] = lt > 0.f ? (m_ref[rb] + log2f(lt)) * kLn2 : -__builtin_inff();
@@ -535,7 +543,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) pread[ks] = (4 * n32 + ((2 * ks + g) ^ ((n32 >> 2) & 3))) * 16;
 
-    f32x16 oacc[4][2];
+    f32x16 oacc[4][kRB];
     // C^T operand of tile t, 16-token half ks, 32-column block mt
     auto av_load = [&](int t, int ks, int mt) __attribute__((always_inline)) -> bf16x8 {
       const MLA_LDS uint8_t* vt = tiles + (t % kBuf) * kTileBytes + ks * 16 * 256;
@@ -560,18 +568,17 @@ decode_mfma_bf16(const DecodeArgs a) {
     // their issue.  Then the operands of tile `next` (if >= 0) are read.
     auto values = [&](int t, bool refill, const TileSrc& nsrc, int next) __attribute__((always_inline)) {
       const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
-      bf16x8 bp[2][2];
+      bf16x8 bp[2][kRB];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bp[ks][0] = *(const MLA_LDS bf16x8*)(pb + pread[ks]);
-        bp[ks][1] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048);
-      }
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < kRB; ++nt) bp[ks][nt] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048 * nt);
       if (refill) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of slice v are done
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ks = i >> 3, mt = (i >> 1) & 3, nt = i & 1;
+      for (int i = 0; i < 8 * kRB; ++i) {
+        const int ks = i / (4 * kRB), mt = (i / kRB) & 3, nt = i % kRB;
         oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
-        if (refill && (i & 1) == 0) lat_copy(nsrc, i >> 1);
+        if (refill && nt == 0) lat_copy(nsrc, i / kRB);
         sched_fence();
       }
       if (next >= 0) load_av(next);
@@ -582,7 +589,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) oacc[mt][nt] = f32x16{};
+        for (int nt = 0; nt < kRB; ++nt) oacc[mt][nt] = f32x16{};
       if (!first) {
         issue_tile(0, blk_a);
         issue_tile(1, blk_b);
@@ -622,7 +629,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     // rows of 512 fp32 plus 16 bytes of pad
     wg_barrier();  // row sums
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kRB; ++nt) {
       const int r = nt * 32 + n32;
       const float lt = xl[r] + xl[64 + r];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -645,7 +652,7 @@ decode_mfma_bf16(const DecodeArgs a) {
     float* obase = a.o + slot * (int64_t)rows * 512;
     const int c16 = tid & 127;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kRows / 4; ++k) {
       const int r = (tid >> 7) + 4 * k;
       const f32x4 o = *(const MLA_LDS f32x4*)(tiles + r * kORow + c16 * 16);
       if (row_base + r < rows) *(f32x4*)(obase + (int64_t)(row_base + r) * 512 + 4 * c16) = o;
@@ -695,7 +702,7 @@ decode_mfma_fp8(const DecodeArgs a) {
   const int q4 = lane >> 4;       // k-quarter of a 16x16 operand / token quad of its result
   const int i16 = lane & 15;
   const int rows = a.rows;
-  const int row_base = wk.rb * kRowsPerWg;
+  const int row_base = wk.rb * kDecodeRowsPerWg;
   const int64_t slot = (int64_t)wk.b * a.num_splits + wk.split;
   const int ntiles = wk.ntiles;
   const uint32_t tiles_lds = lds_addr(tiles);
@@ -1265,5 +1272,8 @@ __global__ void __launch_bounds__(256) decode_f32(const DecodeArgs a) {
   orow[tid + 256] = o1 * inv;
   if (tid == 0) a.lse[slot * a.rows + row] = l > 0.f ? m + logf(l) : -__builtin_inff();
 }
+
+template __global__ void decode_mfma_bf16<64>(const DecodeArgs a);
+template __global__ void decode_mfma_bf16<32>(const DecodeArgs a);
 
 }  // namespace mla

@@ -22,9 +22,10 @@ struct DecodeArgs {
   float softmax_scale, scale_log2;
 };
 
+template <int kRows>  // query rows per workgroup: 64, or 32 for launches with few units
 __global__ void decode_mfma_bf16(const DecodeArgs a);
 __global__ void decode_mfma_fp8(const DecodeArgs a);
-constexpr int kDecodeRowsPerWg = 64;
+constexpr int kDecodeRowsPerWg = 64;  // the fp8 kernel's, and the bf16 kernel's by default
 __global__ void decode_f32(const DecodeArgs a);
 
 struct AbsorbArgs {

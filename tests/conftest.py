@@ -6,6 +6,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+import pytest
+
+
+@pytest.fixture(params=["64", "32"], ids=lambda r: f"rows{r}")
+def decode_rows(request, monkeypatch):
+    """Runs a test with the bf16 decode fixed at 64, then at 32 query rows
+    per workgroup (the library otherwise picks by launch size)."""
+    monkeypatch.setenv("MLA_DECODE_ROWS", request.param)
+    yield request.param
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
 

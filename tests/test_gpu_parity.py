@@ -6,7 +6,8 @@ import mla_inputs as MI
 import oracle as O
 from parity import check, metrics
 
-pytestmark = pytest.mark.gpu
+# every case runs at 64 and at 32 query rows per decode workgroup
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("decode_rows")]
 
 
 def run_gpu(inp, num_splits=None):
