@@ -249,9 +249,9 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
     else
       st = launch("mla::decode_mfma_fp8", (const void*)mla::decode_mfma_fp8, dim3((unsigned)grid), dim3(512), a, s);
   } else {
-    const int64_t grid = units * rows;
+    const int64_t grid = (units * rows + 7) / 8 * 8;  // a multiple of the 8 XCDs (see the kernel's placement)
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    st = launch("mla::decode_f32", (const void*)mla::decode_f32, dim3((unsigned)grid), dim3(256), a, s);
+    st = launch("mla::decode_f32", (const void*)mla::decode_f32, dim3((unsigned)grid), dim3(512), a, s);
   }
   return st;
 }
@@ -583,8 +583,12 @@ int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* nu
                             ((rows + mla::kDecodeRowsPerWg - 1) / mla::kDecodeRowsPerWg);
   const int pages = (max_seq_len + kBlock - 1) / kBlock;
   int64_t ns = (cus + per_split - 1) / per_split;
-  // keep at least 4 pages (256 tokens) per chunk so each workgroup streams enough
-  const int64_t max_ns = pages / 4 > 0 ? pages / 4 : 1;
+  // keep at least 4 pages (256 tokens) per chunk so each workgroup streams
+  // enough, except with few query rows (below one 64-row block per
+  // sequence), where a page per chunk spreads a small problem over more
+  // compute units
+  const int min_pages = rows >= mla::kDecodeRowsPerWg ? 4 : 1;
+  const int64_t max_ns = pages / min_pages > 0 ? pages / min_pages : 1;
   if (ns > max_ns) ns = max_ns;
   if (ns > MLA_MAX_SPLITS) ns = MLA_MAX_SPLITS;
   if (ns < 1) ns = 1;

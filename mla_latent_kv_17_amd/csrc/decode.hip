@@ -17,7 +17,8 @@
 //    contractions on the matrix cores, fixed per-row softmax reference.
 //  * decode_mfma_fp8 (E4M3 cache + fp32 token scales): the same pipeline with
 //    register-staged tiles converted to bf16 and the scales applied in fp32.
-//  * decode_f32 (fp32 cache): fp32 VALU, one workgroup per query row.
+//  * decode_f32 (fp32 cache): fp32 VALU, one workgroup per (chunk, query row)
+//    over 16-token tiles copied to LDS by DMA, three tiles in flight.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -551,21 +552,22 @@ decode_mfma_bf16(const DecodeArgs a) {
       const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
       return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    // the C^T operands of the next tile are read ahead, at the end of the
-    // previous product (its tile has landed by then), so that a product
-    // waits only for its P reads
+    // C^T operands, one register set per 16-token half: half 0 of a tile is
+    // read in the iteration before its product, right after that
+    // iteration's half-0 products; half 1 at the start of the product's own
+    // iteration, behind the P reads.  So no operand read waits at a barrier,
+    // and a product waits only for its P reads.
     bf16x8 av[2][4];
-    auto load_av = [&](int t) __attribute__((always_inline)) {
+    auto load_half = [&](int t, int ks) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
+      for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
     };
-    // value product of tile t (its C^T operands already in av): two 16-token
-    // halves, eight 32x32x16 products each.  With `refill`, once every
-    // operand read of slice v has completed, the slice is refilled with tile
-    // nsrc: its eight copies go between the products, whose execution covers
-    // their issue.  Then the operands of tile `next` (if >= 0) are read.
+    // value product of tile t (half 0 of its C^T operands already in av):
+    // two 16-token halves, eight 32x32x16 products each (four with 32
+    // rows).  Between the halves, once every read of tile t's slice v has
+    // completed, half 0 of tile `next` (if >= 0) is read; with `refill` the
+    // slice is then refilled with tile nsrc: its eight copies go between the
+    // second half's products, whose execution covers their issue.
     auto values = [&](int t, bool refill, const TileSrc& nsrc, int next) __attribute__((always_inline)) {
       const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
       bf16x8 bp[2][kRB];
@@ -573,15 +575,30 @@ decode_mfma_bf16(const DecodeArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int nt = 0; nt < kRB; ++nt) bp[ks][nt] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048 * nt);
-      if (refill) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of slice v are done
+      load_half(t, 1);
 #pragma unroll
-      for (int i = 0; i < 8 * kRB; ++i) {
-        const int ks = i / (4 * kRB), mt = (i / kRB) & 3, nt = i % kRB;
-        oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
-        if (refill && nt == 0) lat_copy(nsrc, i / kRB);
+      for (int i = 0; i < 4 * kRB; ++i) {
+        const int mt = i / kRB, nt = i % kRB;
+        oacc[mt][nt] = mfma32x32x16(av[0][mt], bp[0][nt], oacc[mt][nt]);
         sched_fence();
       }
-      if (next >= 0) load_av(next);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every read of tile t's slice v is done
+      if (next >= 0) load_half(next, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * kRB; ++i) {
+        const int mt = i / kRB, nt = i % kRB;
+        oacc[mt][nt] = mfma32x32x16(av[1][mt], bp[1][nt], oacc[mt][nt]);
+        if (refill) {
+          if (kRB == 1) {
+            lat_copy(nsrc, 2 * i);
+            lat_copy(nsrc, 2 * i + 1);
+          } else if (nt == 0) {
+            lat_copy(nsrc, 2 * mt);
+            lat_copy(nsrc, 2 * mt + 1);
+          }
+        }
+        sched_fence();
+      }
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -600,7 +617,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
       int blk_next = tile_block(4);
       if (ntiles > 0) {
-        load_av(0);
+        load_half(0, 0);
         issue_tile(2, tile_block(2));
         issue_tile(3, tile_block(3));
         if (first) wg_barrier();  // the score waves' reference exchange
@@ -1186,21 +1203,44 @@ decode_mfma_fp8(const DecodeArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// fp32 cache and queries: one workgroup (256 threads) per (sequence, KV chunk,
-// query row), fp32 VALU throughout.  Tokens are taken 256 at a time: thread j
-// forms the score of token j (a 576-wide dot product, float4 loads of the
-// token's row, the block table read once per token), the block merges the
-// group's maximum and sum into its running ones (rescaling the output), and
-// thread c accumulates latent columns c and c + 256 over the group.
+// fp32 cache and queries: one workgroup (512 threads) per (sequence, KV chunk,
+// query row), fp32 arithmetic throughout.  The chunk is walked in 16-token
+// tiles copied HBM -> LDS by DMA into a ring of four buffers (three tiles in
+// flight).  Waves 4..7 only issue the copies (lane i of a copy brings 16
+// bytes of the tile's rows: coalesced), split over the two phases of a
+// tile so that their issue overlaps the arithmetic of waves 0..3:
+//   scores: wave w forms the scores of tokens 4w .. 4w+3, lane l summing
+//           q . c_t over latent floats 4l..4l+3 and 256+4l..+3 and RoPE
+//           float l (16-byte LDS reads, q held in registers), then a DPP
+//           wave sum;
+//   values: thread i rescales and accumulates latent columns 2i, 2i+1 with
+//           the tile's 16 weights (online softmax in the log2 domain,
+//           hardware exp2).
+// Two barriers per tile.  Rows past the row's visible range are zeroed in
+// LDS by the waves that copied them once their copies have landed (an
+// uninitialised pool row may hold NaN; its weight is 0).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) decode_f32(const DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) float q_s[576];
-  __shared__ float p_s[256];
-  __shared__ const float* row_s[256];
-  __shared__ float red[8];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row = blockIdx.x % a.rows;
-  const int unit = blockIdx.x / a.rows;
+__global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
+  constexpr int kT = 16;          // tokens per tile
+  constexpr int kRowF = 576;      // floats of a staged token row: latent, then RoPE key
+  constexpr int kBufN = 4;        // tile ring
+  constexpr int kCopies = kT * kRowF * 4 / 1024 / 4;  // 1 KB copies per copy wave per tile (9)
+  static_assert(kT * kRowF * 4 == 4 * kCopies * 1024, "whole copies per wave");
+  __shared__ __attribute__((aligned(1024))) float tile[kBufN][kT * kRowF];
+  __shared__ float sc[2][kT];
+  if (blockDim.x != 512) return;  // the roles below assume eight waves
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool copyw = wave >= 4;
+  const int cw = wave & 3;
+  // XCD-aware placement: workgroup ids are dealt round-robin over the 8
+  // XCDs, so XCD x takes a contiguous range of (unit, row) pairs and the rows
+  // of a chunk, which read the same pages, share that XCD's L2
+  const int total = a.units * a.rows;
+  const int per_xcd = (total + 7) >> 3;
+  const int lin = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int row = lin % a.rows;
+  const int unit = lin / a.rows;
   const int b = unit / a.num_splits, split = unit % a.num_splits;
   const int len = a.seq_lens[b];
   const int npages = (len + 63) >> 6;
@@ -1209,68 +1249,123 @@ __global__ void __launch_bounds__(256) decode_f32(const DecodeArgs a) {
   const int qi = row / a.heads;
   const int nvis = len - (a.sq - 1 - qi);
   const int tok0 = p0 * 64;
-  const int tok1 = min(min(p1 * 64, len), max(nvis, 0));
+  const int tok1 = min(min(p1 * 64, len), max(nvis, 0));  // this row's tokens of the chunk: [tok0, tok1)
+  const int ntiles = tok1 > tok0 ? (tok1 - tok0 + kT - 1) / kT : 0;
+  const uint32_t tiles_lds = lds_addr((MLA_LDS float*)&tile[0][0]);
+
+  // copy k of copy wave cw brings 16-byte piece idx = (9 cw + k) 64 + lane of
+  // the tile: row idx / 144, floats 4 (idx % 144) .. (the row's latent, then
+  // its RoPE key); tiles past the chunk, and rows past the range, copy the
+  // range's last row (any valid row: they are never used)
+  int blk = 0;
+  auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
+    const int t0 = min(tok0 + t * kT, tok1 - 1);
+    // scalar load: a vector one would make the compiler wait for the copies
+    return load_uniform(a.block_table, (int64_t)b * a.max_blocks + (t0 >> 6));
+  };
+  auto issue = [&](int t, int k0, int k1) __attribute__((always_inline)) {
+    const int t0 = min(tok0 + t * kT, tok1 - 1) & ~(kT - 1);  // tiles never cross a page
+    const uint32_t lbase = tiles_lds + (uint32_t)((t % kBufN) * kT * kRowF * 4);
+#pragma unroll
+    for (int k = k0; k < k1; ++k) {
+      const int idx = (kCopies * cw + k) * 64 + lane, tr = idx / 144, c4 = idx - tr * 144;
+      const int64_t prow = min(t0 + tr, tok1 - 1) & 63;  // same page as t0
+      const uint8_t* src = c4 < 128 ? a.latent + blk * a.lat_bs + prow * a.lat_rs + 16 * c4
+                                    : a.rope + blk * a.rope_bs + prow * a.rope_rs + 16 * (c4 - 128);
+      dma16(src, lbase + (uint32_t)((kCopies * cw + k) * 1024));
+    }
+  };
+  // zero this wave's copied pieces of tile t that lie past the range
+  auto fix_tile = [&](int t) __attribute__((always_inline)) {
+    const int t0 = tok0 + t * kT;
+    if (t0 + kT > tok1) {
+#pragma unroll
+      for (int k = 0; k < kCopies; ++k) {
+        const int idx = (kCopies * cw + k) * 64 + lane, tr = idx / 144;
+        if (t0 + tr >= tok1) *(MLA_LDS f32x4*)(MLA_LDS float*)&tile[t % kBufN][idx * 4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  if (copyw) {
+    // ================= copy waves =================
+    if (ntiles > 0) {
+      for (int t = 0; t < 3; ++t) {
+        blk = tile_block(t);
+        issue(t, 0, kCopies);
+      }
+      blk = tile_block(3);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      wait_vmcnt<2 * kCopies>();  // tile t (tiles t+1, t+2 may still be in flight)
+      fix_tile(t);
+      __syncthreads();
+      issue(t + 3, 0, 5);  // into the buffer of tile t-1, whose reads ended before the barrier
+      __syncthreads();
+      issue(t + 3, 5, kCopies);
+      blk = tile_block(t + 4);
+    }
+    wait_vmcnt<0>();  // copies issued for tiles past the range have landed
+    return;
+  }
+
+  // ================= arithmetic waves =================
   const int64_t qoff = (int64_t)b * a.rows + row;
   const float* ql = (const float*)a.q_lat + qoff * 512;
-  const float* qr = (const float*)a.q_rope + qoff * 64;
-  for (int i = tid; i < 576; i += 256) q_s[i] = i < 512 ? ql[i] : qr[i - 512];
-  __syncthreads();
-  auto block_reduce = [&](float v, bool is_max) -> float {
-    v = is_max ? wave_max(v) : wave_sum(v);
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    const float r = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
-    return r;
-  };
+  const f32x4 qa = *(const f32x4*)(ql + 4 * lane);
+  const f32x4 qb = *(const f32x4*)(ql + 256 + 4 * lane);
+  const float qr = ((const float*)a.q_rope + qoff * 64)[lane];
+  const int c2 = 2 * (cw * 64 + lane);  // this thread's latent columns c2, c2 + 1
   float m = -__builtin_inff(), l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c0 = tok0; c0 < tok1; c0 += 256) {
-    const int n = min(256, tok1 - c0);
-    float sc = -__builtin_inff();
-    if (tid < n) {
-      const int t = c0 + tid;
-      const int blk = a.block_table[(int64_t)b * a.max_blocks + (t >> 6)];
-      const float* lp = (const float*)(a.latent + blk * a.lat_bs + (int64_t)(t & 63) * a.lat_rs);
-      const float* rp = (const float*)(a.rope + blk * a.rope_bs + (int64_t)(t & 63) * a.rope_rs);
-      row_s[tid] = lp;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < 128; ++i) {
-        const f32x4 v = ((const f32x4*)lp)[i];
-        const f32x4 q = ((const MLA_LDS f32x4*)q_s)[i];
-        acc = fmaf(v[0], q[0], fmaf(v[1], q[1], fmaf(v[2], q[2], fmaf(v[3], q[3], acc))));
-      }
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    const MLA_LDS float* tl = (const MLA_LDS float*)&tile[t % kBufN][0];
+    float part[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const f32x4 v = ((const f32x4*)rp)[i];
-        const f32x4 q = ((const MLA_LDS f32x4*)q_s)[128 + i];
-        acc = fmaf(v[0], q[0], fmaf(v[1], q[1], fmaf(v[2], q[2], fmaf(v[3], q[3], acc))));
-      }
-      sc = acc * a.softmax_scale;
+    for (int u = 0; u < 4; ++u) {
+      const MLA_LDS float* tr = tl + (4 * cw + u) * kRowF;
+      const f32x4 x = *(const MLA_LDS f32x4*)(tr + 4 * lane);
+      const f32x4 y = *(const MLA_LDS f32x4*)(tr + 256 + 4 * lane);
+      float acc = tr[512 + lane] * qr;
+      acc = fmaf(x[0], qa[0], fmaf(x[1], qa[1], fmaf(x[2], qa[2], fmaf(x[3], qa[3], acc))));
+      acc = fmaf(y[0], qb[0], fmaf(y[1], qb[1], fmaf(y[2], qb[2], fmaf(y[3], qb[3], acc))));
+      part[u] = acc;
     }
-    const float mn = fmaxf(m, block_reduce(sc, true));
-    const float alpha = m == -__builtin_inff() ? 0.f : expf(m - mn);
-    const float pj = tid < n ? expf(sc - mn) : 0.f;
-    p_s[tid] = pj;
-    const float gsum = block_reduce(pj, false);  // its barriers also publish p_s and row_s
-    l = l * alpha + gsum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float sdot = wave_sum_rows(part[u]);
+      const int tok = tok0 + t * kT + 4 * cw + u;
+      if (lane == u) sc[t & 1][4 * cw + u] = tok < tok1 ? sdot * a.scale_log2 : -__builtin_inff();
+    }
+    __syncthreads();
+    float x[kT];
+    float mt = m;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      x[u] = sc[t & 1][u];
+      mt = fmaxf(mt, x[u]);
+    }
+    // every tile holds at least one token of the range, so mt is finite
+    const float alpha = __builtin_amdgcn_exp2f(m - mt);  // 0 on the first tile (m = -inf)
+    l *= alpha;
     o0 *= alpha;
     o1 *= alpha;
-    m = mn;
-    for (int j = 0; j < n; ++j) {
-      const float w = p_s[j];
-      const float* lp = row_s[j];
-      o0 = fmaf(w, lp[tid], o0);
-      o1 = fmaf(w, lp[tid + 256], o1);
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      const float pu = __builtin_amdgcn_exp2f(x[u] - mt);
+      const float c0 = tl[u * kRowF + c2], c1 = tl[u * kRowF + c2 + 1];  // one 8-byte read
+      l += pu;
+      o0 = fmaf(pu, c0, o0);
+      o1 = fmaf(pu, c1, o1);
     }
-    __syncthreads();  // p_s / row_s are rewritten by the next group
+    m = mt;
   }
   const int64_t slot = (int64_t)b * a.num_splits + split;
   float* orow = a.o + (slot * a.rows + row) * 512;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  orow[tid] = o0 * inv;
-  orow[tid + 256] = o1 * inv;
-  if (tid == 0) a.lse[slot * a.rows + row] = l > 0.f ? m + logf(l) : -__builtin_inff();
+  orow[c2] = o0 * inv;
+  orow[c2 + 1] = o1 * inv;
+  if (tid == 0) a.lse[slot * a.rows + row] = l > 0.f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
 }
 
 template __global__ void decode_mfma_bf16<64>(const DecodeArgs a);

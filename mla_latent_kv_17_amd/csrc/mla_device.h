@@ -76,4 +76,45 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Lane moves within rows of 16 lanes (every lane has a source in these
+// patterns): swap neighbours, swap pairs, mirror within 8, mirror within 16.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(dpp<kCtrl>(__float_as_int(v)));
+}
+
+// Every lane of a row of 16 lanes receives the row's maximum / sum (fixed
+// order).
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppMirror>(v);
+}
+
+// The same over the whole wave: the four rows' results combined from lanes
+// 0, 16, 32 and 48 (returned to every lane).
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_rows(float v) {
+  v = row_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v = row_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
 }  // namespace mla
