@@ -552,22 +552,21 @@ decode_mfma_bf16(const DecodeArgs a) {
       const u32x2 hi = lds_read_tr16_b64(vt + voff[1][mt]);
       return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    // C^T operands, one register set per 16-token half: half 0 of a tile is
-    // read in the iteration before its product, right after that
-    // iteration's half-0 products; half 1 at the start of the product's own
-    // iteration, behind the P reads.  So no operand read waits at a barrier,
-    // and a product waits only for its P reads.
+    // the C^T operands of the next tile are read ahead, at the end of the
+    // previous product (its tile has landed by then), so that a product
+    // waits only for its P reads
     bf16x8 av[2][4];
-    auto load_half = [&](int t, int ks) __attribute__((always_inline)) {
+    auto load_av = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) av[ks][mt] = av_load(t, ks, mt);
     };
-    // value product of tile t (half 0 of its C^T operands already in av):
-    // two 16-token halves, eight 32x32x16 products each (four with 32
-    // rows).  Between the halves, once every read of tile t's slice v has
-    // completed, half 0 of tile `next` (if >= 0) is read; with `refill` the
-    // slice is then refilled with tile nsrc: its eight copies go between the
-    // second half's products, whose execution covers their issue.
+    // value product of tile t (its C^T operands already in av): two 16-token
+    // halves, eight 32x32x16 products each.  With `refill`, once every
+    // operand read of slice v has completed, the slice is refilled with tile
+    // nsrc: its eight copies go between the products, whose execution covers
+    // their issue.  Then the operands of tile `next` (if >= 0) are read.
     auto values = [&](int t, bool refill, const TileSrc& nsrc, int next) __attribute__((always_inline)) {
       const MLA_LDS uint8_t* pb = pbuf + (t & 1) * kPBytes;
       bf16x8 bp[2][kRB];
@@ -575,30 +574,15 @@ decode_mfma_bf16(const DecodeArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int nt = 0; nt < kRB; ++nt) bp[ks][nt] = *(const MLA_LDS bf16x8*)(pb + pread[ks] + 2048 * nt);
-      load_half(t, 1);
+      if (refill) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of slice v are done
 #pragma unroll
-      for (int i = 0; i < 4 * kRB; ++i) {
-        const int mt = i / kRB, nt = i % kRB;
-        oacc[mt][nt] = mfma32x32x16(av[0][mt], bp[0][nt], oacc[mt][nt]);
+      for (int i = 0; i < 8 * kRB; ++i) {
+        const int ks = i / (4 * kRB), mt = (i / kRB) & 3, nt = i % kRB;
+        oacc[mt][nt] = mfma32x32x16(av[ks][mt], bp[ks][nt], oacc[mt][nt]);
+        if (refill && nt == 0) lat_copy(nsrc, i / kRB);
         sched_fence();
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every read of tile t's slice v is done
-      if (next >= 0) load_half(next, 0);
-#pragma unroll
-      for (int i = 0; i < 4 * kRB; ++i) {
-        const int mt = i / kRB, nt = i % kRB;
-        oacc[mt][nt] = mfma32x32x16(av[1][mt], bp[1][nt], oacc[mt][nt]);
-        if (refill) {
-          if (kRB == 1) {
-            lat_copy(nsrc, 2 * i);
-            lat_copy(nsrc, 2 * i + 1);
-          } else if (nt == 0) {
-            lat_copy(nsrc, 2 * mt);
-            lat_copy(nsrc, 2 * mt + 1);
-          }
-        }
-        sched_fence();
-      }
+      if (next >= 0) load_av(next);
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -617,7 +601,7 @@ decode_mfma_bf16(const DecodeArgs a) {
 
       int blk_next = tile_block(4);
       if (ntiles > 0) {
-        load_half(0, 0);
+        load_av(0);
         issue_tile(2, tile_block(2));
         issue_tile(3, tile_block(3));
         if (first) wg_barrier();  // the score waves' reference exchange
