@@ -66,13 +66,16 @@ extern "C" {
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
  * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append;
  * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2); 7: adds mla_moe_gate;
- * 8: adds mla_source_hash; 9: adds mla_cache_append_static and MLA_ERR_SCRATCH */
-#define MLA_ABI_VERSION 9
+ * 8: adds mla_source_hash; 9: adds mla_cache_append_static and MLA_ERR_SCRATCH;
+ * 10: the chunk partials of mla_decode may be fp16 (MLA_F16): o_dtype of
+ * mla_decode, part_dtype of mla_split_combine and mla_combine_out_uv */
+#define MLA_ABI_VERSION 10
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
   MLA_BF16 = 1,
-  MLA_FP8_E4M3 = 2 /* OCP E4M3FN, one fp32 scale per cached token */
+  MLA_FP8_E4M3 = 2, /* OCP E4M3FN, one fp32 scale per cached token */
+  MLA_F16 = 3        /* IEEE binary16: mla_decode's chunk partials only */
 } mla_dtype;
 
 typedef enum mla_status {
@@ -176,19 +179,25 @@ int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int
  *   chunks of ceil(pages / num_splits) pages; chunk s writes its own
  *   normalised result: o = [batch][num_splits][q_per_seq][heads][d_latent],
  *   lse = [batch][num_splits][q_per_seq][heads]; merge with mla_split_combine.
+ * o_dtype: F32, or (num_splits > 1 with a BF16 or FP8 cache) F16: the
+ *   normalised chunk result, accumulated in fp32, rounded to nearest-even
+ *   binary16 (relative error below 2^-11; the merge reads half the bytes);
+ *   lse is fp32 in every case.  Anything else is MLA_ERR_DTYPE.
  * A query (or chunk) that sees no token writes o = 0 and lse = -inf.
  * Arithmetic: bf16/fp8 caches use bf16 matrix cores with fp32 accumulation
  * (E4M3 codes are exact in bf16; the per-token scale is applied in fp32);
  * the F32 cache is computed in fp32 throughout. */
 int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int32_t q_dtype,
-               const mla_paged_kv* kv, int32_t num_splits, float* o, float* lse, void* stream);
+               const mla_paged_kv* kv, int32_t num_splits, void* o, int32_t o_dtype, float* lse, void* stream);
 
 /* Log-sum-exp merge of mla_decode's per-chunk results:
  *   lse = ln sum_s exp(lse_s),   o_lat = sum_s exp(lse_s - lse) o_s.
  * Chunks with lse_s = -inf carry weight 0; if all do, o_lat = 0 and lse = -inf.
- * o_part: [batch][num_splits][q_per_seq][heads][d_latent], lse_part: [batch][num_splits][q_per_seq][heads]
- * o_lat:  [batch*q_per_seq][heads][d_latent];  lse: same layout as mla_decode's, or NULL. */
-int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_part,
+ * o_part: [batch][num_splits][q_per_seq][heads][d_latent], part_dtype (F32 or F16,
+ *         as mla_decode wrote it); lse_part: [batch][num_splits][q_per_seq][heads] fp32
+ * o_lat:  [batch*q_per_seq][heads][d_latent] fp32;  lse: same layout as
+ *         mla_decode's, or NULL.  Sums are fp32. */
+int mla_split_combine(const mla_dims* dims, int32_t num_splits, const void* o_part, int32_t part_dtype,
                       const float* lse_part, float* o_lat, float* lse, void* stream);
 
 /* Output absorption (W_UV folded into the output side, same formula box):
@@ -207,14 +216,15 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
  * from the chunks' partials and never written,
  *   out[r][h][d] = sum_c w_uv[h][d][c] * (sum_s exp(lse_s - lse) o_s[r][h][c]),
  *   lse[r][h]    = ln sum_s exp(lse_s).
- * o_part, lse_part: mla_decode's outputs for num_splits > 1 (layouts above);
+ * o_part, part_dtype, lse_part: mla_decode's outputs for num_splits > 1
+ * (layouts and partial dtypes as for mla_split_combine);
  * w_uv, w_dtype, out, out_dtype: as for mla_out_uv; lse: [batch*q_per_seq][heads]
  * fp32, or NULL.
  * Chunks with lse_s = -inf carry weight 0 (their o_s is not read); a row whose
  * chunks all do gets out = 0 and lse = -inf.  Same accuracy as the two calls. */
-int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
-                       const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, float* lse,
-                       void* stream);
+int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_part, int32_t part_dtype,
+                       const float* lse_part, const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype,
+                       float* lse, void* stream);
 
 /* Cache append: the step that writes the S_q newest tokens of each sequence
  * into the paged cache before mla_decode reads them (same page, section 1,

@@ -17,7 +17,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 
-MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_F16 = 0, 1, 2, 3
 MLA_OK = 0
 MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_ALIGN = -1, -2, -3, -4
 MLA_ERR_SPLITS, MLA_ERR_LAUNCH, MLA_ERR_DEVICE, MLA_ERR_SCRATCH = -5, -6, -7, -8
@@ -85,10 +85,10 @@ def _load():
         "mla_abi_version": ([], ctypes.c_int),
         "mla_source_hash": ([], ctypes.c_char_p),
         "mla_absorb_q": ([dp, vp, vp, i32, vp, i32, vp], ctypes.c_int),
-        "mla_decode": ([dp, vp, vp, i32, kvp, i32, f32p, f32p, vp], ctypes.c_int),
-        "mla_split_combine": ([dp, i32, f32p, f32p, f32p, f32p, vp], ctypes.c_int),
+        "mla_decode": ([dp, vp, vp, i32, kvp, i32, vp, i32, f32p, vp], ctypes.c_int),
+        "mla_split_combine": ([dp, i32, vp, i32, f32p, f32p, f32p, vp], ctypes.c_int),
         "mla_out_uv": ([dp, f32p, vp, i32, vp, i32, vp], ctypes.c_int),
-        "mla_combine_out_uv": ([dp, i32, f32p, f32p, vp, i32, vp, i32, f32p, vp], ctypes.c_int),
+        "mla_combine_out_uv": ([dp, i32, vp, i32, f32p, vp, i32, vp, i32, f32p, vp], ctypes.c_int),
         "mla_decode_num_splits": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
         "mla_cache_append": ([dp, i32, vp, vp, vp, i32, ctypes.c_float, kvp, vp, ctypes.c_int64, vp], ctypes.c_int),
         "mla_cache_append_workspace_size": ([dp, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
@@ -152,7 +152,7 @@ def _stream(stream) -> Optional[int]:
 
 def _dtype_code(t) -> int:
     import torch
-    return {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16,
+    return {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16, torch.float16: MLA_F16,
             torch.float8_e4m3fn: MLA_FP8_E4M3, torch.uint8: MLA_FP8_E4M3}[t.dtype]
 
 
@@ -196,15 +196,18 @@ def mla_absorb_q(dims: MlaDims, q_nope, w_uk, q_lat, stream=None):
 
 def mla_decode(dims: MlaDims, q_lat, q_rope, cache: PagedCache, num_splits: int, o, lse, stream=None):
     """Decode attention over the paged latent cache; o/lse are o_lat/lse
-    (num_splits == 1) or the per-chunk partials (num_splits > 1)."""
+    (num_splits == 1) or the per-chunk partials (num_splits > 1; o fp32, or
+    fp16 with a bf16 / fp8 cache)."""
     _check("mla_decode", _lib.mla_decode(ctypes.byref(dims), _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat),
-                                         ctypes.byref(cache.kv), int(num_splits), _ptr(o), _ptr(lse),
-                                         _stream(stream)))
+                                         ctypes.byref(cache.kv), int(num_splits), _ptr(o), _dtype_code(o),
+                                         _ptr(lse), _stream(stream)))
 
 
 def mla_split_combine(dims: MlaDims, num_splits: int, o_part, lse_part, o_lat, lse=None, stream=None):
+    """o_lat (fp32) and lse merged from the chunk partials (o_part fp32 or fp16)."""
     _check("mla_split_combine", _lib.mla_split_combine(ctypes.byref(dims), int(num_splits), _ptr(o_part),
-                                                       _ptr(lse_part), _ptr(o_lat), _ptr(lse), _stream(stream)))
+                                                       _dtype_code(o_part), _ptr(lse_part), _ptr(o_lat), _ptr(lse),
+                                                       _stream(stream)))
 
 
 def mla_out_uv(dims: MlaDims, o_lat, w_uv, out, stream=None):
@@ -216,8 +219,9 @@ def mla_out_uv(dims: MlaDims, o_lat, w_uv, out, stream=None):
 def mla_combine_out_uv(dims: MlaDims, num_splits: int, o_part, lse_part, w_uv, out, lse=None, stream=None):
     """out[r][h][:] = W_UV[h] (log-sum-exp merge of the chunk partials), lse = merged lse; out is fp32 or bf16."""
     _check("mla_combine_out_uv", _lib.mla_combine_out_uv(ctypes.byref(dims), int(num_splits), _ptr(o_part),
-                                                         _ptr(lse_part), _ptr(w_uv), _dtype_code(w_uv), _ptr(out),
-                                                         _dtype_code(out), _ptr(lse), _stream(stream)))
+                                                         _dtype_code(o_part), _ptr(lse_part), _ptr(w_uv),
+                                                         _dtype_code(w_uv), _ptr(out), _dtype_code(out), _ptr(lse),
+                                                         _stream(stream)))
 
 
 def mla_decode_num_splits(dims: MlaDims, max_seq_len: int) -> int:

@@ -167,7 +167,7 @@ int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int
 }
 
 int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int32_t q_dtype,
-               const mla_paged_kv* kv, int32_t num_splits, float* o, float* lse, void* stream) {
+               const mla_paged_kv* kv, int32_t num_splits, void* o, int32_t o_dtype, float* lse, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!kv || !q_lat || !q_rope || !o || !lse) return MLA_ERR_NULL;
@@ -182,6 +182,8 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   else return MLA_ERR_DTYPE;
   if (fmt == 2 && !kv->scale) return MLA_ERR_NULL;
   if (fmt != 2 && kv->scale) return MLA_ERR_DTYPE;
+  // fp16 chunk partials: split bf16 / fp8 decodes only
+  if (o_dtype != MLA_F32 && !(o_dtype == MLA_F16 && num_splits > 1 && fmt != 0)) return MLA_ERR_DTYPE;
   if (kv->latent_row_stride < kDL || kv->rope_row_stride < kDR || kv->latent_block_stride < 0 ||
       kv->rope_block_stride < 0 || (fmt == 2 && kv->scale_block_stride < kBlock))
     return MLA_ERR_SHAPE;
@@ -216,6 +218,7 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   a.seq_lens = kv->seq_lens;
   a.o = o;
   a.lse = lse;
+  a.o_f16 = o_dtype == MLA_F16;
   a.batch = dims->batch;
   a.sq = dims->q_per_seq;
   a.heads = dims->heads;
@@ -256,19 +259,21 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   return st;
 }
 
-int mla_split_combine(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
-                      float* o_lat, float* lse, void* stream) {
+int mla_split_combine(const mla_dims* dims, int32_t num_splits, const void* o_part, int32_t part_dtype,
+                      const float* lse_part, float* o_lat, float* lse, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!o_part || !lse_part || !o_lat) return MLA_ERR_NULL;
+  if (part_dtype != MLA_F32 && part_dtype != MLA_F16) return MLA_ERR_DTYPE;
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
   if (!aligned16(o_part) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
   const int rows = dims->q_per_seq * dims->heads;
   const int64_t grid = (int64_t)dims->batch * rows;
   if (grid == 0) return MLA_OK;
   mla::CombineArgs a{o_part, lse_part, o_lat, lse, dims->batch, num_splits, rows};
-  st = launch("mla::split_combine", (const void*)mla::split_combine, dim3((unsigned)((grid + 1) / 2)), dim3(256), a,
-              (hipStream_t)stream);
+  const void* k = part_dtype == MLA_F16 ? (const void*)mla::split_combine<_Float16>
+                                         : (const void*)mla::split_combine<float>;
+  st = launch("mla::split_combine", k, dim3((unsigned)((grid + 1) / 2)), dim3(256), a, (hipStream_t)stream);
   return st;
 }
 
@@ -283,7 +288,7 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
   const int rows = dims->batch * dims->q_per_seq;
   if (rows == 0) return MLA_OK;
   mla::OutUvArgs a{o_lat, w_uv, out, rows, dims->heads, nullptr, nullptr, nullptr, 1, dims->q_per_seq,
-                   out_dtype == MLA_BF16};
+                   out_dtype == MLA_BF16, 0};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
     st = launch("mla::out_uv_mfma", (const void*)mla::out_uv_mfma, dim3((dims->heads + 7) / 8 * 16),
@@ -295,11 +300,13 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
   return st;
 }
 
-int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_part, const float* lse_part,
-                       const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, float* lse, void* stream) {
+int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_part, int32_t part_dtype,
+                       const float* lse_part, const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype,
+                       float* lse, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!o_part || !lse_part || !w_uv || !out) return MLA_ERR_NULL;
+  if (part_dtype != MLA_F32 && part_dtype != MLA_F16) return MLA_ERR_DTYPE;
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
   if (w_dtype != MLA_F32 && w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
@@ -307,11 +314,12 @@ int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const float* o_
   const int rows = dims->batch * dims->q_per_seq;
   if (rows == 0) return MLA_OK;
   mla::OutUvArgs a{nullptr, w_uv, out, rows, dims->heads, o_part, lse_part, lse, num_splits, dims->q_per_seq,
-                   out_dtype == MLA_BF16};
+                   out_dtype == MLA_BF16, part_dtype == MLA_F16};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
-    st = launch("mla::merge_out_uv_mfma", (const void*)mla::merge_out_uv_mfma, dim3((dims->heads + 7) / 8 * 16),
-                dim3(256), a, s);
+    const void* k = part_dtype == MLA_F16 ? (const void*)mla::merge_out_uv_mfma<_Float16>
+                                           : (const void*)mla::merge_out_uv_mfma<float>;
+    st = launch("mla::merge_out_uv_mfma", k, dim3((dims->heads + 7) / 8 * 16), dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;
     st = launch("mla::out_uv_f32<merge>", (const void*)mla::out_uv_f32<true>, dim3(dims->heads, rows), dim3(128), a,

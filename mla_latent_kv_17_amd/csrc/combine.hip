@@ -6,6 +6,7 @@
 // inference time": attention over all earlier tokens).  Chunks that saw no
 // token carry lse_s = -inf and weight 0.
 //
+// The partials are fp32 or fp16 (template argument); sums are fp32.
 // 128 threads x 4 columns per query row, two rows per workgroup.  Up to
 // kBatch chunks are handled per round with every load (log-sum-exps and
 // partial rows) issued before any arithmetic, so a round costs one memory
@@ -15,6 +16,7 @@
 
 namespace mla {
 
+template <typename PT>
 __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
   constexpr int kBatch = 8;
   const int gr = blockIdx.x * 2 + (threadIdx.x >> 7);
@@ -23,7 +25,7 @@ __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
   const int ns = a.num_splits;
   const int c = (threadIdx.x & 127) * 4;
   const float* lp = a.lse_part + (int64_t)b * ns * a.rows + row;
-  const float* op = a.o_part + ((int64_t)b * ns * a.rows + row) * 512 + c;
+  const PT* op = (const PT*)a.o_part + ((int64_t)b * ns * a.rows + row) * 512 + c;
   const int64_t ostride = (int64_t)a.rows * 512;
   float m = -__builtin_inff(), z = 0.f;  // running maximum and sum of exp(lse_s - m)
   f32x4 acc = f32x4{};                   // running sum of exp(lse_s - m) o_s
@@ -34,7 +36,7 @@ __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
     for (int j = 0; j < kBatch; ++j) {
       const bool in = s0 + j < ns;
       ls[j] = in ? lp[(int64_t)(s0 + j) * a.rows] : -__builtin_inff();
-      v[j] = in ? *(const f32x4*)(op + (s0 + j) * ostride) : f32x4{};
+      v[j] = in ? load4(op + (s0 + j) * ostride) : f32x4{};
     }
     float mb = m;
 #pragma unroll
@@ -57,5 +59,8 @@ __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
   if (a.lse && (threadIdx.x & 127) == 0)
     a.lse[(int64_t)b * a.rows + row] = z > 0.f ? m + logf(z) : -__builtin_inff();
 }
+
+template __global__ void split_combine<float>(const CombineArgs a);
+template __global__ void split_combine<_Float16>(const CombineArgs a);
 
 }  // namespace mla

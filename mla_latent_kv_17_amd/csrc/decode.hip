@@ -646,17 +646,24 @@ decode_mfma_bf16(const DecodeArgs a) {
       }
     }
   }
-  // all eight waves write the staged rows: a wave's store covers 1 KB of a
-  // row (the accumulator layout would write 32 rows x 32 bytes per store)
+  // all eight waves write the staged rows: a wave's store covers a row's 2
+  // KB (fp32) or 1 KB (fp16 partials) (the accumulator layout would write 32
+  // rows x 32 bytes per store)
   wg_barrier();
   {
-    float* obase = a.o + slot * (int64_t)rows * 512;
     const int c16 = tid & 127;
+    const int64_t obase = slot * (int64_t)rows * 512;
 #pragma unroll
     for (int k = 0; k < kRows / 4; ++k) {
       const int r = (tid >> 7) + 4 * k;
       const f32x4 o = *(const MLA_LDS f32x4*)(tiles + r * kORow + c16 * 16);
-      if (row_base + r < rows) *(f32x4*)(obase + (int64_t)(row_base + r) * 512 + 4 * c16) = o;
+      const int64_t e = obase + (int64_t)(row_base + r) * 512 + 4 * c16;  // first element of the piece
+      if (row_base + r < rows) {
+        if (a.o_f16)
+          *(f16x4*)((_Float16*)a.o + e) = to_f16x4(o);
+        else
+          *(f32x4*)((float*)a.o + e) = o;
+      }
     }
   }
 }
@@ -1170,17 +1177,24 @@ decode_mfma_fp8(const DecodeArgs a) {
       }
     }
   }
-  // all eight waves write the staged rows: a wave's store covers 1 KB of a
-  // row (the accumulator layout would write 32 rows x 32 bytes per store)
+  // all eight waves write the staged rows: a wave's store covers a row's 2
+  // KB (fp32) or 1 KB (fp16 partials) (the accumulator layout would write 32
+  // rows x 32 bytes per store)
   wg_barrier();
   {
-    float* obase = a.o + slot * (int64_t)rows * 512;
     const int c16 = tid & 127;
+    const int64_t obase = slot * (int64_t)rows * 512;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int r = (tid >> 7) + 4 * k;
       const f32x4 o = *(const MLA_LDS f32x4*)(tiles + r * kORow + c16 * 16);
-      if (row_base + r < rows) *(f32x4*)(obase + (int64_t)(row_base + r) * 512 + 4 * c16) = o;
+      const int64_t e = obase + (int64_t)(row_base + r) * 512 + 4 * c16;  // first element of the piece
+      if (row_base + r < rows) {
+        if (a.o_f16)
+          *(f16x4*)((_Float16*)a.o + e) = to_f16x4(o);
+        else
+          *(f32x4*)((float*)a.o + e) = o;
+      }
     }
   }
 }
@@ -1345,7 +1359,7 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
     m = mt;
   }
   const int64_t slot = (int64_t)b * a.num_splits + split;
-  float* orow = a.o + (slot * a.rows + row) * 512;
+  float* orow = (float*)a.o + (slot * a.rows + row) * 512;  // fp32 only (the launcher refuses fp16 here)
   const float inv = l > 0.f ? 1.f / l : 0.f;
   orow[c2] = o0 * inv;
   orow[c2 + 1] = o1 * inv;

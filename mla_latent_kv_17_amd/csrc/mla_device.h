@@ -14,6 +14,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -48,6 +49,18 @@ template <bool kHi>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi);
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four consecutive chunk-partial values as fp32 (fp32 or fp16 storage; the
+// pointer is 16- or 8-byte aligned).
+__device__ __forceinline__ f32x4 load4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load4(const _Float16* p) {
+  const f16x4 h = *(const f16x4*)p;
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+// Four fp32 values rounded to nearest-even binary16.
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 v) {
+  return f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
 }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {

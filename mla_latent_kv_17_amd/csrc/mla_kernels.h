@@ -16,8 +16,9 @@ struct DecodeArgs {
   int64_t lat_bs, lat_rs, rope_bs, rope_rs, scale_bs;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* o;    // o_lat [slot][rows][512], slot = b * num_splits + split
+  void* o;     // o_lat [slot][rows][512], slot = b * num_splits + split: fp32, or fp16 if o_f16
   float* lse;  // [slot][rows]
+  int o_f16;   // 1: chunk partials written as binary16 (round to nearest even)
   int batch, sq, heads, rows, row_blocks, num_splits, units, max_blocks;
   float softmax_scale, scale_log2;
 };
@@ -40,12 +41,13 @@ template <bool kOutBf16>
 __global__ void absorb_q_f32(const AbsorbArgs a);    // fp32 inputs
 
 struct CombineArgs {
-  const float* o_part;    // [B][ns][S_q][H][512]
+  const void* o_part;     // [B][ns][S_q][H][512], fp32 or fp16 (the kernel's template argument)
   const float* lse_part;  // [B][ns][S_q][H]
   float* o_lat;           // [B*S_q][H][512]
   float* lse;             // [B*S_q][H] or null
   int batch, num_splits, rows;  // rows = S_q * H
 };
+template <typename PT>  // partial type: float or _Float16
 __global__ void split_combine(const CombineArgs a);
 
 struct OutUvArgs {
@@ -54,13 +56,15 @@ struct OutUvArgs {
   void* out;              // [R][H][128], fp32 or (out_bf16) bf16 bits
   int rows, heads;        // R = B * S_q
   // merged form: o_lat = log-sum-exp merge of the chunk partials
-  const float* o_part;    // [B][ns][S_q][H][512]
+  const void* o_part;     // [B][ns][S_q][H][512], fp32 or fp16 (part_f16)
   const float* lse_part;  // [B][ns][S_q][H]
   float* lse;             // [R][H] or null
   int num_splits, sq;
   int out_bf16;           // 1: round the fp32 sums to bf16 (nearest even)
+  int part_f16;           // merged form: 1 if the partials are fp16
 };
 __global__ void out_uv_mfma(const OutUvArgs a);        // bf16 weights, hi/lo split of o_lat
+template <typename PT>  // partial type: float or _Float16
 __global__ void merge_out_uv_mfma(const OutUvArgs a);  // the same with the chunk merge on the way
 template <bool kMerge>
 __global__ void out_uv_f32(const OutUvArgs a);   // fp32 weights

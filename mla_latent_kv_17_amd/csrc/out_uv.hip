@@ -114,7 +114,9 @@ __global__ void __launch_bounds__(256) out_uv_mfma(const OutUvArgs a) {
 //    64 x 128 weight slice in registers); the four partial tiles are summed
 //    through LDS.
 // More than four chunks take further rounds of two; more than 64 recompute
-// their weights from the row's max and sum.
+// their weights from the row's max and sum.  The partials are fp32 or fp16
+// (template argument; fp16 halves the bytes read), converted to fp32 on load.
+template <typename PT>
 __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
   constexpr int kPad = 33;  // LDS row stride (floats) of the partial tiles
   constexpr int kW = 64;    // chunk weights held in LDS per round
@@ -154,15 +156,15 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) lv[k] = lp[(int64_t)min(lj + 8 * k, ns - 1) * rs];
     asm volatile("" ::: "memory");  // keep the lse loads ahead of the partial rows
-    const float* vrow[16];  // chunk 0 of the thread's rows (clamped to a real row)
+    const PT* vrow[16];  // chunk 0 of the thread's rows (clamped to a real row)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vrow[i] = a.o_part + prow(min(m0 + r0 + 2 * i, a.rows - 1)) * 512 + 4 * c;
+    for (int i = 0; i < 16; ++i) vrow[i] = (const PT*)a.o_part + prow(min(m0 + r0 + 2 * i, a.rows - 1)) * 512 + 4 * c;
     f32x4 v0[kF][16];
 #pragma unroll
     for (int jj = 0; jj < kF; ++jj) {
       const int64_t so = (int64_t)min(jj, ns - 1) * cs;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v0[jj][i] = *(const f32x4*)(vrow[i] + so);
+      for (int i = 0; i < 16; ++i) v0[jj][i] = load4(vrow[i] + so);
     }
     // (an empty use of every lse value here keeps its load where it is, ahead
     // of the partial rows, instead of being moved into the branch below)
@@ -236,7 +238,7 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
       for (int jj = 0; jj < 2; ++jj) {
         const int64_t so = (int64_t)min(s0 + jj, ns - 1) * cs;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[jj][i] = *(const f32x4*)(vrow[i] + so);
+        for (int i = 0; i < 16; ++i) v[jj][i] = load4(vrow[i] + so);
       }
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
@@ -305,7 +307,7 @@ __global__ void __launch_bounds__(128) out_uv_f32(const OutUvArgs a) {
     const int64_t rs = (int64_t)a.sq * a.heads;
     const int64_t base = (int64_t)b * a.num_splits * rs + (int64_t)q * a.heads + h;
     const float* lp = a.lse_part + base;
-    const float* op = a.o_part + base * 512 + 4 * d;
+    const int64_t op = base * 512 + 4 * d;  // element index of the chunk-0 partial
     float m = -__builtin_inff();
     for (int s = 0; s < a.num_splits; ++s) m = fmaxf(m, lp[s * rs]);
     f32x4 x = f32x4{};
@@ -316,7 +318,8 @@ __global__ void __launch_bounds__(128) out_uv_f32(const OutUvArgs a) {
         if (ls == -__builtin_inff()) continue;
         const float e = expf(ls - m);
         z += e;
-        x += e * *(const f32x4*)(op + s * rs * 512);
+        const int64_t i = op + s * rs * 512;
+        x += e * (a.part_f16 ? load4((const _Float16*)a.o_part + i) : load4((const float*)a.o_part + i));
       }
     }
     *(f32x4*)&xs[4 * d] = x * (z > 0.f ? 1.f / z : 0.f);
@@ -338,6 +341,8 @@ __global__ void __launch_bounds__(128) out_uv_f32(const OutUvArgs a) {
   store_out(a.out, ((int64_t)r * a.heads + h) * 128 + d, acc, a.out_bf16);
 }
 
+template __global__ void merge_out_uv_mfma<float>(const OutUvArgs);
+template __global__ void merge_out_uv_mfma<_Float16>(const OutUvArgs);
 template __global__ void out_uv_f32<false>(const OutUvArgs);
 template __global__ void out_uv_f32<true>(const OutUvArgs);
 

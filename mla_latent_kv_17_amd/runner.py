@@ -82,8 +82,10 @@ class DecodeStep:
         self.lse = torch.empty((R, H), dtype=torch.float32, device=device)
         self.out = torch.empty((R, H, 128), dtype=torch.float32, device=device)
         if num_splits > 1:
-            self.o_part = torch.empty((dev.batch, num_splits, dev.q_per_seq, H, 512), dtype=torch.float32,
-                                      device=device)
+            # chunk partials: fp16 for the bf16 / fp8 caches (half the bytes
+            # written by the decode and read by the merge), fp32 for fp32
+            part = torch.float32 if dev.wl.cache_dtype == "f32" else torch.float16
+            self.o_part = torch.empty((dev.batch, num_splits, dev.q_per_seq, H, 512), dtype=part, device=device)
             self.lse_part = torch.empty((dev.batch, num_splits, dev.q_per_seq, H), dtype=torch.float32,
                                         device=device)
         else:

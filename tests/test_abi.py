@@ -38,15 +38,15 @@ def test_source_hash_matches_the_sources():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 9
+    assert M.abi_version() == 10
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
 
 
-def _call_decode(dims, kv, ns=1, q=0x1000, qr=0x2000, o=0x3000, lse=0x4000, qdt=M.MLA_BF16):
+def _call_decode(dims, kv, ns=1, q=0x1000, qr=0x2000, o=0x3000, lse=0x4000, qdt=M.MLA_BF16, odt=M.MLA_F32):
     return M._lib.mla_decode(ctypes.byref(dims), q, qr, qdt, ctypes.byref(kv) if kv is not None else None,
-                             ns, o, lse, None)
+                             ns, o, odt, lse, None)
 
 
 def _kv(latent=0x10000, rope=0x10000 + 1024, ldt=M.MLA_BF16, rdt=M.MLA_BF16, scale=None, bs=64):
@@ -68,6 +68,10 @@ def test_decode_validation():
     assert _call_decode(d, _kv(), q=0x1004) == M.MLA_ERR_ALIGN
     bad = M.make_dims(2, 129, 128)
     assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
+    # fp16 partials: only for split decodes of bf16 / fp8 caches
+    assert _call_decode(d, _kv(), ns=1, odt=M.MLA_F16) == M.MLA_ERR_DTYPE
+    assert _call_decode(d, _kv(), ns=4, odt=M.MLA_BF16) == M.MLA_ERR_DTYPE
+    assert _call_decode(d, _kv(ldt=M.MLA_F32, rdt=M.MLA_F32), ns=4, qdt=M.MLA_F32, odt=M.MLA_F16) == M.MLA_ERR_DTYPE
     bad = M.make_dims(2, 0, 128)
     assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
     bad = M.MlaDims(2, 1, 128, 256, 64, 128, 0.1)
@@ -87,16 +91,20 @@ def test_other_entry_points_validation():
     assert L.mla_absorb_q(ctypes.byref(d), 0x1000, 0x1000, M.MLA_FP8_E4M3, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_DTYPE
     assert L.mla_absorb_q(ctypes.byref(d), 0x1002, 0x1000, M.MLA_BF16, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_ALIGN
     assert L.mla_absorb_q(None, 0x1000, 0x1000, M.MLA_BF16, 0x2000, M.MLA_BF16, None) == M.MLA_ERR_NULL
-    assert L.mla_split_combine(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, None, None) == M.MLA_ERR_SPLITS
-    assert L.mla_split_combine(ctypes.byref(d), 4, None, 0x2000, 0x3000, None, None) == M.MLA_ERR_NULL
-    assert L.mla_split_combine(ctypes.byref(d), 4, 0x1004, 0x2000, 0x3000, None, None) == M.MLA_ERR_ALIGN
+    F32, F16 = M.MLA_F32, M.MLA_F16
+    assert L.mla_split_combine(ctypes.byref(d), 0, 0x1000, F32, 0x2000, 0x3000, None, None) == M.MLA_ERR_SPLITS
+    assert L.mla_split_combine(ctypes.byref(d), 4, None, F32, 0x2000, 0x3000, None, None) == M.MLA_ERR_NULL
+    assert L.mla_split_combine(ctypes.byref(d), 4, 0x1004, F16, 0x2000, 0x3000, None, None) == M.MLA_ERR_ALIGN
+    assert L.mla_split_combine(ctypes.byref(d), 4, 0x1000, M.MLA_BF16, 0x2000, 0x3000, None, None) == M.MLA_ERR_DTYPE
     assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_FP8_E4M3, 0x3000, M.MLA_F32, None) == M.MLA_ERR_DTYPE
     assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_BF16, 0x3000, M.MLA_FP8_E4M3, None) == M.MLA_ERR_DTYPE
     assert L.mla_out_uv(ctypes.byref(d), None, 0x2000, M.MLA_BF16, 0x3000, M.MLA_F32, None) == M.MLA_ERR_NULL
     assert L.mla_out_uv(ctypes.byref(d), 0x1000, 0x2000, M.MLA_BF16, 0x3008, M.MLA_BF16, None) == M.MLA_ERR_ALIGN
-    assert L.mla_combine_out_uv(ctypes.byref(d), 4, 0x1000, 0x2000, 0x3000, M.MLA_BF16, 0x4000, 7, None,
+    assert L.mla_combine_out_uv(ctypes.byref(d), 4, 0x1000, F32, 0x2000, 0x3000, M.MLA_BF16, 0x4000, 7, None,
                                 None) == M.MLA_ERR_DTYPE
-    assert L.mla_combine_out_uv(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, M.MLA_BF16, 0x4000, M.MLA_F32, None,
+    assert L.mla_combine_out_uv(ctypes.byref(d), 4, 0x1000, M.MLA_FP8_E4M3, 0x2000, 0x3000, M.MLA_BF16, 0x4000,
+                                M.MLA_F32, None, None) == M.MLA_ERR_DTYPE
+    assert L.mla_combine_out_uv(ctypes.byref(d), 0, 0x1000, F16, 0x2000, 0x3000, M.MLA_BF16, 0x4000, M.MLA_F32, None,
                                 None) == M.MLA_ERR_SPLITS
     out = ctypes.c_int32(0)
     assert L.mla_decode_num_splits(ctypes.byref(d), 100, None) == M.MLA_ERR_NULL

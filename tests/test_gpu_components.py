@@ -113,17 +113,25 @@ def _combine_case(B, ns, Sq, heads, seed):
     return o_part, lse_part
 
 
+def _as_part(o_part, part):
+    """The partials in the storage dtype of the case: fp32 as drawn, or their
+    fp16 rounding (the oracle then merges exactly those fp16 values)."""
+    return o_part if part == "f32" else o_part.astype(np.float16)
+
+
+@pytest.mark.parametrize("part", ["f32", "f16"])
 @pytest.mark.parametrize("B,ns,Sq,heads", [(3, 5, 2, 128), (2, 64, 1, 128), (1, 1024, 1, 16), (4, 1, 1, 16)])
-def test_split_combine(B, ns, Sq, heads):
+def test_split_combine(B, ns, Sq, heads, part):
     import torch
     import mla_latent_kv_17_amd as M
-    print(f"[case] split_combine B={B} ns={ns} Sq={Sq} H={heads}", flush=True)
+    print(f"[case] split_combine B={B} ns={ns} Sq={Sq} H={heads} partials {part}", flush=True)
     o_part, lse_part = _combine_case(B, ns, Sq, heads, 3300 + ns)
+    o_part = _as_part(o_part, part)
     o_lat = torch.empty((B * Sq, heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((B * Sq, heads), dtype=torch.float32, device="cuda")
     M.mla_split_combine(M.make_dims(B, Sq, heads), ns, torch.from_numpy(o_part).cuda(),
                         torch.from_numpy(lse_part).cuda(), o_lat, lse)
-    o_ref, lse_ref = O.combine_partials(o_part, lse_part)
+    o_ref, lse_ref = O.combine_partials(o_part.astype(np.float64), lse_part)
     got = o_lat.cpu().numpy().reshape(B, Sq, heads, 512)
     gl = lse.cpu().numpy().reshape(B, Sq, heads)
     assert np.isfinite(got).all()
@@ -134,16 +142,17 @@ def test_split_combine(B, ns, Sq, heads):
     assert np.max(np.abs(gl[~none] - lse_ref[~none])) <= 1e-5 * max(1.0, np.abs(lse_ref[~none]).max())
 
 
+@pytest.mark.parametrize("part", ["f32", "f16"])
 @pytest.mark.parametrize("B,ns,Sq,heads,wdt", [(3, 5, 2, 128, "bf16"), (37, 3, 1, 100, "bf16"),
                                                (2, 64, 1, 128, "bf16"), (5, 7, 2, 16, "f32")])
-def test_combine_out_uv(B, ns, Sq, heads, wdt):
+def test_combine_out_uv(B, ns, Sq, heads, wdt, part):
     """The merge fused into the projection against the fp64 merge followed by
     the fp64 projection, and against mla_split_combine + mla_out_uv."""
     import torch
     import mla_latent_kv_17_amd as M
-    print(f"[case] combine_out_uv B={B} ns={ns} Sq={Sq} H={heads} w={wdt}", flush=True)
+    print(f"[case] combine_out_uv B={B} ns={ns} Sq={Sq} H={heads} w={wdt} partials {part}", flush=True)
     o_part, lse_part = _combine_case(B, ns, Sq, heads, 3400 + ns)
-    o_part *= np.float32(0.05)
+    o_part = _as_part(o_part * np.float32(0.05), part)
     rng = np.random.default_rng(3500 + heads)
     wf = rng.standard_normal((heads, 128, 512), dtype=np.float32) * np.float32(1.0 / math.sqrt(512))
     if wdt == "bf16":
@@ -156,7 +165,7 @@ def test_combine_out_uv(B, ns, Sq, heads, wdt):
     out = torch.empty((B * Sq, heads, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B * Sq, heads), dtype=torch.float32, device="cuda")
     M.mla_combine_out_uv(dims, ns, op, lp, w_dev, out, lse)
-    o_ref, lse_ref = O.combine_partials(o_part, lse_part)
+    o_ref, lse_ref = O.combine_partials(o_part.astype(np.float64), lse_part)
     ref = O.project_output(o_ref.reshape(B * Sq, heads, 512), w64)
     got, gl = out.cpu().numpy(), lse.cpu().numpy().reshape(B, Sq, heads)
     assert np.isfinite(got).all()
