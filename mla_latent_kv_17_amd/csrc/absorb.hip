@@ -132,22 +132,39 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(const AbsorbArgs a) {
 }
 
 // fp32 inputs: one thread per latent column, fp32 FMA over d_head.
+// fp32 inputs: workgroup = (head, block of 64 latent columns); wave w
+// holds the weight rows d = 32w .. 32w+31 of the block in registers (lane l:
+// column c0 + l, 32 coalesced loads issued together) and reuses them for
+// every query row; the four waves' partial sums over their rows of d meet
+// in LDS.
 template <bool kOutBf16>
 __global__ void __launch_bounds__(256) absorb_q_f32(const AbsorbArgs a) {
   __shared__ float qs[128];
-  const int h = blockIdx.x, r = blockIdx.z;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  const float* q = (const float*)a.q_nope + ((int64_t)r * a.heads + h) * 128;
-  if (threadIdx.x < 128) qs[threadIdx.x] = q[threadIdx.x];
-  __syncthreads();
-  const float* w = (const float*)a.w + (int64_t)h * 128 * 512 + c;
-  float acc = 0.f;
-  for (int d = 0; d < 128; ++d) acc = fmaf(w[(int64_t)d * 512], qs[d], acc);
-  const int64_t off = ((int64_t)r * a.heads + h) * 512 + c;
-  if (kOutBf16)
-    ((uint16_t*)a.q_lat)[off] = f32_to_bf16_bits(acc);
-  else
-    ((float*)a.q_lat)[off] = acc;
+  __shared__ float part[4][64];
+  const int h = blockIdx.x >> 3, c0 = (blockIdx.x & 7) * 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* w = (const float*)a.w + ((int64_t)h * 128 + 32 * wave) * 512 + c0 + lane;
+  float wr[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) wr[d] = w[(int64_t)d * 512];
+  for (int r = 0; r < a.rows; ++r) {
+    const float* q = (const float*)a.q_nope + ((int64_t)r * a.heads + h) * 128;
+    if (threadIdx.x < 128) qs[threadIdx.x] = q[threadIdx.x];
+    __syncthreads();
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc = fmaf(wr[d], qs[32 * wave + d], acc);
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      const float v = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+      const int64_t off = ((int64_t)r * a.heads + h) * 512 + c0 + lane;
+      if (kOutBf16)
+        ((uint16_t*)a.q_lat)[off] = f32_to_bf16_bits(v);
+      else
+        ((float*)a.q_lat)[off] = v;
+    }
+  }
 }
 
 template __global__ void absorb_q_mfma<true>(const AbsorbArgs);

@@ -156,7 +156,7 @@ int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int
     else
       st = launch("mla::absorb_q_mfma<false>", (const void*)mla::absorb_q_mfma<false>, grid, dim3(256), a, s);
   } else {
-    dim3 grid(dims->heads, kDL / 256, rows);
+    dim3 grid(dims->heads * (kDL / 64));  // (head, block of 64 latent columns)
     if (rows > 65535) return MLA_ERR_SHAPE;
     if (q_lat_dtype == MLA_BF16)
       st = launch("mla::absorb_q_f32<true>", (const void*)mla::absorb_q_f32<true>, grid, dim3(256), a, s);
@@ -273,7 +273,7 @@ int mla_split_combine(const mla_dims* dims, int32_t num_splits, const void* o_pa
   mla::CombineArgs a{o_part, lse_part, o_lat, lse, dims->batch, num_splits, rows};
   const void* k = part_dtype == MLA_F16 ? (const void*)mla::split_combine<_Float16>
                                          : (const void*)mla::split_combine<float>;
-  st = launch("mla::split_combine", k, dim3((unsigned)((grid + 1) / 2)), dim3(256), a, (hipStream_t)stream);
+  st = launch("mla::split_combine", k, dim3((unsigned)grid), dim3(256), a, (hipStream_t)stream);
   return st;
 }
 
@@ -295,7 +295,8 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
                 dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;
-    st = launch("mla::out_uv_f32", (const void*)mla::out_uv_f32<false>, dim3(dims->heads, rows), dim3(128), a, s);
+    st = launch("mla::out_uv_f32", (const void*)mla::out_uv_f32<false>, dim3(dims->heads * (kDH / 16)), dim3(256), a,
+                s);
   }
   return st;
 }
@@ -322,8 +323,8 @@ int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_p
     st = launch("mla::merge_out_uv_mfma", k, dim3((dims->heads + 7) / 8 * 16), dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;
-    st = launch("mla::out_uv_f32<merge>", (const void*)mla::out_uv_f32<true>, dim3(dims->heads, rows), dim3(128), a,
-                s);
+    st = launch("mla::out_uv_f32<merge>", (const void*)mla::out_uv_f32<true>, dim3(dims->heads * (kDH / 16)),
+                dim3(256), a, s);
   }
   return st;
 }

@@ -296,49 +296,71 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
   }
 }
 
-// fp32 weights: one thread per output element, fp32 FMA over the latent.
+// fp32 weights: workgroup = (head, block of 16 output dims d); wave w holds
+// the weight rows d0 + 4w .. d0 + 4w + 3 in registers (lane l: columns
+// 8l .. 8l+7 of each, a row read as 2 KB per wave) and reuses them for every
+// query row: per row the wave's four dot products are reduced across the
+// wave (DPP).  o_lat comes from memory, or (kMerge) is merged from the chunk
+// partials into LDS first (weights exp(lse_s - max) over their sum, as in
+// split_combine).
 template <bool kMerge>
-__global__ void __launch_bounds__(128) out_uv_f32(const OutUvArgs a) {
-  __shared__ float xs[512];
-  const int h = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
-  if constexpr (kMerge) {
-    // thread d merges columns 4d .. 4d+3 (same weights as merge_row)
-    const int b = r / a.sq, q = r - b * a.sq;
-    const int64_t rs = (int64_t)a.sq * a.heads;
-    const int64_t base = (int64_t)b * a.num_splits * rs + (int64_t)q * a.heads + h;
-    const float* lp = a.lse_part + base;
-    const int64_t op = base * 512 + 4 * d;  // element index of the chunk-0 partial
-    float m = -__builtin_inff();
-    for (int s = 0; s < a.num_splits; ++s) m = fmaxf(m, lp[s * rs]);
-    f32x4 x = f32x4{};
-    float z = 0.f;
-    if (m != -__builtin_inff()) {
-      for (int s = 0; s < a.num_splits; ++s) {
-        const float ls = lp[s * rs];
-        if (ls == -__builtin_inff()) continue;
-        const float e = expf(ls - m);
-        z += e;
-        const int64_t i = op + s * rs * 512;
-        x += e * (a.part_f16 ? load4((const _Float16*)a.o_part + i) : load4((const float*)a.o_part + i));
+__global__ void __launch_bounds__(256) out_uv_f32(const OutUvArgs a) {
+  __shared__ __attribute__((aligned(16))) float xs[512];
+  const int h = blockIdx.x >> 3, d0 = (blockIdx.x & 7) * 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  f32x4 wr[4][2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float* w = (const float*)a.w + ((int64_t)h * 128 + d0 + 4 * wave + k) * 512 + 8 * lane;
+    wr[k][0] = *(const f32x4*)w;
+    wr[k][1] = *(const f32x4*)(w + 4);
+  }
+  for (int r = 0; r < a.rows; ++r) {
+    __syncthreads();  // xs of the previous row is read
+    if constexpr (kMerge) {
+      if (tid < 128) {
+        // thread t merges columns 4t .. 4t+3
+        const int b = r / a.sq, q = r - b * a.sq;
+        const int64_t rs = (int64_t)a.sq * a.heads;
+        const int64_t base = (int64_t)b * a.num_splits * rs + (int64_t)q * a.heads + h;
+        const float* lp = a.lse_part + base;
+        const int64_t op = base * 512 + 4 * tid;  // element index of the chunk-0 partial
+        float m = -__builtin_inff();
+        for (int s = 0; s < a.num_splits; ++s) m = fmaxf(m, lp[s * rs]);
+        f32x4 x = f32x4{};
+        float z = 0.f;
+        if (m != -__builtin_inff()) {
+          for (int s = 0; s < a.num_splits; ++s) {
+            const float ls = lp[s * rs];
+            if (ls == -__builtin_inff()) continue;
+            const float e = expf(ls - m);
+            z += e;
+            const int64_t i = op + s * rs * 512;
+            x += e * (a.part_f16 ? load4((const _Float16*)a.o_part + i) : load4((const float*)a.o_part + i));
+          }
+        }
+        *(f32x4*)&xs[4 * tid] = x * (z > 0.f ? 1.f / z : 0.f);
+        if (a.lse && tid == 0 && (blockIdx.x & 7) == 0)
+          a.lse[(int64_t)r * a.heads + h] = z > 0.f ? m + logf(z) : -__builtin_inff();
       }
+    } else {
+      if (tid < 128) *(f32x4*)&xs[4 * tid] = *(const f32x4*)(a.o_lat + ((int64_t)r * a.heads + h) * 512 + 4 * tid);
     }
-    *(f32x4*)&xs[4 * d] = x * (z > 0.f ? 1.f / z : 0.f);
-    if (a.lse && d == 0) a.lse[(int64_t)r * a.heads + h] = z > 0.f ? m + logf(z) : -__builtin_inff();
-  } else {
-    const float* x = a.o_lat + ((int64_t)r * a.heads + h) * 512;
-    for (int i = threadIdx.x; i < 512; i += 128) xs[i] = x[i];
+    __syncthreads();
+    const f32x4 x0 = *(const f32x4*)&xs[8 * lane], x1 = *(const f32x4*)&xs[8 * lane + 4];
+    float acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v = fmaf(wr[k][0][e], x0[e], fmaf(wr[k][1][e], x1[e], v));
+      acc[k] = wave_sum_rows(v);
+    }
+    if (lane < 4) {
+      const float v = lane == 0 ? acc[0] : lane == 1 ? acc[1] : lane == 2 ? acc[2] : acc[3];
+      store_out(a.out, ((int64_t)r * a.heads + h) * 128 + d0 + 4 * wave + lane, v, a.out_bf16);
+    }
   }
-  __syncthreads();
-  const float* w = (const float*)a.w + ((int64_t)h * 128 + d) * 512;
-  float acc = 0.f;
-  for (int c = 0; c < 512; c += 4) {
-    const f32x4 wv = *(const f32x4*)(w + c);
-    acc = fmaf(wv[0], xs[c], acc);
-    acc = fmaf(wv[1], xs[c + 1], acc);
-    acc = fmaf(wv[2], xs[c + 2], acc);
-    acc = fmaf(wv[3], xs[c + 3], acc);
-  }
-  store_out(a.out, ((int64_t)r * a.heads + h) * 128 + d, acc, a.out_bf16);
 }
 
 template __global__ void merge_out_uv_mfma<float>(const OutUvArgs);
