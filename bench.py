@@ -42,7 +42,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_bf16_b32_h128_t4k_counters.jso
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "mla_device.h", "mla_kernels.h"):
+    for f in ("decode.hip", "mla_copy.h", "mla_device.h", "mla_kernels.h"):
         h.update(open(os.path.join(ROOT, "mla_latent_kv_17_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -168,6 +168,63 @@ def blas_vendor() -> str:
         return "unknown"
 
 
+def forms_sweep(args):
+    """Both forms of the attention on the same prefill chunk, per S_q: the
+    absorbed one (absorb_q + decode + merge / out_uv, splits chosen by the
+    library) and the explicit one (rebuild_kv + attend_explicit).  Each step
+    timed alone after an eviction read, median of --steps."""
+    import numpy as np
+    import torch
+    import mla_inputs as MI
+    from mla_latent_kv_17_amd import MLA_BF16, MLA_FORM_EXPLICIT, mla_attention_form
+    from mla_latent_kv_17_amd.runner import DecodeStep, DeviceInputs, ExplicitStep
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush.fill_(1.0)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in ev:
+            torch.sum(flush)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    for sq in args.forms:
+        wl = MI.WORKLOADS["bf16_b32_h128_t4k"].scaled(name=f"prefill_b{args.forms_batch}_sq{sq}",
+                                                      batch=args.forms_batch, q_per_seq=sq,
+                                                      seq_len=args.forms_context, num_splits=0, seed=3000 + sq)
+        print(f"[forms] generating {wl.name}", file=sys.stderr, flush=True)
+        inp = MI.generate(wl)
+        dev = DeviceInputs(inp)
+        absorbed, explicit = DecodeStep(dev, 0), ExplicitStep(dev)
+        a_us = timed(absorbed.run)
+        e_us = timed(explicit.run)
+        pairs = sum(max(0, int(L) - (sq - 1 - i)) for L in inp.seq_lens for i in range(sq))
+        kv = int(inp.seq_lens.astype(np.int64).sum())
+        H = wl.heads
+        a_flops = pairs * H * 2 * (576 + 512) + 2 * wl.batch * sq * H * 2 * 128 * 512
+        rebuild_flops = kv * H * 2 * 2 * 128 * 512
+        e_flops = pairs * H * 2 * (192 + 128) + rebuild_flops
+        diff = (explicit.out - absorbed.out).float().norm() / absorbed.out.float().norm()
+        print(json.dumps({
+            "forms": wl.name, "q_per_seq": sq, "batch": wl.batch, "context": args.forms_context, "heads": H,
+            "absorbed_us": a_us, "explicit_us": e_us, "absorbed_splits": absorbed.num_splits,
+            "absorbed_tflops": a_flops / (a_us * 1e-6) / 1e12, "explicit_tflops": e_flops / (e_us * 1e-6) / 1e12,
+            "absorbed_gflop": a_flops / 1e9, "explicit_gflop": e_flops / 1e9, "rebuild_gflop": rebuild_flops / 1e9,
+            "faster": "explicit" if e_us < a_us else "absorbed",
+            "library_choice": "explicit" if mla_attention_form(dev.dims, MLA_BF16) == MLA_FORM_EXPLICIT
+            else "absorbed",
+            "rel_l2_explicit_vs_absorbed": float(diff),
+            "timing": f"median of {args.steps} steps, each after a 1 GiB eviction read, HIP events"}), flush=True)
+        del absorbed, explicit, dev, inp
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +253,12 @@ def main():
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--rotate-gib", type=float, default=1.5,
                     help="total size of the cache copies the decode timing rotates over")
+    ap.add_argument("--forms", type=int, nargs="*", default=None,
+                    help="time the absorbed and the explicit form (keys and values rebuilt) at these query "
+                         "tokens per sequence on one bf16 prefill chunk (B=--forms-batch, H=128, a "
+                         "--forms-context-token context incl. the chunk), one JSON line each, and exit")
+    ap.add_argument("--forms-batch", type=int, default=1)
+    ap.add_argument("--forms-context", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (the decode shards by "
@@ -211,6 +274,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
+    if args.forms is not None:
+        forms_sweep(args)
         return
     import mla_inputs as MI
     from mla_latent_kv_17_amd import mla_decode

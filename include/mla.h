@@ -65,11 +65,13 @@ extern "C" {
 
 /* 2: adds mla_combine_out_uv; 3: adds the MLA_CHECK validation of mla_decode;
  * 4: adds out_dtype to mla_out_uv and mla_combine_out_uv; 5: adds mla_cache_append;
- * 6: q_per_seq up to MLA_MAX_Q_PER_SEQ (was 2); 7: adds mla_moe_gate;
+ * 6: q_per_seq up to 128 (was 2); 7: adds mla_moe_gate;
  * 8: adds mla_source_hash; 9: adds mla_cache_append_static and MLA_ERR_SCRATCH;
  * 10: the chunk partials of mla_decode may be fp16 (MLA_F16): o_dtype of
- * mla_decode, part_dtype of mla_split_combine and mla_combine_out_uv */
-#define MLA_ABI_VERSION 10
+ * mla_decode, part_dtype of mla_split_combine and mla_combine_out_uv;
+ * 11: q_per_seq up to 4096; adds the explicit form (mla_attend_explicit,
+ * mla_attend_explicit_workspace_size) and mla_attention_form */
+#define MLA_ABI_VERSION 11
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -92,17 +94,13 @@ typedef enum mla_status {
 
 #define MLA_MAX_SPLITS 1024
 /* Query tokens per sequence in one call (multi-token decode: speculative
- * tokens, short prefill chunks).  The absorbed form costs 2 (576 + 512)
- * flops per (query, token, head) against 2 (128 x 512) x 2 per (token, head)
- * plus 2 (192 + 128) per (query, token, head) for rebuilding K and V
- * explicitly: the absorbed form is the cheaper one below about 171 query
- * tokens per sequence, so it is the only form here. */
-#define MLA_MAX_Q_PER_SEQ 128
+ * tokens, prefill chunks). */
+#define MLA_MAX_Q_PER_SEQ 4096
 
 /* Static description of one decode batch. */
 typedef struct mla_dims {
   int32_t batch;       /* B: sequences                                       */
-  int32_t q_per_seq;   /* S_q: query tokens per sequence (1..128)            */
+  int32_t q_per_seq;   /* S_q: query tokens per sequence (1..4096)           */
   int32_t heads;       /* H: attention heads (1..1024)                       */
   int32_t d_latent;    /* 512                                                */
   int32_t d_rope;      /* 64                                                 */
@@ -317,6 +315,60 @@ int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top
 /* Bytes of workspace mla_moe_gate needs for these sizes (host-only). */
 int mla_moe_gate_workspace_size(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t in_dtype,
                                 int64_t* bytes);
+
+/* Attention in the explicit form (same page, section 1, "Store a latent,
+ * rebuild the keys and values" and the formula box "MLA: compress once,
+ * reconstruct in attention"): per sequence and head the keys and values are
+ * rebuilt from the cached latent,
+ *   k_t = [W_UK[h] c_t ; k^R_t]  (192 values),   v_t = W_UV[h] c_t  (128 values),
+ * and attention runs on them:
+ *   s_t = ([q_nope ; q_rope] . k_t) * softmax_scale,  t visible to the query,
+ *   out = sum_t softmax(s)_t v_t,   lse = ln sum_t exp(s_t).
+ * The same result as mla_absorb_q + mla_decode + mla_split_combine +
+ * mla_out_uv (the absorbed form is this algebra regrouped) at another cost:
+ * the absorbed form spends 2 (576 + 512) flops per (query token, cached
+ * token, head); this one 2 (192 + 128) per (query token, cached token, head)
+ * plus 2 x 2 x 128 x 512 per (cached token, head) to rebuild K and V once.
+ * With many query tokens per sequence (chunked prefill) this form is cheaper;
+ * mla_attention_form says which to use.
+ * q_nope: [batch*q_per_seq][heads][d_head] BF16 (in_dtype must be BF16)
+ * q_rope: [batch*q_per_seq][heads][d_rope] BF16
+ * kv:     a BF16 latent + BF16 rope cache (other caches: MLA_ERR_DTYPE)
+ * w_uk, w_uv: [heads][d_head][d_latent] BF16
+ * workspace: device memory of at least mla_attend_explicit_workspace_size()
+ *         bytes (16-byte aligned): the rebuilt keys and values, bf16
+ *         (contents on return unspecified)
+ * out:    [batch*q_per_seq][heads][d_head], out_dtype F32 or BF16 (rounded to
+ *         nearest-even from the fp32 result)
+ * lse:    [batch*q_per_seq][heads] fp32, or NULL
+ * Visibility as for mla_decode (query i sees the first len - (S_q - 1 - i)
+ * tokens); a query that sees no token gets out = 0 and lse = -inf.
+ * Arithmetic: keys and values are rebuilt with fp32 sums and rounded to bf16;
+ * scores and the weighted sum of values run on bf16 matrix cores with fp32
+ * accumulation (weights rounded to bf16), softmax in fp32.  Errors as for
+ * mla_decode (MLA_ERR_SHAPE also for a short workspace); nothing is launched
+ * on an error. */
+int mla_attend_explicit(const mla_dims* dims, const void* q_nope, const void* q_rope, int32_t in_dtype,
+                        const mla_paged_kv* kv, const void* w_uk, const void* w_uv, void* workspace,
+                        int64_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream);
+
+/* Bytes of workspace mla_attend_explicit needs for these sizes and a page
+ * table of max_blocks_per_seq entries per sequence (host-only):
+ * batch x heads x T x 512, T = max_blocks_per_seq x 64 rounded up to a
+ * multiple of 256 (at most 2^24). */
+int mla_attend_explicit_workspace_size(const mla_dims* dims, int32_t max_blocks_per_seq, int64_t* bytes);
+
+/* The cheaper form for these sizes and cache (host-only): writes
+ * MLA_FORM_EXPLICIT when the cache is BF16 and q_per_seq is at least
+ * MLA_EXPLICIT_MIN_Q, else MLA_FORM_ABSORBED (FP8 and F32 caches always take
+ * the absorbed form).  The flop counts above cross at 171 query tokens; on
+ * MI355X (128 heads, a 4096-token context) the absorbed form measured faster
+ * up to 256 and the explicit one from 320 on, since rebuilding K and V runs
+ * further below the matrix-core peak than the absorbed decode does. */
+#define MLA_FORM_ABSORBED 0
+#define MLA_FORM_EXPLICIT 1
+#define MLA_EXPLICIT_MIN_Q 288
+int mla_attention_form(const mla_dims* dims, int32_t latent_dtype, int32_t* form);
 
 /* A launch-shape helper: the num_splits mla_decode should use so that the
  * device's compute units are filled, given the longest sequence length the

@@ -23,14 +23,17 @@ MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_ALIGN = -1, -2, -3, -4
 MLA_ERR_SPLITS, MLA_ERR_LAUNCH, MLA_ERR_DEVICE, MLA_ERR_SCRATCH = -5, -6, -7, -8
 MLA_STATIC_SCRATCH_BYTES = 16 << 20
 MLA_MAX_SPLITS = 1024
-MLA_MAX_Q_PER_SEQ = 128
+MLA_MAX_Q_PER_SEQ = 4096
+MLA_FORM_ABSORBED, MLA_FORM_EXPLICIT = 0, 1
+MLA_EXPLICIT_MIN_Q = 288
 D_LATENT, D_ROPE, D_HEAD, BLOCK = 512, 64, 128, 64
 
 # the C entry points this binding exposes (also checked by the tests)
 EXPORTS = ["mla_status_str", "mla_abi_version", "mla_source_hash", "mla_absorb_q", "mla_decode",
            "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits",
            "mla_cache_append", "mla_cache_append_workspace_size", "mla_cache_append_static", "mla_moe_gate",
-           "mla_moe_gate_workspace_size"]
+           "mla_moe_gate_workspace_size", "mla_attend_explicit", "mla_attend_explicit_workspace_size",
+           "mla_attention_form"]
 MLA_GATE_MAX_EXPERTS, MLA_GATE_MAX_TOP_K = 256, 16
 
 
@@ -95,6 +98,9 @@ def _load():
         "mla_cache_append_static": ([dp, i32, vp, vp, vp, i32, ctypes.c_float, kvp, vp], ctypes.c_int),
         "mla_moe_gate": ([i32, i32, i32, i32, vp, vp, i32, vp, f32p, f32p, vp, ctypes.c_int64, vp], ctypes.c_int),
         "mla_moe_gate_workspace_size": ([i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+        "mla_attend_explicit": ([dp, vp, vp, i32, kvp, vp, vp, vp, ctypes.c_int64, vp, i32, f32p, vp], ctypes.c_int),
+        "mla_attend_explicit_workspace_size": ([dp, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+        "mla_attention_form": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -282,3 +288,30 @@ def mla_moe_gate(u, e, top_k: int, idx, weight, workspace, scores=None, stream=N
                                              _ptr(e), _dtype_code(u), _ptr(idx), _ptr(weight), _ptr(scores),
                                              _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                              _stream(stream)))
+
+
+def mla_attend_explicit_workspace_size(dims: MlaDims, max_blocks_per_seq: int) -> int:
+    """Bytes of workspace mla_attend_explicit needs."""
+    out = ctypes.c_int64(0)
+    _check("mla_attend_explicit_workspace_size",
+           _lib.mla_attend_explicit_workspace_size(ctypes.byref(dims), int(max_blocks_per_seq), ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_attend_explicit(dims: MlaDims, q_nope, q_rope, cache: PagedCache, w_uk, w_uv, workspace, out, lse=None,
+                        stream=None):
+    """Attention in the explicit form: K = [W_UK c ; k^R] and V = W_UV c rebuilt
+    per head into the workspace, then softmax attention on them; out is fp32
+    or bf16 [B*S_q][H][128], lse [B*S_q][H] fp32 or None."""
+    _check("mla_attend_explicit",
+           _lib.mla_attend_explicit(ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _dtype_code(q_nope),
+                                    ctypes.byref(cache.kv), _ptr(w_uk), _ptr(w_uv), _ptr(workspace),
+                                    int(workspace.numel() * workspace.element_size()), _ptr(out), _dtype_code(out),
+                                    _ptr(lse), _stream(stream)))
+
+
+def mla_attention_form(dims: MlaDims, latent_dtype: int) -> int:
+    """MLA_FORM_EXPLICIT or MLA_FORM_ABSORBED: the cheaper form for these sizes."""
+    out = ctypes.c_int32(0)
+    _check("mla_attention_form", _lib.mla_attention_form(ctypes.byref(dims), int(latent_dtype), ctypes.byref(out)))
+    return int(out.value)

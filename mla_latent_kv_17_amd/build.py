@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 PEAKS_LIB = os.path.join(PKG, "libmla_peaks.so")
-SOURCES = ["api.hip", "decode.hip", "absorb.hip", "combine.hip", "out_uv.hip", "append.hip", "gate.hip"]
+SOURCES = ["api.hip", "decode.hip", "absorb.hip", "combine.hip", "out_uv.hip", "append.hip", "gate.hip", "explicit.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -239,9 +239,9 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, int3
   a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
   if (fmt == 1 || fmt == 2) {
-    // matrix-core kernels: 8 waves per (sequence, chunk, 64-row block)
-    const int64_t padded = (units + 7) / 8 * 8;
-    const int64_t grid = padded * a.row_blocks;
+    // matrix-core kernels: 8 waves per (sequence, chunk, row block), a
+    // multiple of the 8 XCDs (see the kernels' placement)
+    const int64_t grid = (units * a.row_blocks + 7) / 8 * 8;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
     if (fmt == 1 && rows_per_wg == 32)
       st = launch("mla::decode_mfma_bf16<32>", (const void*)mla::decode_mfma_bf16<32>, dim3((unsigned)grid), dim3(512),
@@ -576,6 +576,105 @@ int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top
   const void* const finish[4] = {(const void*)mla::gate_finish<1, 16>, (const void*)mla::gate_finish<2, 16>,
                                  (const void*)mla::gate_finish<3, 16>, (const void*)mla::gate_finish<4, 16>};
   return launch("mla::gate_finish", finish[(n_experts + 63) / 64 - 1], dim3((tokens + 15) / 16), dim3(256), a, s);
+}
+
+// Token capacity of the explicit form's workspace: the page table's span,
+// rounded up to whole rebuild tiles.
+static int64_t explicit_tokens(int32_t max_blocks_per_seq) {
+  const int64_t t = (int64_t)max_blocks_per_seq * kBlock;
+  return (t + mla::kRebuildTok - 1) / mla::kRebuildTok * mla::kRebuildTok;
+}
+
+int mla_attend_explicit_workspace_size(const mla_dims* dims, int32_t max_blocks_per_seq, int64_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bytes) return MLA_ERR_NULL;
+  if (max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  const int64_t tokens = explicit_tokens(max_blocks_per_seq);
+  if (tokens > (1 << 24)) return MLA_ERR_SHAPE;
+  *bytes = (int64_t)dims->batch * dims->heads * tokens * kDH * 2 * 2;  // K and V^T, bf16
+  return MLA_OK;
+}
+
+int mla_attend_explicit(const mla_dims* dims, const void* q_nope, const void* q_rope, int32_t in_dtype,
+                        const mla_paged_kv* kv, const void* w_uk, const void* w_uv, void* workspace,
+                        int64_t workspace_bytes, void* out, int32_t out_dtype, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!kv || !q_nope || !q_rope || !w_uk || !w_uv || !workspace || !out) return MLA_ERR_NULL;
+  if (!kv->latent || !kv->rope || !kv->block_table || !kv->seq_lens) return MLA_ERR_NULL;
+  if (in_dtype != MLA_BF16 || kv->latent_dtype != MLA_BF16 || kv->rope_dtype != MLA_BF16 || kv->scale)
+    return MLA_ERR_DTYPE;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (kv->block_size != kBlock || kv->num_blocks < 1 || kv->max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  if (kv->latent_row_stride < kDL || kv->rope_row_stride < kDR || kv->latent_block_stride < 0 ||
+      kv->rope_block_stride < 0)
+    return MLA_ERR_SHAPE;
+  // the kernels' per-lane copy offsets within a page are 32-bit
+  if (kv->latent_row_stride > (1 << 24) || kv->rope_row_stride > (1 << 24)) return MLA_ERR_SHAPE;
+  const int64_t lat_rs = kv->latent_row_stride * 2, lat_bs = kv->latent_block_stride * 2;
+  const int64_t rope_rs = kv->rope_row_stride * 2, rope_bs = kv->rope_block_stride * 2;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(workspace) ||
+      !aligned16(out) || !aligned16(kv->latent) || !aligned16(kv->rope) || (lat_rs & 15) || (lat_bs & 15) ||
+      (rope_rs & 15) || (rope_bs & 15))
+    return MLA_ERR_ALIGN;
+  int64_t need = 0;
+  st = mla_attend_explicit_workspace_size(dims, kv->max_blocks_per_seq, &need);
+  if (st) return st;
+  if (workspace_bytes < need) return MLA_ERR_SHAPE;
+  if (dims->batch == 0) return MLA_OK;
+  if (check_mode()) {
+    st = check_paging(dims->batch, kv, (hipStream_t)stream);
+    if (st) return st;
+  }
+
+  const int64_t tokens = explicit_tokens(kv->max_blocks_per_seq);
+  mla::ExplicitArgs a;
+  a.q_nope = (const uint16_t*)q_nope;
+  a.q_rope = (const uint16_t*)q_rope;
+  a.latent = (const uint8_t*)kv->latent;
+  a.rope = (const uint8_t*)kv->rope;
+  a.lat_bs = lat_bs;
+  a.lat_rs = lat_rs;
+  a.rope_bs = rope_bs;
+  a.rope_rs = rope_rs;
+  a.block_table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.w_uk = (const uint16_t*)w_uk;
+  a.w_uv = (const uint16_t*)w_uv;
+  a.k = (uint16_t*)workspace;
+  a.vt = (uint16_t*)workspace + (int64_t)dims->batch * dims->heads * tokens * kDH;
+  a.out = out;
+  a.lse = lse;
+  a.batch = dims->batch;
+  a.sq = dims->q_per_seq;
+  a.heads = dims->heads;
+  a.max_blocks = kv->max_blocks_per_seq;
+  a.tokens = (int)tokens;
+  a.tiles = (int)(tokens / mla::kRebuildTok);
+  a.qblocks = (dims->q_per_seq + mla::kExplicitQ - 1) / mla::kExplicitQ;
+  a.out_bf16 = out_dtype == MLA_BF16;
+  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
+  // grids: a multiple of the 8 XCDs over the (token tile, head) blocks and
+  // the ((sequence, head), query block) items -- see the kernels' placement
+  const int64_t rb_items = ((int64_t)dims->batch * a.tiles + mla::kRbBlockT - 1) / mla::kRbBlockT *
+                           ((dims->heads + mla::kRbBlockH - 1) / mla::kRbBlockH) * mla::kRbBlockT * mla::kRbBlockH;
+  const int64_t rb_grid = (rb_items + 7) / 8 * 8;
+  const int64_t at_grid = 8 * (((int64_t)dims->batch * dims->heads + 7) / 8) * a.qblocks;
+  if (rb_grid > 0x7fffffff || at_grid > 0x7fffffff) return MLA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  st = launch("mla::rebuild_kv", (const void*)mla::rebuild_kv, dim3((unsigned)rb_grid), dim3(512), a, s);
+  if (st) return st;
+  return launch("mla::attend_explicit", (const void*)mla::attend_explicit, dim3((unsigned)at_grid), dim3(256), a, s);
+}
+
+int mla_attention_form(const mla_dims* dims, int32_t latent_dtype, int32_t* form) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!form) return MLA_ERR_NULL;
+  if (latent_dtype != MLA_F32 && latent_dtype != MLA_BF16 && latent_dtype != MLA_FP8_E4M3) return MLA_ERR_DTYPE;
+  *form = latent_dtype == MLA_BF16 && dims->q_per_seq >= MLA_EXPLICIT_MIN_Q ? MLA_FORM_EXPLICIT : MLA_FORM_ABSORBED;
+  return MLA_OK;
 }
 
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits) {

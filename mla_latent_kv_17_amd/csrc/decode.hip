@@ -21,6 +21,7 @@
 //    over 16-token tiles copied to LDS by DMA, three tiles in flight.
 #include <type_traits>
 
+#include "mla_copy.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -43,109 +44,28 @@ constexpr float kRefSlack = 64.0f;              // log2 headroom above a row's r
 __device__ __forceinline__ int s16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int s8(int r) { return (r >> 1) & 7; }
 
-__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) { return (uint32_t)(size_t)p; }
-
-// Wave-wide HBM -> LDS copy of 16 bytes per lane: lane i's data lands at
-// lds_base + 16 * i (the base travels in M0, which is saved and restored so
-// the compiler's own use of M0 is untouched; one wait state separates the M0
-// write from the load that reads it).  Issued through asm so that the
-// compiler does not turn later LDS reads into waits for every outstanding
-// copy; completion is tracked with explicit s_waitcnt vmcnt.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
-}
-
-// Same copy with a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
-// byte offset (no per-lane address arithmetic).
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
-  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-  // readfirstlane returns int: widen each half through uint32_t (a sign
-  // extension of the low half would overwrite the high half of the address)
-  const uint64_t b = (uint64_t)base;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-  base = (const void*)(((uint64_t)hi << 32) | (uint64_t)lo);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-// Same copy where lane i's byte offset is (lc_i ^ x16) + lrow_i + row: a
-// per-lane chunk offset (XORed with a wave-uniform swizzle) and row offset
-// plus a wave-uniform row offset.
-__device__ __forceinline__ void dma16xy(const void* base, uint32_t lc, uint32_t x16, uint32_t lrow, uint32_t row,
-                                        uint32_t lds_base) {
-  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-  x16 = __builtin_amdgcn_readfirstlane(x16);
-  row = __builtin_amdgcn_readfirstlane(row);
-  const uint64_t b = (uint64_t)base;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-  base = (const void*)(((uint64_t)hi << 32) | (uint64_t)lo);
-  uint32_t saved, off;
-  asm volatile(
-      "v_xor_b32 %1, %2, %3\n\t"
-      "v_add3_u32 %1, %1, %4, %5\n\t"
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %7\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %6\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved), "=&v"(off)
-      : "v"(lc), "s"(x16), "v"(lrow), "s"(row), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-// Scalar (constant address space) load of a wave-uniform int: tracked by
-// lgkmcnt, so it never waits on the outstanding HBM -> LDS copies.
-__device__ __forceinline__ int load_uniform(const int32_t* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
 struct Work {
   int b, split, rb;
   int len, tok0, tok1, ntiles;
 };
 
 // XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs
-// (id % 8), so each XCD takes a contiguous range of (sequence, chunk) units
-// and runs the row blocks of a unit back to back: a tile is fetched from HBM
-// once and read from that XCD's L2 by the other row blocks, and the chunks of
-// one sequence, which share its query block, mostly run on one XCD too.
+// (id % 8).  The (sequence, chunk, row block) items, unit-major, are cut into
+// 8 contiguous ranges, one per XCD, so each XCD runs the row blocks of a
+// unit back to back: a tile is fetched from HBM once and read from that
+// XCD's L2 by the other row blocks, and the chunks of one sequence, which
+// share its query block, mostly run on one XCD too.  With fewer units than
+// XCDs a unit's row blocks spread over several XCDs (each fetches the tiles)
+// rather than leaving XCDs idle.
 __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
   const int id = blockIdx.x;
   const int xcd = id & 7, k = id >> 3;
-  const int upx = (a.units + 7) >> 3;  // units per XCD
-  const int unit = xcd * upx + k / a.row_blocks;
-  w.rb = k % a.row_blocks;
-  if (k >= upx * a.row_blocks || unit >= a.units) return false;
+  const int total = a.units * a.row_blocks;
+  const int per = (total + 7) >> 3;  // items per XCD
+  const int item = xcd * per + k;
+  if (k >= per || item >= total) return false;
+  const int unit = item / a.row_blocks;
+  w.rb = item - unit * a.row_blocks;
   w.b = unit / a.num_splits;
   w.split = unit - w.b * a.num_splits;
   w.len = a.seq_lens[w.b];

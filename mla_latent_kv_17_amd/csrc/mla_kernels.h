@@ -69,6 +69,40 @@ __global__ void merge_out_uv_mfma(const OutUvArgs a);  // the same with the chun
 template <bool kMerge>
 __global__ void out_uv_f32(const OutUvArgs a);   // fp32 weights
 
+// Explicit form (k = [W_UK c ; k^R], v = W_UV c rebuilt per head, then
+// attention on them).  Workspace, per sequence b and head h, with
+// tokens = the token capacity (a multiple of 256):
+//   K   [B][H][tokens][128] bf16: token-major rebuilt keys (no RoPE part)
+//   V^T [B][H][tokens / 32][128][32] bf16: rebuilt values per group of 32
+//       tokens, a dimension's 32 values adjacent; position 8 q + 4 k + i of a
+//       group holds token 16 k + 4 q + i (q < 4, k < 2, i < 4), the order in
+//       which the attention's value product consumes them.
+struct ExplicitArgs {
+  const uint16_t* q_nope;  // [B*S_q][H][128] bf16
+  const uint16_t* q_rope;  // [B*S_q][H][64] bf16
+  const uint8_t* latent;   // cache latent rows (bf16)
+  const uint8_t* rope;     // cache RoPE-key rows (bf16)
+  int64_t lat_bs, lat_rs, rope_bs, rope_rs;  // bytes
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const uint16_t* w_uk;    // [H][128][512] bf16
+  const uint16_t* w_uv;    // [H][128][512] bf16
+  uint16_t* k;             // workspace K
+  uint16_t* vt;            // workspace V^T
+  void* out;               // [B*S_q][H][128], fp32 or (out_bf16) bf16
+  float* lse;              // [B*S_q][H] or null
+  int batch, sq, heads, max_blocks, tokens;  // tokens: workspace token capacity
+  int tiles;               // rebuild: 256-token tiles per sequence
+  int qblocks;             // attention: 128-query blocks per sequence
+  int out_bf16;
+  float scale_log2;        // softmax_scale * log2(e)
+};
+constexpr int kRebuildTok = 256;  // tokens per rebuild workgroup
+constexpr int kRbBlockT = 4, kRbBlockH = 8;  // rebuild placement block: token tiles x heads
+constexpr int kExplicitQ = 128;   // query tokens per attention workgroup
+__global__ void rebuild_kv(const ExplicitArgs a);
+__global__ void attend_explicit(const ExplicitArgs a);
+
 // Cache append (c_t = W_DKV h_t, k^R_t = RoPE_p(W_KR h_t), written to the
 // paged cache).  Projections in two steps: fp32 partial sums over 512-wide
 // chunks of d_model into the caller's workspace, then per token the chunk

@@ -16,9 +16,10 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PagedCache, make_dims, mla_absorb_q, mla_cache_append, mla_cache_append_workspace_size,
-               mla_combine_out_uv, mla_decode, mla_decode_num_splits, mla_moe_gate, mla_moe_gate_workspace_size,
-               mla_out_uv, mla_split_combine, MLA_BF16, MLA_F32)
+from . import (PagedCache, make_dims, mla_absorb_q, mla_attend_explicit, mla_attend_explicit_workspace_size,
+               mla_attention_form, mla_cache_append, mla_cache_append_workspace_size, mla_combine_out_uv, mla_decode,
+               mla_decode_num_splits, mla_moe_gate, mla_moe_gate_workspace_size, mla_out_uv, mla_split_combine,
+               MLA_BF16, MLA_F32, MLA_FP8_E4M3, MLA_FORM_EXPLICIT)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -146,6 +147,35 @@ class DecodeStep:
         self.combine(stream)
         self.project(stream)
         return self.out
+
+
+class ExplicitStep:
+    """Owns the workspace (rebuilt keys and values) and the outputs of one
+    attention call in the explicit form (mla_attend_explicit)."""
+
+    def __init__(self, dev: DeviceInputs, out_dtype=torch.float32):
+        self.dev = dev
+        R, H = dev.batch * dev.q_per_seq, dev.heads
+        device = dev.q_nope.device
+        n = mla_attend_explicit_workspace_size(dev.dims, dev.cache.kv.max_blocks_per_seq)
+        self.workspace = torch.empty(max(n // 2, 8), dtype=torch.bfloat16, device=device)
+        self.out = torch.empty((R, H, 128), dtype=out_dtype, device=device)
+        self.lse = torch.empty((R, H), dtype=torch.float32, device=device)
+
+    def run(self, stream=None, with_lse: bool = True):
+        d = self.dev
+        mla_attend_explicit(d.dims, d.q_nope, d.q_rope, d.cache, d.w_uk, d.w_uv, self.workspace, self.out,
+                            self.lse if with_lse else None, stream)
+        return self.out
+
+
+def attention_step(dev: DeviceInputs, num_splits: int = 0):
+    """The step in the form the library calls cheaper for these sizes
+    (mla_attention_form): an ExplicitStep or a DecodeStep."""
+    code = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}[dev.wl.cache_dtype]
+    if mla_attention_form(dev.dims, code) == MLA_FORM_EXPLICIT:
+        return ExplicitStep(dev)
+    return DecodeStep(dev, num_splits)
 
 
 class CacheAppend:

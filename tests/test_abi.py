@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 17, syms
     lib = ctypes.CDLL(M.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
@@ -38,7 +38,7 @@ def test_source_hash_matches_the_sources():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 10
+    assert M.abi_version() == 11
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -66,7 +66,7 @@ def test_decode_validation():
     assert _call_decode(d, _kv(scale=0x50000)) == M.MLA_ERR_DTYPE               # scale only with fp8
     assert _call_decode(d, _kv(latent=0x10008)) == M.MLA_ERR_ALIGN
     assert _call_decode(d, _kv(), q=0x1004) == M.MLA_ERR_ALIGN
-    bad = M.make_dims(2, 129, 128)
+    bad = M.make_dims(2, M.MLA_MAX_Q_PER_SEQ + 1, 128)
     assert _call_decode(bad, _kv()) == M.MLA_ERR_SHAPE
     # fp16 partials: only for split decodes of bf16 / fp8 caches
     assert _call_decode(d, _kv(), ns=1, odt=M.MLA_F16) == M.MLA_ERR_DTYPE
@@ -207,3 +207,53 @@ def test_moe_gate_validation():
     assert call(T=0, wsb=0) == M.MLA_OK                                 # nothing to do
     assert call(T=0, u=0, idx=0, w=0, ws=0, wsb=0) == M.MLA_OK          # ... and no pointer read
     assert call(T=0, K=0) == M.MLA_ERR_SHAPE                            # sizes still checked
+
+
+def _call_explicit(dims, kv, qn=0x1000, qr=0x2000, wk=0x3000, wv=0x4000, ws=0x5000, ws_bytes=1 << 40, out=0x6000,
+                   idt=M.MLA_BF16, odt=M.MLA_F32):
+    return M._lib.mla_attend_explicit(ctypes.byref(dims), qn, qr, idt, ctypes.byref(kv) if kv is not None else None,
+                                      wk, wv, ws, ws_bytes, out, odt, None, None)
+
+
+def test_explicit_validation():
+    d = M.make_dims(2, 300, 16)
+    n = ctypes.c_int64(0)
+    assert M._lib.mla_attend_explicit_workspace_size(ctypes.byref(d), 4, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 2 * 16 * 256 * 128 * 2 * 2          # 4 pages = 256 tokens
+    assert M._lib.mla_attend_explicit_workspace_size(ctypes.byref(d), 5, ctypes.byref(n)) == M.MLA_OK
+    assert n.value == 2 * 16 * 512 * 128 * 2 * 2          # 320 tokens round up to 512
+    assert M._lib.mla_attend_explicit_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == M.MLA_ERR_SHAPE
+    assert M._lib.mla_attend_explicit_workspace_size(ctypes.byref(d), 4, None) == M.MLA_ERR_NULL
+    assert M._lib.mla_attend_explicit_workspace_size(ctypes.byref(d), (1 << 18) + 1, ctypes.byref(n)) == \
+        M.MLA_ERR_SHAPE                                     # more than 2^24 tokens
+    assert _call_explicit(d, None) == M.MLA_ERR_NULL
+    assert _call_explicit(d, _kv(), ws=0) == M.MLA_ERR_NULL
+    assert _call_explicit(d, _kv(), wv=0) == M.MLA_ERR_NULL
+    assert _call_explicit(d, _kv(), idt=M.MLA_F32) == M.MLA_ERR_DTYPE
+    assert _call_explicit(d, _kv(ldt=M.MLA_FP8_E4M3, scale=0x50000)) == M.MLA_ERR_DTYPE
+    assert _call_explicit(d, _kv(ldt=M.MLA_F32, rdt=M.MLA_F32)) == M.MLA_ERR_DTYPE
+    assert _call_explicit(d, _kv(), odt=M.MLA_F16) == M.MLA_ERR_DTYPE
+    assert _call_explicit(d, _kv(bs=32)) == M.MLA_ERR_SHAPE
+    assert _call_explicit(d, _kv(), wk=0x3008) == M.MLA_ERR_ALIGN
+    assert _call_explicit(d, _kv(), ws=0x5004) == M.MLA_ERR_ALIGN
+    need = 2 * 16 * 256 * 128 * 2 * 2                      # _kv(): 4 blocks per sequence
+    assert _call_explicit(d, _kv(), ws_bytes=need - 1) == M.MLA_ERR_SHAPE
+    assert _call_explicit(M.make_dims(2, M.MLA_MAX_Q_PER_SEQ + 1, 16), _kv()) == M.MLA_ERR_SHAPE
+    # batch 0: nothing to do, nothing launched
+    assert _call_explicit(M.make_dims(0, 300, 16), _kv(), ws_bytes=0) == M.MLA_OK
+
+
+def test_attention_form():
+    """The explicit form from MLA_EXPLICIT_MIN_Q query tokens per sequence on,
+    for a bf16 cache only."""
+    form = ctypes.c_int32(-1)
+    L = M._lib
+    for sq, ldt, want in [(1, M.MLA_BF16, M.MLA_FORM_ABSORBED), (M.MLA_EXPLICIT_MIN_Q - 1, M.MLA_BF16,
+                                                                 M.MLA_FORM_ABSORBED),
+                          (M.MLA_EXPLICIT_MIN_Q, M.MLA_BF16, M.MLA_FORM_EXPLICIT),
+                          (4096, M.MLA_BF16, M.MLA_FORM_EXPLICIT), (4096, M.MLA_FP8_E4M3, M.MLA_FORM_ABSORBED),
+                          (4096, M.MLA_F32, M.MLA_FORM_ABSORBED)]:
+        assert L.mla_attention_form(ctypes.byref(M.make_dims(4, sq, 128)), ldt, ctypes.byref(form)) == M.MLA_OK
+        assert form.value == want, (sq, ldt)
+    assert L.mla_attention_form(ctypes.byref(M.make_dims(4, 8, 128)), 7, ctypes.byref(form)) == M.MLA_ERR_DTYPE
+    assert L.mla_attention_form(ctypes.byref(M.make_dims(4, 8, 128)), M.MLA_BF16, None) == M.MLA_ERR_NULL

@@ -77,8 +77,8 @@ MULTI = {
                                                            len_range=None, seed=2203),
     "fp32_sq3": MI.small_variants()["fp32_b1_h16_t1k"].scaled(name="fp32_sq3", q_per_seq=3, seq_len=130,
                                                               seed=2204),
-    # the top of the supported range (MLA_MAX_Q_PER_SEQ = 128): a sequence
-    # shorter than S_q, splits on both sides of the fused-merge limit (8)
+    # many query tokens: a sequence shorter than S_q, splits on both sides
+    # of the fused-merge limit (8)
     "bf16_sq128_split3": MI.small_variants()["bf16_small_paged"].scaled(
         name="bf16_sq128_split3", q_per_seq=128, heads=16, batch=3, lens=(100, 300, 700), len_range=None,
         num_splits=3, seed=2205),
@@ -88,6 +88,13 @@ MULTI = {
     "fp8_sq65_split2": MI.small_variants()["fp8_small_sq2"].scaled(
         name="fp8_sq65_split2", q_per_seq=65, heads=8, batch=4, lens=(40, 64, 65, 300), len_range=None,
         num_splits=2, seed=2207),
+    # past the absorbed/explicit crossover the absorbed form still runs
+    "bf16_sq256_split2": MI.small_variants()["bf16_small_paged"].scaled(
+        name="bf16_sq256_split2", q_per_seq=256, heads=8, batch=2, lens=(200, 1000), len_range=None,
+        num_splits=2, seed=2208),
+    "fp8_sq300": MI.small_variants()["fp8_small_sq2"].scaled(
+        name="fp8_sq300", q_per_seq=300, heads=4, batch=2, lens=(333, 640), len_range=None, num_splits=1,
+        seed=2209),
 }
 # cases with many rows: the batched absorbed form of the oracle (pinned to
 # the explicit definition on the CPU) computes every row
