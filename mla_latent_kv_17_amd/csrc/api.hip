@@ -268,11 +268,15 @@ int mla_split_combine(const mla_dims* dims, int32_t num_splits, const void* o_pa
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_SPLITS;
   if (!aligned16(o_part) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
   const int rows = dims->q_per_seq * dims->heads;
-  const int64_t grid = (int64_t)dims->batch * rows;
-  if (grid == 0) return MLA_OK;
+  const int64_t total = (int64_t)dims->batch * rows;
+  if (total == 0) return MLA_OK;
   mla::CombineArgs a{o_part, lse_part, o_lat, lse, dims->batch, num_splits, rows};
-  const void* k = part_dtype == MLA_F16 ? (const void*)mla::split_combine<_Float16>
-                                         : (const void*)mla::split_combine<float>;
+  // few chunks: a wave per row, four rows per workgroup; many: a workgroup per row
+  const bool solo = num_splits <= mla::kCombineSoloMaxSplits;
+  const bool f16 = part_dtype == MLA_F16;
+  const void* k = solo ? (f16 ? (const void*)mla::split_combine<_Float16, true> : (const void*)mla::split_combine<float, true>)
+                       : (f16 ? (const void*)mla::split_combine<_Float16, false> : (const void*)mla::split_combine<float, false>);
+  const int64_t grid = solo ? (total + 3) / 4 : total;
   st = launch("mla::split_combine", k, dim3((unsigned)grid), dim3(256), a, (hipStream_t)stream);
   return st;
 }

@@ -6,12 +6,15 @@
 // inference time": attention over all earlier tokens).  Chunks that saw no
 // token carry lse_s = -inf and weight 0.
 //
-// The partials are fp32 or fp16 (template argument); sums are fp32.
-// One workgroup (4 waves) per query row: wave w merges chunks w, w + 4, ...
-// (16 of them per round, every load of a round issued before its
-// arithmetic, so a round costs one memory latency), lane l holding latent
-// columns 8l .. 8l+7; the four waves' running maxima, sums and rows then
-// combine through LDS (the same log-sum-exp update).
+// The partials are fp32 or fp16 (template argument); sums are fp32.  Lane
+// l holds latent columns 8l .. 8l+7 of a row; a wave merges its chunks 16 per
+// round, every load of a round issued before its arithmetic, so a round
+// costs one memory latency.  Two shapes:
+//  * kSolo (up to 16 chunks): one wave per query row, four rows per
+//    workgroup, one round;
+//  * otherwise one workgroup (4 waves) per query row: wave w merges chunks
+//    w, w + 4, ..., and the four waves' running maxima, sums and rows then
+//    combine through LDS (the same log-sum-exp update).
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -29,25 +32,27 @@ __device__ __forceinline__ void load8(const PT* p, f32x4& a, f32x4& b) {
 
 }  // namespace
 
-template <typename PT>
+template <typename PT, bool kSolo>
 __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
   __shared__ float xm[4], xz[4];
   __shared__ __attribute__((aligned(16))) float xo[4][512];
-  const int gr = blockIdx.x;  // (sequence, row)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gr = kSolo ? 4 * blockIdx.x + wave : blockIdx.x;  // (sequence, row)
+  if (kSolo && gr >= a.batch * a.rows) return;
   const int b = gr / a.rows, row = gr - b * a.rows;
   const int ns = a.num_splits;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kStride = kSolo ? 1 : 4;  // chunks between a wave's consecutive chunks
   const float* lp = a.lse_part + (int64_t)b * ns * a.rows + row;
   const PT* op = (const PT*)a.o_part + ((int64_t)b * ns * a.rows + row) * 512 + 8 * lane;
   const int64_t ostride = (int64_t)a.rows * 512;
   float m = -__builtin_inff(), z = 0.f;  // this wave's running maximum and sum of exp(lse_s - m)
   f32x4 acc0 = f32x4{}, acc1 = f32x4{};  // its running sum of exp(lse_s - m) o_s
-  for (int s0 = wave; s0 < ns; s0 += 4 * kRound) {
+  for (int s0 = kSolo ? 0 : wave; s0 < ns; s0 += kStride * kRound) {
     float ls[kRound];
     f32x4 v0[kRound], v1[kRound];
 #pragma unroll
     for (int j = 0; j < kRound; ++j) {
-      const int s = s0 + 4 * j;
+      const int s = s0 + kStride * j;
       const bool in = s < ns;
       ls[j] = in ? lp[(int64_t)s * a.rows] : -__builtin_inff();
       if (in)
@@ -72,6 +77,14 @@ __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
       acc1 += e * v1[j];
     }
     m = mb;
+  }
+  if (kSolo) {
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    float* orow = a.o_lat + ((int64_t)b * a.rows + row) * 512 + 8 * lane;
+    *(f32x4*)orow = acc0 * inv;
+    *(f32x4*)(orow + 4) = acc1 * inv;
+    if (a.lse && lane == 0) a.lse[(int64_t)b * a.rows + row] = z > 0.f ? m + logf(z) : -__builtin_inff();
+    return;
   }
   if (lane == 0) {
     xm[wave] = m;
@@ -101,7 +114,9 @@ __global__ void __launch_bounds__(256) split_combine(const CombineArgs a) {
   if (a.lse && lane == 0) a.lse[(int64_t)b * a.rows + row] = zt > 0.f ? mm + logf(zt) : -__builtin_inff();
 }
 
-template __global__ void split_combine<float>(const CombineArgs a);
-template __global__ void split_combine<_Float16>(const CombineArgs a);
+template __global__ void split_combine<float, false>(const CombineArgs a);
+template __global__ void split_combine<_Float16, false>(const CombineArgs a);
+template __global__ void split_combine<float, true>(const CombineArgs a);
+template __global__ void split_combine<_Float16, true>(const CombineArgs a);
 
 }  // namespace mla

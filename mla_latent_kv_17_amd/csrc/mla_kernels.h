@@ -47,7 +47,8 @@ struct CombineArgs {
   float* lse;             // [B*S_q][H] or null
   int batch, num_splits, rows;  // rows = S_q * H
 };
-template <typename PT>  // partial type: float or _Float16
+constexpr int kCombineSoloMaxSplits = 16;  // up to this many chunks: one wave per query row
+template <typename PT, bool kSolo>  // partial type: float or _Float16
 __global__ void split_combine(const CombineArgs a);
 
 struct OutUvArgs {
