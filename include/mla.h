@@ -70,8 +70,9 @@ extern "C" {
  * 10: the chunk partials of mla_decode may be fp16 (MLA_F16): o_dtype of
  * mla_decode, part_dtype of mla_split_combine and mla_combine_out_uv;
  * 11: q_per_seq up to 4096; adds the explicit form (mla_attend_explicit,
- * mla_attend_explicit_workspace_size) and mla_attention_form */
-#define MLA_ABI_VERSION 11
+ * mla_attend_explicit_workspace_size) and mla_attention_form;
+ * 12: adds mla_decode_num_splits_batch */
+#define MLA_ABI_VERSION 12
 
 typedef enum mla_dtype {
   MLA_F32 = 0,
@@ -375,6 +376,18 @@ int mla_attention_form(const mla_dims* dims, int32_t latent_dtype, int32_t* form
  * caller expects.  Writes 1 when one chunk per sequence already fills the
  * device.  Host-only; reads the current device's compute-unit count. */
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits);
+
+/* The same choice given also the sum of the batch's cached lengths (host-side
+ * numbers the caller holds): for nearly uniform lengths (a sum of at least
+ * 0.9 x batch x max_seq_len) the value mla_decode_num_splits writes; for
+ * uneven ones at least enough chunks that a chunk holds about 16 pages on
+ * average (the longest sequences then spread over many compute units and a
+ * short sequence's chunks finish early; 64 sequences of 512 .. 16384 tokens:
+ * 8 chunks), at most the longest sequence's pages and MLA_MAX_SPLITS.
+ * MLA_ERR_SHAPE if total_tokens is negative or above batch * max_seq_len.
+ * Host-only; reads the current device's compute-unit count. */
+int mla_decode_num_splits_batch(const mla_dims* dims, int64_t total_tokens, int32_t max_seq_len,
+                                int32_t* num_splits);
 
 #ifdef __cplusplus
 }

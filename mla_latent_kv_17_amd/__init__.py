@@ -33,7 +33,7 @@ EXPORTS = ["mla_status_str", "mla_abi_version", "mla_source_hash", "mla_absorb_q
            "mla_split_combine", "mla_out_uv", "mla_combine_out_uv", "mla_decode_num_splits",
            "mla_cache_append", "mla_cache_append_workspace_size", "mla_cache_append_static", "mla_moe_gate",
            "mla_moe_gate_workspace_size", "mla_attend_explicit", "mla_attend_explicit_workspace_size",
-           "mla_attention_form"]
+           "mla_attention_form", "mla_decode_num_splits_batch"]
 MLA_GATE_MAX_EXPERTS, MLA_GATE_MAX_TOP_K = 256, 16
 
 
@@ -101,6 +101,7 @@ def _load():
         "mla_attend_explicit": ([dp, vp, vp, i32, kvp, vp, vp, vp, ctypes.c_int64, vp, i32, f32p, vp], ctypes.c_int),
         "mla_attend_explicit_workspace_size": ([dp, i32, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
         "mla_attention_form": ([dp, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+        "mla_decode_num_splits_batch": ([dp, ctypes.c_int64, i32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -207,6 +208,14 @@ def mla_decode(dims: MlaDims, q_lat, q_rope, cache: PagedCache, num_splits: int,
     _check("mla_decode", _lib.mla_decode(ctypes.byref(dims), _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat),
                                          ctypes.byref(cache.kv), int(num_splits), _ptr(o), _dtype_code(o),
                                          _ptr(lse), _stream(stream)))
+
+
+def mla_decode_num_splits_batch(dims: MlaDims, total_tokens: int, max_seq_len: int) -> int:
+    """num_splits for mla_decode from the sum and the maximum of the cached lengths."""
+    out = ctypes.c_int32(0)
+    _check("mla_decode_num_splits_batch", _lib.mla_decode_num_splits_batch(ctypes.byref(dims), int(total_tokens),
+                                                                           int(max_seq_len), ctypes.byref(out)))
+    return int(out.value)
 
 
 def mla_split_combine(dims: MlaDims, num_splits: int, o_part, lse_part, o_lat, lse=None, stream=None):

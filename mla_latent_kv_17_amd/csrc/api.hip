@@ -681,6 +681,32 @@ int mla_attention_form(const mla_dims* dims, int32_t latent_dtype, int32_t* form
   return MLA_OK;
 }
 
+// Pages per chunk an uneven batch is cut for (the headline's chunks: 4096
+// tokens in 4).
+constexpr int kRaggedChunkPages = 16;
+
+int mla_decode_num_splits_batch(const mla_dims* dims, int64_t total_tokens, int32_t max_seq_len,
+                                int32_t* num_splits) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!num_splits) return MLA_ERR_NULL;
+  if (total_tokens < 0 || max_seq_len < 0 || total_tokens > (int64_t)dims->batch * max_seq_len) return MLA_ERR_SHAPE;
+  int32_t ns = 1;
+  st = mla_decode_num_splits(dims, max_seq_len, &ns);
+  if (st) return st;
+  const int64_t b = dims->batch;
+  if (b >= 2 && total_tokens * 10 < b * (int64_t)max_seq_len * 9) {  // uneven lengths
+    const int64_t mean_pages = ((total_tokens + kBlock - 1) / kBlock + b - 1) / b;
+    const int64_t max_pages = ((int64_t)max_seq_len + kBlock - 1) / kBlock;
+    int64_t want = (mean_pages + kRaggedChunkPages / 2) / kRaggedChunkPages;
+    if (want > max_pages) want = max_pages;
+    if (want > MLA_MAX_SPLITS) want = MLA_MAX_SPLITS;
+    if (want > ns) ns = (int32_t)want;
+  }
+  *num_splits = ns;
+  return MLA_OK;
+}
+
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int32_t* num_splits) {
   int st = check_dims(dims);
   if (st) return st;

@@ -79,6 +79,25 @@ __device__ __forceinline__ bool decode_work(const DecodeArgs& a, Work& w) {
   return true;
 }
 
+// A chunk that holds none of its sequence's tokens (the trailing chunks of a
+// sequence shorter than num_splits pages): its rows get o = 0 and lse = -inf,
+// as the pipeline would give them, without staging queries or tiles.
+__device__ __forceinline__ void empty_chunk(const DecodeArgs& a, const Work& w, int nrows) {
+  const int rows = a.rows, row_base = w.rb * nrows;
+  const int64_t slot = (int64_t)w.b * a.num_splits + w.split;
+  for (int i = threadIdx.x; i < nrows * 128; i += blockDim.x) {
+    const int r = i >> 7, c4 = i & 127;
+    if (row_base + r >= rows) continue;
+    const int64_t e = (slot * rows + row_base + r) * 512 + 4 * c4;
+    if (a.o_f16)
+      *(f16x4*)((_Float16*)a.o + e) = f16x4{0, 0, 0, 0};
+    else
+      *(f32x4*)((float*)a.o + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if ((int)threadIdx.x < nrows && row_base + (int)threadIdx.x < rows)
+    a.lse[slot * rows + row_base + threadIdx.x] = -__builtin_inff();
+}
+
 }  // namespace
 
 // bf16 cache.  Workgroup = 8 waves = one (sequence, KV chunk, block of
@@ -127,6 +146,10 @@ decode_mfma_bf16(const DecodeArgs a) {
   if (blockDim.x != 512) return;
   Work wk;
   if (!decode_work(a, wk)) return;
+  if (wk.ntiles == 0) {
+    empty_chunk(a, wk, kRows);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, 0..7
@@ -621,6 +644,10 @@ decode_mfma_fp8(const DecodeArgs a) {
   if (blockDim.x != 512) return;
   Work wk;
   if (!decode_work(a, wk)) return;
+  if (wk.ntiles == 0) {
+    empty_chunk(a, wk, kDecodeRowsPerWg);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, 0..7

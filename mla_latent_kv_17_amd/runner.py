@@ -18,7 +18,7 @@ import torch
 
 from . import (PagedCache, make_dims, mla_absorb_q, mla_attend_explicit, mla_attend_explicit_workspace_size,
                mla_attention_form, mla_cache_append, mla_cache_append_workspace_size, mla_combine_out_uv, mla_decode,
-               mla_decode_num_splits, mla_moe_gate, mla_moe_gate_workspace_size, mla_out_uv, mla_split_combine,
+               mla_decode_num_splits_batch, mla_moe_gate, mla_moe_gate_workspace_size, mla_out_uv, mla_split_combine,
                MLA_BF16, MLA_F32, MLA_FP8_E4M3, MLA_FORM_EXPLICIT)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -68,12 +68,15 @@ class DeviceInputs:
 
 
 class DecodeStep:
-    """Owns the outputs and the split workspace of one decode step."""
+    """Owns the outputs and the split workspace of one decode step
+    (num_splits <= 0: the library's choice, mla_decode_num_splits_batch)."""
 
     def __init__(self, dev: DeviceInputs, num_splits: int = 0):
         self.dev = dev
         if num_splits <= 0:
-            num_splits = mla_decode_num_splits(dev.dims, int(dev.seq_lens_host.max(initial=0)))
+            lens = dev.seq_lens_host
+            num_splits = mla_decode_num_splits_batch(dev.dims, int(lens.astype(np.int64).sum()),
+                                                     int(lens.max(initial=0)))
         self.num_splits = num_splits
         R = dev.batch * dev.q_per_seq
         H = dev.heads

@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 17, syms
+    assert len(syms) == 18, syms
     lib = ctypes.CDLL(M.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
@@ -38,7 +38,7 @@ def test_source_hash_matches_the_sources():
 
 
 def test_version_and_status_strings():
-    assert M.abi_version() == 11
+    assert M.abi_version() == 12
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert M.status_str(code).startswith("MLA_")
     assert "UNKNOWN" in M.status_str(-99)
@@ -257,3 +257,16 @@ def test_attention_form():
         assert form.value == want, (sq, ldt)
     assert L.mla_attention_form(ctypes.byref(M.make_dims(4, 8, 128)), 7, ctypes.byref(form)) == M.MLA_ERR_DTYPE
     assert L.mla_attention_form(ctypes.byref(M.make_dims(4, 8, 128)), M.MLA_BF16, None) == M.MLA_ERR_NULL
+
+
+def test_num_splits_batch_validation():
+    """Validation of mla_decode_num_splits_batch (the choice itself reads the
+    device's compute units: covered by the GPU tests)."""
+    d = M.make_dims(2, 1, 128)
+    L = M._lib
+    ns = ctypes.c_int32(-1)
+    assert L.mla_decode_num_splits_batch(ctypes.byref(d), 10, 4, ctypes.byref(ns)) == M.MLA_ERR_SHAPE  # above 2 x 4
+    assert L.mla_decode_num_splits_batch(ctypes.byref(d), -1, 4, ctypes.byref(ns)) == M.MLA_ERR_SHAPE
+    assert L.mla_decode_num_splits_batch(ctypes.byref(d), 8, -1, ctypes.byref(ns)) == M.MLA_ERR_SHAPE
+    assert L.mla_decode_num_splits_batch(ctypes.byref(d), 4, 4, None) == M.MLA_ERR_NULL
+    assert L.mla_decode_num_splits_batch(None, 4, 4, ctypes.byref(ns)) == M.MLA_ERR_NULL

@@ -115,3 +115,42 @@ def test_multi_token_vs_oracle(name):
     assert np.array_equal(np.isneginf(lse), none)
     assert np.max(np.abs(lse[~none] - lse_ref[~none])) < 1e-2
     assert (out[none] == 0).all()
+
+
+# the library's split choice for an uneven batch (mla_decode_num_splits_batch):
+# more chunks than the longest sequence alone would ask for, so a short
+# sequence's trailing chunks are empty (they write o = 0, lse = -inf without
+# running the pipeline and the merges give them weight 0)
+def test_num_splits_batch_choice():
+    import mla_latent_kv_17_amd as M
+    d = M.make_dims(64, 1, 128)
+    assert M.mla_decode_num_splits_batch(d, 64 * 8448, 16384) == 8        # 64 sequences of 512 .. 16384 tokens
+    assert M.mla_decode_num_splits_batch(M.make_dims(32, 1, 128), 32 * 4096, 4096) == \
+        M.mla_decode_num_splits(M.make_dims(32, 1, 128), 4096)            # uniform: unchanged
+    assert M.mla_decode_num_splits_batch(M.make_dims(2, 1, 128), 300, 200) == \
+        M.mla_decode_num_splits(M.make_dims(2, 1, 128), 200)              # few pages: at most the longest's
+
+
+UNEVEN = {
+    "bf16_uneven_ns16": (MI.small_variants()["bf16_small_paged"].scaled(
+        name="bf16_uneven", batch=4, lens=(0, 70, 300, 1500), len_range=None, seed=2210), 16),
+    "bf16_sq3_h16_ns8": (MI.small_variants()["bf16_small_paged"].scaled(
+        name="bf16_sq3_h16", q_per_seq=3, heads=16, batch=4, lens=(2, 64, 300, 1000), len_range=None, seed=2211), 8),
+    "fp8_ns6": (MI.small_variants()["fp8_small_sq2"], 6),
+    "fp32_uneven_ns9": (MI.small_variants()["fp32_b1_h16_t1k"].scaled(
+        name="fp32_uneven", batch=3, seq_len=None, lens=(100, 700, 1024), paged=True, spare_blocks=2, seed=2212), 9),
+}
+
+
+@pytest.mark.parametrize("name", list(UNEVEN))
+def test_uneven_batch_many_chunks(name):
+    wl, ns = UNEVEN[name]
+    inp = MI.generate(wl)
+    out, o_lat, lse, step = run_gpu(inp, num_splits=ns)
+    assert step.num_splits == ns
+    o_ref, lse_ref = O.explicit_decode(inp)
+    check(f"{name}/o", out, o_ref, wl.cache_dtype)
+    none = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), none)
+    assert np.max(np.abs(lse[~none] - lse_ref[~none])) < 1e-2
+    assert (out[none] == 0).all()
