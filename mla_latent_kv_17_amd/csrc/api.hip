@@ -322,9 +322,16 @@ int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_p
                    out_dtype == MLA_BF16, part_dtype == MLA_F16};
   hipStream_t s = (hipStream_t)stream;
   if (w_dtype == MLA_BF16) {
-    const void* k = part_dtype == MLA_F16 ? (const void*)mla::merge_out_uv_mfma<_Float16>
-                                           : (const void*)mla::merge_out_uv_mfma<float>;
-    st = launch("mla::merge_out_uv_mfma", k, dim3((dims->heads + 7) / 8 * 16), dim3(256), a, s);
+    // workgroups per head: enough to fill the compute units, at most one per
+    // 16-row tile
+    const int tiles = (rows + 15) / 16;
+    const int cus = device_cus() > 0 ? device_cus() : 256;
+    a.groups = std::min(tiles, std::max(1, (cus + dims->heads - 1) / dims->heads));
+    const int64_t grid = (int64_t)(dims->heads + 7) / 8 * 8 * a.groups;
+    if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
+    const void* k = part_dtype == MLA_F16 ? (const void*)mla::merge_out_uv16<_Float16>
+                                           : (const void*)mla::merge_out_uv16<float>;
+    st = launch("mla::merge_out_uv16", k, dim3((unsigned)grid), dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;
     st = launch("mla::out_uv_f32<merge>", (const void*)mla::out_uv_f32<true>, dim3(dims->heads * (kDH / 16)),

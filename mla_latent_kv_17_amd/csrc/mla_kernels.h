@@ -63,10 +63,11 @@ struct OutUvArgs {
   int num_splits, sq;
   int out_bf16;           // 1: round the fp32 sums to bf16 (nearest even)
   int part_f16;           // merged form: 1 if the partials are fp16
+  int groups;             // merge_out_uv16: workgroups per head (each takes every groups-th 16-row tile)
 };
 __global__ void out_uv_mfma(const OutUvArgs a);        // bf16 weights, hi/lo split of o_lat
 template <typename PT>  // partial type: float or _Float16
-__global__ void merge_out_uv_mfma(const OutUvArgs a);  // the same with the chunk merge on the way
+__global__ void merge_out_uv16(const OutUvArgs a);  // the same with the chunk merge on the way (16-row tiles)
 template <bool kMerge>
 __global__ void out_uv_f32(const OutUvArgs a);   // fp32 weights
 

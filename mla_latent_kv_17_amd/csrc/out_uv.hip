@@ -10,19 +10,22 @@
 // multiplied by the exact bf16 weights with fp32 sums, which keeps about
 // 16 significant bits of o_lat (fp32-level error for this product).
 //
-// Workgroup = (head, half of d_head): its 64 x 512 weight slice (64 KB) is
-// read from HBM once into registers and reused for every 32-row tile.  The
+// out_uv_mfma: workgroup = (head, half of d_head): its 64 x 512 weight
+// slice (64 KB) is read from HBM once into registers and reused for every
+// 32-row tile.  The
 // four waves split the latent (K) dimension, 128 columns each, so every wave
 // issues all of its loads at once; the partial tiles are summed through LDS.
 // The two halves of a head run on one XCD (block ids 8 apart), where the
 // second read of each o_lat row is an L2 hit.
 //
-// Merged form (merge_out_uv_mfma, out_uv_f32<true>): o_lat is not read but
+// Merged form (merge_out_uv16, out_uv_f32<true>): o_lat is not read but
 // formed on the fly from the KV chunks' normalised partial outputs o_s and
 // log-sum-exps lse_s (the split merge, same arithmetic as split_combine:
 // weights exp(lse_s - max) over their sum, chunks with lse_s = -inf taking
 // weight 0 whatever their o_s holds), so the merged rows never go through
-// memory; the merged lse is written once per (row, head).
+// memory; the merged lse is written once per (row, head).  merge_out_uv16
+// gives each merged row to one workgroup, which holds its head's whole
+// weight block (see the kernel).
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -99,130 +102,146 @@ __global__ void __launch_bounds__(256) out_uv_mfma(const OutUvArgs a) {
   }
 }
 
-// Merged form, bf16 weights.  Workgroup = (head, half of d_head), 4 waves
-// (one per SIMD, so each holds up to 512 registers).  Per 32-row tile:
-//  * every global load the tile needs is issued first: the weight slice, the
-//    rows' chunk log-sum-exps and the first four chunks' partial rows
-//    (thread t owns 16-byte column chunk t % 128 of rows t / 128 + 2 i, so a
-//    wave's load covers 1 KB of one row);
-//  * the merge weights exp(lse_s - max) / sum: 8 lanes per row, the lse held
-//    in registers, reduced with lane shuffles, stored to LDS;
-//  * the merged tile is summed in registers and stored to LDS as its bf16 hi
-//    and lo terms, 16-byte chunk q of row r at slot q ^ r (32 rows read at
-//    one chunk by the products then spread over the banks);
-//  * wave w multiplies latent columns 128w .. 128w+127 (A from LDS, B = its
-//    64 x 128 weight slice in registers); the four partial tiles are summed
-//    through LDS.
-// More than four chunks take further rounds of two; more than 64 recompute
-// their weights from the row's max and sum.  The partials are fp32 or fp16
-// (template argument; fp16 halves the bytes read), converted to fp32 on load.
+// Eight consecutive chunk-partial values of one row (fp16 or fp32 storage,
+// 16-byte aligned), converted to fp32 when used.
 template <typename PT>
-__global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
-  constexpr int kPad = 33;  // LDS row stride (floats) of the partial tiles
-  constexpr int kW = 64;    // chunk weights held in LDS per round
-  constexpr int kF = 4;     // chunks loaded with the first round
-  __shared__ float red[4][2][32 * kPad];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][32 * 1024];  // merged tile: hi, lo bf16
-  __shared__ float wt[32][kW];
-  __shared__ float rowm[32], rowinv[32];
-  const int h = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7), half = (blockIdx.x >> 3) & 1;
+struct Piece8;
+template <>
+struct Piece8<_Float16> {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  f16x8 v;
+  __device__ __forceinline__ void load(const _Float16* p) { v = *(const f16x8*)p; }
+  __device__ __forceinline__ float operator[](int k) const { return (float)v[k]; }
+};
+template <>
+struct Piece8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *(const f32x4*)p;
+    hi = *(const f32x4*)(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int k) const { return k < 4 ? lo[k] : hi[k - 4]; }
+};
+
+// Merged form, bf16 weights, 16-row tiles.  Workgroup = (head, row group):
+// the a.groups workgroups of a head take its 16-row tiles in turn (block
+// ids 8 apart, so that they share an XCD and the head's weights in L2).
+// Four waves, one per SIMD.  Wave w holds the weight rows (output dims)
+// 32 w .. 32 w + 31 over all 512 latent columns in registers, so it
+// multiplies the full K for its outputs and no partial sums are exchanged;
+// each merged row is formed once, by one workgroup.  Per tile:
+//  * thread t merges row t / 16, columns 8 (t % 16) + 128 j + 0..7 (j < 4):
+//    the row's chunk log-sum-exps are loaded first, then the first four
+//    chunks' pieces (16 bytes each, a wave load covering 256 contiguous
+//    bytes of four rows);
+//  * the 16 lanes of a row form its merge weights exp(lse_s - max) / sum
+//    with lane shuffles while the pieces are in flight, and keep them in LDS;
+//  * the merged pieces are summed in registers (a chunk whose weight is 0,
+//    one that saw no token, is dropped whatever it holds) and stored to LDS
+//    as bf16 hi and lo terms, 16-byte chunk q of row r at slot q ^ r;
+//  * out^T[32 w + 16 db + 0..15][16 rows] with v_mfma_f32_16x16x32_bf16,
+//    A = the weights (registers), B = the merged rows (LDS), hi then lo.
+// More than four chunks take further rounds of two; more than 64 recompute
+// their weights from the row's max and sum.
+template <typename PT>
+__global__ void __launch_bounds__(256) merge_out_uv16(const OutUvArgs a) {
+  const int groups = a.groups;
+  constexpr int kW = 64;  // chunk weights held in LDS per round
+  constexpr int kF = 4;   // chunks loaded with the first round
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * 1024];  // merged tile: hi, lo bf16
+  __shared__ float wt[16][kW];
+  __shared__ float rowm[16], rowinv[16];
+  const int bid = blockIdx.x;
+  const int h = bid / (8 * groups) * 8 + (bid & 7), grp = (bid >> 3) % groups;
   if (h >= a.heads) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n32 = lane & 31, g = lane >> 5;
+  const int i16 = lane & 15, q4 = lane >> 4;
   const int ns = a.num_splits;
   const int64_t rs = (int64_t)a.sq * a.heads;  // partial rows between consecutive chunks
-  const int64_t cs = rs * 512;                 // floats between consecutive chunks
-  // partial row of query row r (head h), chunk 0
-  auto prow = [&](int r) -> int64_t {
+  const int64_t cs = rs * 512;                 // elements between consecutive chunks
+  auto prow = [&](int r) -> int64_t {          // partial row of query row r (head h), chunk 0
     const int b = r / a.sq, q = r - b * a.sq;
     return (int64_t)b * ns * rs + (int64_t)q * a.heads + h;
   };
-  // B operand: W[d][c], d = 64 half + 32 nt + n32, c = 128 wave + 16 ks + 8 g + j
-  bf16x8 bw[2][8];
+  // A operand of k-step ks for block db: W[d][c], d = 32 wave + 16 db + i16,
+  // c = 32 ks + 8 q4 .. +7
+  bf16x8 aw[2][16];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint16_t* w = (const uint16_t*)a.w + ((int64_t)h * 128 + half * 64 + nt * 32 + n32) * 512 + wave * 128 + 8 * g;
+  for (int db = 0; db < 2; ++db) {
+    const uint16_t* w = (const uint16_t*)a.w + ((int64_t)h * 128 + 32 * wave + 16 * db + i16) * 512 + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bw[nt][ks] = as_bf16x8(*(const u32x4*)(w + ks * 16));
+    for (int ks = 0; ks < 16; ++ks) aw[db][ks] = as_bf16x8(*(const u32x4*)(w + 32 * ks));
   }
-  const int c = tid & 127, r0 = tid >> 7;
-  for (int m0 = 0; m0 < a.rows; m0 += 32) {
-    // ---- loads: the lse of row m0 + tid / 8 first (unconditional, clamped
-    // indices), then the first chunks' partial rows: the weights wait only
-    // for the former, the partial rows stay in flight meanwhile
-    const int lr = tid >> 3, lj = tid & 7, r = m0 + lr;
-    const float* lp = a.lse_part + prow(min(r, a.rows - 1));
-    float lv[8];
+  const int lr = tid >> 4, cj = tid & 15;
+  for (int m0 = 16 * grp; m0 < a.rows; m0 += 16 * groups) {
+    const int r = m0 + lr;
+    const int64_t pr = prow(min(r, a.rows - 1));
+    const float* lp = a.lse_part + pr;
+    float lv[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) lv[k] = lp[(int64_t)min(lj + 8 * k, ns - 1) * rs];
-    asm volatile("" ::: "memory");  // keep the lse loads ahead of the partial rows
-    const PT* vrow[16];  // chunk 0 of the thread's rows (clamped to a real row)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) vrow[i] = (const PT*)a.o_part + prow(min(m0 + r0 + 2 * i, a.rows - 1)) * 512 + 4 * c;
-    f32x4 v0[kF][16];
+    for (int k = 0; k < 4; ++k) lv[k] = lp[(int64_t)min(cj + 16 * k, ns - 1) * rs];
+    asm volatile("" ::: "memory");  // keep the lse loads ahead of the partial pieces
+    const PT* vr = (const PT*)a.o_part + pr * 512 + 8 * cj;
+    Piece8<PT> v0[kF][4];
 #pragma unroll
     for (int jj = 0; jj < kF; ++jj) {
       const int64_t so = (int64_t)min(jj, ns - 1) * cs;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v0[jj][i] = load4(vrow[i] + so);
+      for (int j = 0; j < 4; ++j) v0[jj][j].load(vr + so + 128 * j);
     }
-    // (an empty use of every lse value here keeps its load where it is, ahead
-    // of the partial rows, instead of being moved into the branch below)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(lv[k]));
+    for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(lv[k]));
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (!(r < a.rows && lj + 8 * k < ns)) lv[k] = -__builtin_inff();
-    // ---- merge weights of row lr (8 lanes per row)
+    for (int k = 0; k < 4; ++k)
+      if (!(r < a.rows && cj + 16 * k < ns)) lv[k] = -__builtin_inff();
+    // ---- merge weights of row lr (its 16 lanes)
     float m = -__builtin_inff();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = fmaxf(m, lv[k]);
+    for (int k = 0; k < 4; ++k) m = fmaxf(m, lv[k]);
     if (r < a.rows)
-      for (int sk = lj + 64; sk < ns; sk += 8) m = fmaxf(m, lp[sk * rs]);
+      for (int sk = cj + 64; sk < ns; sk += 16) m = fmaxf(m, lp[(int64_t)sk * rs]);
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float z = 0.f, ev[8];
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float z = 0.f, ev[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       ev[k] = lv[k] == -__builtin_inff() ? 0.f : expf(lv[k] - m);
       z += ev[k];
     }
     if (r < a.rows)
-      for (int sk = lj + 64; sk < ns; sk += 8) {
-        const float ls = lp[sk * rs];
+      for (int sk = cj + 64; sk < ns; sk += 16) {
+        const float ls = lp[(int64_t)sk * rs];
         z += ls == -__builtin_inff() ? 0.f : expf(ls - m);
       }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) z += __shfl_xor(z, o, 64);
+    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
     const float inv = z > 0.f ? 1.f / z : 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) wt[lr][lj + 8 * k] = ev[k] * inv;
-    if (lj == 0) {
+    for (int k = 0; k < 4; ++k) wt[lr][cj + 16 * k] = ev[k] * inv;
+    if (cj == 0) {
       rowm[lr] = m;
       rowinv[lr] = inv;
-      if (a.lse && half == 0 && r < a.rows) a.lse[(int64_t)r * a.heads + h] = z > 0.f ? m + logf(z) : -__builtin_inff();
+      if (a.lse && r < a.rows) a.lse[(int64_t)r * a.heads + h] = z > 0.f ? m + logf(z) : -__builtin_inff();
     }
-    // LDS-only barrier: the weights are visible, the partial rows' loads stay
-    // in flight (a full barrier would wait for every outstanding load)
+    // LDS-only barrier: the weights are visible, the pieces stay in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // ---- merged tile in registers, chunk by chunk as the rows land; a chunk
-    // past the end, or one whose weight is 0 (it saw no token: its data may
-    // be anything), is dropped
-    f32x4 acc[16];
+    float acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = f32x4{};
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int jj = 0; jj < kF; ++jj)
+      for (int k = 0; k < 8; ++k) acc[j][k] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = jj < ns ? wt[r0 + 2 * i][jj] : 0.f;
+    for (int jj = 0; jj < kF; ++jj) {
+      const float e = jj < ns ? wt[lr][jj] : 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[i][k] = e > 0.f ? fmaf(e, v0[jj][i][k], acc[i][k]) : acc[i][k];
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[j][k] = e > 0.f ? fmaf(e, v0[jj][j][k], acc[j][k]) : acc[j][k];
+    }
     for (int s0 = kF; s0 < ns; s0 += 2) {
       if (s0 % kW == 0) {  // weights of chunks s0 .. s0 + kW - 1 from the rows' max and sum
         __syncthreads();
-        for (int idx = tid; idx < 32 * kW; idx += 256) {
+        for (int idx = tid; idx < 16 * kW; idx += 256) {
           const int rr = idx / kW, j = idx - rr * kW, rj = m0 + rr;
           float e = 0.f;
           if (rj < a.rows && s0 + j < ns && rowm[rr] != -__builtin_inff()) {
@@ -233,66 +252,63 @@ __global__ void __launch_bounds__(256) merge_out_uv_mfma(const OutUvArgs a) {
         }
         __syncthreads();
       }
-      f32x4 v[2][16];
+      Piece8<PT> v[2][4];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int64_t so = (int64_t)min(s0 + jj, ns - 1) * cs;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[jj][i] = load4(vrow[i] + so);
+        for (int j = 0; j < 4; ++j) v[jj][j].load(vr + so + 128 * j);
       }
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < 2; ++jj) {
+        const float e = s0 + jj < ns ? wt[lr][(s0 + jj) % kW] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = s0 + jj < ns ? wt[r0 + 2 * i][(s0 + jj) % kW] : 0.f;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) acc[i][k] += e > 0.f ? e * v[jj][i][k] : 0.f;
-        }
+          for (int k = 0; k < 8; ++k) acc[j][k] = e > 0.f ? fmaf(e, v[jj][j][k], acc[j][k]) : acc[j][k];
+      }
     }
+    // ---- the merged row as bf16 hi + lo: chunk cj + 16 j of row lr
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rr = r0 + 2 * i;
-      uint32_t hi[2], lo[2];
+    for (int j = 0; j < 4; ++j) {
+      uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float x0 = acc[i][2 * k], x1 = acc[i][2 * k + 1];
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = acc[j][2 * k], x1 = acc[j][2 * k + 1];
         hi[k] = pack_bf16x2(x0, x1);
         lo[k] = pack_bf16x2(x0 - __builtin_bit_cast(float, hi[k] << 16), x1 - __builtin_bit_cast(float, hi[k] & 0xFFFF0000u));
       }
-      const int off = rr * 1024 + (((c >> 1) ^ rr) << 4) + (c & 1) * 8;
-      *(u32x2*)(xs[0] + off) = u32x2{hi[0], hi[1]};
-      *(u32x2*)(xs[1] + off) = u32x2{lo[0], lo[1]};
+      const int off = lr * 1024 + (((cj + 16 * j) ^ lr) << 4);
+      *(u32x4*)(xs[0] + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *(u32x4*)(xs[1] + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
     __syncthreads();
-    // ---- products: A = merged rows n32, columns 128 wave + 16 ks + 8 g .. +7
-    f32x16 acc2[2] = {f32x16{}, f32x16{}};
+    // ---- products: B = merged row i16, columns 32 ks + 8 q4 .. +7
+    f32x4 acc2[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int q = 16 * wave + 2 * ks + g;
-      const int off = n32 * 1024 + ((q ^ n32) << 4);
-      const bf16x8 ah = *(const bf16x8*)(xs[0] + off);
-      const bf16x8 al = *(const bf16x8*)(xs[1] + off);
+    for (int ks = 0; ks < 16; ++ks) {
+      const int off = i16 * 1024 + (((4 * ks + q4) ^ i16) << 4);
+      const bf16x8 bh = *(const bf16x8*)(xs[0] + off);
+      const bf16x8 bl = *(const bf16x8*)(xs[1] + off);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        acc2[nt] = mfma32x32x16(ah, bw[nt][ks], acc2[nt]);
-        acc2[nt] = mfma32x32x16(al, bw[nt][ks], acc2[nt]);
+      for (int db = 0; db < 2; ++db) {
+        acc2[db] = mfma16x16x32(aw[db][ks], bh, acc2[db]);
+        acc2[db] = mfma16x16x32(aw[db][ks], bl, acc2[db]);
       }
     }
-    // partial tile of this wave's latent quarter: D row (i/4)*8 + 4g + i%4, column n32
+    // D: column i16 = row m0 + i16, rows 4 q4 + i = output dims of the block
+    const int orow = m0 + i16;
+    if (orow < a.rows) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) red[wave][nt][((i >> 2) * 8 + 4 * g + (i & 3)) * kPad + n32] = acc2[nt][i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = i * 256 + tid;
-      const int row = idx >> 6, d = idx & 63, nt = d >> 5, n = d & 31;
-      const float v = red[0][nt][row * kPad + n] + red[1][nt][row * kPad + n] + red[2][nt][row * kPad + n] +
-                      red[3][nt][row * kPad + n];
-      if (m0 + row < a.rows) store_out(a.out, ((int64_t)(m0 + row) * a.heads + h) * 128 + half * 64 + d, v, a.out_bf16);
+      for (int db = 0; db < 2; ++db) {
+        const int64_t e = ((int64_t)orow * a.heads + h) * 128 + 32 * wave + 16 * db + 4 * q4;
+        if (a.out_bf16)
+          *(u32x2*)((uint16_t*)a.out + e) = u32x2{pack_bf16x2(acc2[db][0], acc2[db][1]), pack_bf16x2(acc2[db][2], acc2[db][3])};
+        else
+          *(f32x4*)((float*)a.out + e) = acc2[db];
+      }
     }
-    __syncthreads();  // red, xs and wt are rewritten by the next tile
+    __syncthreads();  // xs and wt are rewritten by the next tile
   }
 }
 
@@ -363,8 +379,8 @@ __global__ void __launch_bounds__(256) out_uv_f32(const OutUvArgs a) {
   }
 }
 
-template __global__ void merge_out_uv_mfma<float>(const OutUvArgs);
-template __global__ void merge_out_uv_mfma<_Float16>(const OutUvArgs);
+template __global__ void merge_out_uv16<float>(const OutUvArgs);
+template __global__ void merge_out_uv16<_Float16>(const OutUvArgs);
 template __global__ void out_uv_f32<false>(const OutUvArgs);
 template __global__ void out_uv_f32<true>(const OutUvArgs);
 

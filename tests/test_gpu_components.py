@@ -144,7 +144,9 @@ def test_split_combine(B, ns, Sq, heads, part):
 
 @pytest.mark.parametrize("part", ["f32", "f16"])
 @pytest.mark.parametrize("B,ns,Sq,heads,wdt", [(3, 5, 2, 128, "bf16"), (37, 3, 1, 100, "bf16"),
-                                               (2, 64, 1, 128, "bf16"), (5, 7, 2, 16, "f32")])
+                                               (2, 64, 1, 128, "bf16"), (5, 7, 2, 16, "f32"),
+                                               # several 16-row tiles per workgroup; chunks past the first 64
+                                               (40, 4, 2, 128, "bf16"), (2, 130, 1, 128, "bf16")])
 def test_combine_out_uv(B, ns, Sq, heads, wdt, part):
     """The merge fused into the projection against the fp64 merge followed by
     the fp64 projection, and against mla_split_combine + mla_out_uv."""
