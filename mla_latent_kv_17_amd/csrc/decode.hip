@@ -1150,10 +1150,10 @@ decode_mfma_fp8(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 cache and queries: one workgroup (512 threads) per (sequence, KV chunk,
 // query row), fp32 arithmetic throughout.  The chunk is walked in 16-token
-// tiles copied HBM -> LDS by DMA into a ring of four buffers (three tiles in
-// flight).  Waves 4..7 only issue the copies (lane i of a copy brings 16
-// bytes of the tile's rows: coalesced), split over the two phases of a
-// tile so that their issue overlaps the arithmetic of waves 0..3:
+// tiles copied HBM -> LDS by DMA into a ring of four buffers (the first four
+// tiles requested at once, then two in flight).  Waves 4..7 only issue the
+// copies (lane i of a copy brings 16 bytes of the tile's rows: coalesced);
+// waves 0..3 do the arithmetic, per tile t:
 //   scores: wave w forms the scores of tokens 4w .. 4w+3, lane l summing
 //           q . c_t over latent floats 4l..4l+3 and 256+4l..+3 and RoPE
 //           float l (16-byte LDS reads, q held in registers), then a DPP
@@ -1161,7 +1161,8 @@ decode_mfma_fp8(const DecodeArgs a) {
 //   values: thread i rescales and accumulates latent columns 2i, 2i+1 with
 //           the tile's 16 weights (online softmax in the log2 domain,
 //           hardware exp2).
-// Two barriers per tile.  Rows past the row's visible range are zeroed in
+// One barrier per tile: after it, the scores of tile t+1 and the values of
+// tile t (double-buffered scores).  Rows past the row's visible range are zeroed in
 // LDS by the waves that copied them once their copies have landed (an
 // uninitialised pool row may hold NaN; its weight is 0).
 // ---------------------------------------------------------------------------
@@ -1223,7 +1224,7 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
   // zero this wave's copied pieces of tile t that lie past the range
   auto fix_tile = [&](int t) __attribute__((always_inline)) {
     const int t0 = tok0 + t * kT;
-    if (t0 + kT > tok1) {
+    if (t < ntiles && t0 + kT > tok1) {
 #pragma unroll
       for (int k = 0; k < kCopies; ++k) {
         const int idx = (kCopies * cw + k) * 64 + lane, tr = idx / 144;
@@ -1234,21 +1235,30 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
 
   if (copyw) {
     // ================= copy waves =================
+    // Barrier A0 needs tile 0, barrier B_j tile j+1.  Tiles 0..3 go out at
+    // once (all four buffers are free); after B_j (j >= 1) the buffer of
+    // tile j-1, read for the last time before B_j, takes tile j+3.
     if (ntiles > 0) {
-      for (int t = 0; t < 3; ++t) {
+      for (int t = 0; t < 4; ++t) {
         blk = tile_block(t);
         issue(t, 0, kCopies);
       }
-      blk = tile_block(3);
-    }
-    for (int t = 0; t < ntiles; ++t) {
-      wait_vmcnt<2 * kCopies>();  // tile t (tiles t+1, t+2 may still be in flight)
-      fix_tile(t);
-      __syncthreads();
-      issue(t + 3, 0, 5);  // into the buffer of tile t-1, whose reads ended before the barrier
-      __syncthreads();
-      issue(t + 3, 5, kCopies);
-      blk = tile_block(t + 4);
+      blk = tile_block(4);
+      wait_vmcnt<3 * kCopies>();  // tile 0 (tiles 1..3 may still be in flight)
+      fix_tile(0);
+      __syncthreads();  // A0
+      wait_vmcnt<2 * kCopies>();  // tile 1
+      fix_tile(1);
+      __syncthreads();  // B_0
+      for (int j = 1; j < ntiles; ++j) {
+        if (j >= 2) {
+          issue(j + 2, 0, kCopies);  // into the buffer of tile j-2
+          blk = tile_block(j + 3);
+        }
+        wait_vmcnt<kCopies>();  // tile j+1 (tile j+2 may still be in flight)
+        fix_tile(j + 1);
+        __syncthreads();  // B_j
+      }
     }
     wait_vmcnt<0>();  // copies issued for tiles past the range have landed
     return;
@@ -1262,8 +1272,8 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
   const float qr = ((const float*)a.q_rope + qoff * 64)[lane];
   const int c2 = 2 * (cw * 64 + lane);  // this thread's latent columns c2, c2 + 1
   float m = -__builtin_inff(), l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
+  // scores of tile t: wave w takes tokens 4w .. 4w+3, written to sc[t & 1]
+  auto scores = [&](int t) __attribute__((always_inline)) {
     const MLA_LDS float* tl = (const MLA_LDS float*)&tile[t % kBufN][0];
     float part[4];
 #pragma unroll
@@ -1282,7 +1292,10 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
       const int tok = tok0 + t * kT + 4 * cw + u;
       if (lane == u) sc[t & 1][4 * cw + u] = tok < tok1 ? sdot * a.scale_log2 : -__builtin_inff();
     }
-    __syncthreads();
+  };
+  // online softmax and values of tile t (its scores complete in sc[t & 1])
+  auto values = [&](int t) __attribute__((always_inline)) {
+    const MLA_LDS float* tl = (const MLA_LDS float*)&tile[t % kBufN][0];
     float x[kT];
     float mt = m;
 #pragma unroll
@@ -1304,6 +1317,18 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
       o1 = fmaf(pu, c1, o1);
     }
     m = mt;
+  };
+  // one barrier per tile: after B_t the scores of tile t+1 and the values of
+  // tile t (sc is double-buffered: B_t orders the values of tile t-1, which
+  // read sc[(t+1) & 1], before the scores of tile t+1 rewrite it)
+  if (ntiles > 0) {
+    __syncthreads();  // A0: tile 0 has landed
+    scores(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();  // B_t: the scores of tile t are complete, tile t+1 has landed
+    if (t + 1 < ntiles) scores(t + 1);
+    values(t);
   }
   const int64_t slot = (int64_t)b * a.num_splits + split;
   float* orow = (float*)a.o + (slot * a.rows + row) * 512;  // fp32 only (the launcher refuses fp16 here)
