@@ -676,7 +676,8 @@ int mla_attend_explicit(const mla_dims* dims, const void* q_nope, const void* q_
   hipStream_t s = (hipStream_t)stream;
   st = launch("mla::rebuild_kv", (const void*)mla::rebuild_kv, dim3((unsigned)rb_grid), dim3(512), a, s);
   if (st) return st;
-  return launch("mla::attend_explicit", (const void*)mla::attend_explicit, dim3((unsigned)at_grid), dim3(256), a, s);
+  return launch("mla::attend_explicit", (const void*)mla::attend_explicit, dim3((unsigned)at_grid), dim3(64 * mla::kAtWaves),
+                a, s);
 }
 
 int mla_attention_form(const mla_dims* dims, int32_t latent_dtype, int32_t* form) {

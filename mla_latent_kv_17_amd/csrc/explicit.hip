@@ -19,10 +19,11 @@
 //    values transposed per 32-token group (each group's 128 x 32 block
 //    contiguous, the tokens of a value dimension adjacent), both rounded to
 //    bf16, into the caller's workspace.
-//  * attend_explicit: workgroup = (sequence, head, 128 query tokens); wave w
-//    holds query tokens 32w .. 32w+31 as the 192-wide [q_nope ; q_rope] in
-//    registers.  Per 32 cached tokens (keys, RoPE keys from the cache, values
-//    in LDS): S^T = K Q^T over the 192 key dimensions, causal mask (query i
+//  * attend_explicit: workgroup = (sequence, head, 256 query tokens), eight
+//    waves; wave w holds query tokens 32w .. 32w+31 as the 192-wide
+//    [q_nope ; q_rope] in registers.  Per 32 cached tokens (keys, RoPE keys
+//    from the cache, values; copied to LDS by waves 0..3, four tiles in the
+//    ring): S^T = K Q^T over the 192 key dimensions, causal mask (query i
 //    sees the first len - (S_q - 1 - i) tokens), online softmax in the log2
 //    domain (running max and per-lane partial sums, the output rescaled),
 //    O^T += V^T P^T.  The scores' accumulator layout is the value product's
@@ -53,7 +54,7 @@ constexpr int kAtK = 0;                            // keys: 32 rows x 256 B
 constexpr int kAtRope = kAtTok * 256;              // RoPE keys: 32 rows x 128 B
 constexpr int kAtV = kAtRope + kAtTok * 128;       // values: 128 dims x 64 B
 constexpr int kAtTile = kAtV + 128 * kAtTok * 2;   // 20 KB
-constexpr int kAtBufs = 3;
+constexpr int kAtBufs = 4;
 constexpr float kSlack = 8.0f;                     // log2 headroom above a query's reference max
 
 // Bank swizzles of the attention tile (16-byte chunk index XOR): key rows
@@ -197,7 +198,7 @@ __global__ void __launch_bounds__(512) rebuild_kv(const ExplicitArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(256) attend_explicit(const ExplicitArgs a) {
+__global__ void __launch_bounds__(64 * kAtWaves) attend_explicit(const ExplicitArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kAtTile * kAtBufs];
   MLA_LDS uint8_t* const lds = (MLA_LDS uint8_t*)&smem[0];
   // placement: the query blocks of one (sequence, head) run on one XCD, back
@@ -250,6 +251,7 @@ __global__ void __launch_bounds__(256) attend_explicit(const ExplicitArgs a) {
   }
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int t) {
+    if (wave >= 4) return;  // waves 0..3 copy the tiles
     const int j0 = t * kAtTok;
     const int blk = load_uniform(a.block_table, (int64_t)b * a.max_blocks + (j0 >> 6));
     const uint8_t* rbase = a.rope + (int64_t)blk * a.rope_bs + (int64_t)(j0 & 63) * a.rope_rs;

@@ -101,7 +101,8 @@ struct ExplicitArgs {
 };
 constexpr int kRebuildTok = 256;  // tokens per rebuild workgroup
 constexpr int kRbBlockT = 4, kRbBlockH = 8;  // rebuild placement block: token tiles x heads
-constexpr int kExplicitQ = 128;   // query tokens per attention workgroup
+constexpr int kAtWaves = 8;       // waves per attention workgroup (32 query tokens each)
+constexpr int kExplicitQ = 32 * kAtWaves;  // query tokens per attention workgroup
 __global__ void rebuild_kv(const ExplicitArgs a);
 __global__ void attend_explicit(const ExplicitArgs a);
 

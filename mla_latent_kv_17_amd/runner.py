@@ -113,7 +113,7 @@ class DecodeStep:
     def project(self, stream=None):
         mla_out_uv(self.dev.dims, self.o_lat, self.dev.w_uv, self.out, stream)
 
-    # the fused merge walks the chunks a few at a time per 32-row tile, so it
+    # the fused merge walks the chunks a few at a time per 16-row tile, so it
     # pays one memory latency per round: with many chunks and few query rows
     # the separate merge, which spreads rows over workgroups, is faster
     FUSED_MERGE_MAX_SPLITS = 8
