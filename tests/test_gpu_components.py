@@ -1,6 +1,7 @@
 """Each C-ABI entry point on its own against the oracle's definition of that
-step: mla_absorb_q, mla_out_uv and mla_split_combine, at row counts that span
-several 32-row tiles with a ragged tail, and at the largest split count."""
+step: mla_absorb_q, mla_out_uv, mla_split_combine and mla_combine_out_uv, at
+row counts that span several row tiles with a ragged tail, and at the largest
+split count."""
 import math
 
 import numpy as np
