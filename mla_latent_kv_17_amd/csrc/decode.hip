@@ -1150,8 +1150,8 @@ decode_mfma_fp8(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 cache and queries: one workgroup (512 threads) per (sequence, KV chunk,
 // query row), fp32 arithmetic throughout.  The chunk is walked in 16-token
-// tiles copied HBM -> LDS by DMA into a ring of four buffers (the first four
-// tiles requested at once, then two in flight).  Waves 4..7 only issue the
+// tiles copied HBM -> LDS by DMA into a ring of four buffers (two or three
+// tiles in flight).  Waves 4..7 only issue the
 // copies (lane i of a copy brings 16 bytes of the tile's rows: coalesced);
 // waves 0..3 do the arithmetic, per tile t:
 //   scores: wave w forms the scores of tokens 4w .. 4w+3, lane l summing
@@ -1235,19 +1235,26 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
 
   if (copyw) {
     // ================= copy waves =================
-    // Barrier A0 needs tile 0, barrier B_j tile j+1.  Tiles 0..3 go out at
-    // once (all four buffers are free); after B_j (j >= 1) the buffer of
-    // tile j-1, read for the last time before B_j, takes tile j+3.
+    // Barrier A0 needs tile 0, barrier B_j tile j+1.  Tiles 0 and 1 go out
+    // first and A0 follows as soon as tile 0 has landed (the copies of a
+    // compute unit are issued at a limited rate: a chunk's first tiles are
+    // not held up behind its later ones); tiles 2 and 3 go out after A0, and
+    // after B_j (j >= 2) the buffer of tile j-2, read for the last time
+    // before B_{j-1}, takes tile j+2.
     if (ntiles > 0) {
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2; ++t) {
+        blk = tile_block(t);
+        issue(t, 0, kCopies);
+      }
+      wait_vmcnt<kCopies>();  // tile 0 (tile 1 may still be in flight)
+      fix_tile(0);
+      __syncthreads();  // A0
+      for (int t = 2; t < 4; ++t) {
         blk = tile_block(t);
         issue(t, 0, kCopies);
       }
       blk = tile_block(4);
-      wait_vmcnt<3 * kCopies>();  // tile 0 (tiles 1..3 may still be in flight)
-      fix_tile(0);
-      __syncthreads();  // A0
-      wait_vmcnt<2 * kCopies>();  // tile 1
+      wait_vmcnt<2 * kCopies>();  // tile 1 (tiles 2, 3 may still be in flight)
       fix_tile(1);
       __syncthreads();  // B_0
       for (int j = 1; j < ntiles; ++j) {
