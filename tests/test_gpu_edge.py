@@ -109,6 +109,26 @@ def test_late_score_far_above_first_page(alpha):
         compare(inp, ns)
 
 
+def _plant_token_f32(inp, b, t, head, alpha):
+    """_plant_token for an fp32 cache."""
+    qr = inp.q_rope[b * inp.wl.q_per_seq, head]
+    blk = inp.block_table[b, t // 64]
+    inp.latent[blk, t % 64, 512:] = np.where(qr >= 0, alpha, -alpha).astype(np.float32)
+
+
+@pytest.mark.parametrize("alpha", [20.0, 100.0])
+def test_late_score_far_above_first_page_fp32(alpha):
+    """The same for the fp32 decode, whose weights are formed against tile 0's
+    maximum: a later score far above it makes the chunk be walked again."""
+    wl = MI.small_variants()["fp32_b1_h16_t1k"].scaled(name=f"edge_jump_f32_{alpha:g}", batch=2, seq_len=700,
+                                                       num_splits=1, seed=4310)
+    inp = MI.generate(wl)
+    _plant_token_f32(inp, 0, 300, 0, alpha)
+    _plant_token_f32(inp, 1, 650, 5, alpha)
+    for ns in (1, 2):
+        compare(inp, ns)
+
+
 def test_empty_batch_launches_nothing():
     import torch
     import mla_latent_kv_17_amd as M
