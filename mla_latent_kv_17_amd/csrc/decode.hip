@@ -1150,33 +1150,38 @@ decode_mfma_fp8(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 cache and queries: one workgroup (512 threads) per (sequence, KV chunk,
 // query row), fp32 arithmetic throughout.  The chunk is walked in 16-token
-// tiles copied HBM -> LDS by DMA into a ring of four buffers (two or three
-// tiles in flight).  Waves 4..7 only issue the
-// copies (lane i of a copy brings 16 bytes of the tile's rows: coalesced);
-// waves 0..3 do the arithmetic, per tile t:
-//   scores: wave w forms the scores of tokens 4w .. 4w+3, lane l summing
-//           q . c_t over latent floats 4l..4l+3 and 256+4l..+3 and RoPE
-//           float l (16-byte LDS reads, q held in registers), then a DPP
-//           wave sum;
-//   values: thread i rescales and accumulates latent columns 2i, 2i+1 with
-//           the tile's 16 weights (online softmax in the log2 domain,
-//           hardware exp2).
-// One barrier per tile: after it, the scores of tile t+1 and the values of
-// tile t (double-buffered scores).  Rows past the row's visible range are zeroed in
-// LDS by the waves that copied them once their copies have landed (an
-// uninitialised pool row may hold NaN; its weight is 0).
+// tiles copied HBM -> LDS by DMA into a ring of four buffers (latent rows and
+// RoPE keys in separate arrays, so every 1 KB copy reads from one
+// wave-uniform base; two or three tiles in flight).  Two roles of four waves:
+//   score waves 0..3: wave w forms the scores of tokens 4w .. 4w+3, lane l
+//       summing q . c_t over latent floats 4l..4l+3 and 256+4l..+3 and RoPE
+//       float l (16-byte LDS reads against the query held in registers); the
+//       four tokens' sums are reduced within each row of 16 lanes (DPP) and
+//       the four row sums of each token go to LDS;
+//   value waves 4..7 issue the copies, and fold tile t into the output: lane
+//       l of every 16-lane row takes token l of the tile (the sum of its four
+//       row sums), the row maximum updates the running one (online softmax in
+//       the log2 domain, hardware exp2), and thread i accumulates latent
+//       columns 2i, 2i+1 with the 16 weights read from their lanes.
+// One barrier per tile: after barrier t the score waves form the scores of
+// tile t+1 while the value waves fold in tile t (scores double-buffered).
+// Rows past the row's visible range are zeroed in LDS by the waves that
+// copied them once their copies have landed (an uninitialised pool row may
+// hold NaN; its weight is 0).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
   constexpr int kT = 16;          // tokens per tile
-  constexpr int kRowF = 576;      // floats of a staged token row: latent, then RoPE key
+  constexpr int kRowF = 576;      // floats of a token row: latent, then RoPE key
   constexpr int kBufN = 4;        // tile ring
-  constexpr int kCopies = kT * kRowF * 4 / 1024 / 4;  // 1 KB copies per copy wave per tile (9)
+  constexpr int kCopies = kT * kRowF * 4 / 1024 / 4;  // 1 KB copies per value wave per tile (9)
   static_assert(kT * kRowF * 4 == 4 * kCopies * 1024, "whole copies per wave");
-  __shared__ __attribute__((aligned(1024))) float tile[kBufN][kT * kRowF];
-  __shared__ float sc[2][kT];
+  // a tile's latent rows [16][512] and RoPE keys [16][64], each ring slot
+  __shared__ __attribute__((aligned(1024))) float tlat[kBufN][kT * 512];
+  __shared__ __attribute__((aligned(1024))) float trope[kBufN][kT * 64];
+  __shared__ __attribute__((aligned(16))) float sp[2][kT * 4];  // [token][16-lane row] score sums
   if (blockDim.x != 512) return;  // the roles below assume eight waves
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const bool copyw = wave >= 4;
+  const bool valw = wave >= 4;
   const int cw = wave & 3;
   // XCD-aware placement: workgroup ids are dealt round-robin over the 8
   // XCDs, so XCD x takes a contiguous range of (unit, row) pairs and the rows
@@ -1197,28 +1202,34 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
   const int tok0 = p0 * 64;
   const int tok1 = min(min(p1 * 64, len), max(nvis, 0));  // this row's tokens of the chunk: [tok0, tok1)
   const int ntiles = tok1 > tok0 ? (tok1 - tok0 + kT - 1) / kT : 0;
-  const uint32_t tiles_lds = lds_addr((MLA_LDS float*)&tile[0][0]);
+  const uint32_t lat_lds = lds_addr((MLA_LDS float*)&tlat[0][0]);
+  const uint32_t rope_lds = lds_addr((MLA_LDS float*)&trope[0][0]);
 
-  // copy k of copy wave cw brings 16-byte piece idx = (9 cw + k) 64 + lane of
-  // the tile: row idx / 144, floats 4 (idx % 144) .. (the row's latent, then
-  // its RoPE key); tiles past the chunk, and rows past the range, copy the
-  // range's last row (any valid row: they are never used)
+  // The 36 1 KB copies of a tile, g = 9 cw + k for value wave 4 + cw: g < 32
+  // brings half g & 1 of latent row g / 2, g >= 32 the RoPE keys of rows
+  // 4 (g - 32) .. +3 (lane i: row + i / 16, bytes 16 (i % 16)).  Every copy
+  // reads one 64-row page from a wave-uniform base; rows past the range are
+  // read from the page (a whole block) and zeroed once landed.
   int blk = 0;
   auto tile_block = [&](int t) __attribute__((always_inline)) -> int {
     const int t0 = min(tok0 + t * kT, tok1 - 1);
     // scalar load: a vector one would make the compiler wait for the copies
     return load_uniform(a.block_table, (int64_t)b * a.max_blocks + (t0 >> 6));
   };
-  auto issue = [&](int t, int k0, int k1) __attribute__((always_inline)) {
-    const int t0 = min(tok0 + t * kT, tok1 - 1) & ~(kT - 1);  // tiles never cross a page
-    const uint32_t lbase = tiles_lds + (uint32_t)((t % kBufN) * kT * kRowF * 4);
+  const uint32_t rope_off = (uint32_t)((lane >> 4) * a.rope_rs + 16 * (lane & 15));
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int prow0 = (tok0 + t * kT) & 63;  // t < ntiles; tiles never cross a page
+    const uint8_t* lat = a.latent + blk * a.lat_bs + prow0 * a.lat_rs;
+    const uint8_t* rope = a.rope + blk * a.rope_bs + prow0 * a.rope_rs;
 #pragma unroll
-    for (int k = k0; k < k1; ++k) {
-      const int idx = (kCopies * cw + k) * 64 + lane, tr = idx / 144, c4 = idx - tr * 144;
-      const int64_t prow = min(t0 + tr, tok1 - 1) & 63;  // same page as t0
-      const uint8_t* src = c4 < 128 ? a.latent + blk * a.lat_bs + prow * a.lat_rs + 16 * c4
-                                    : a.rope + blk * a.rope_bs + prow * a.rope_rs + 16 * (c4 - 128);
-      dma16(src, lbase + (uint32_t)((kCopies * cw + k) * 1024));
+    for (int k = 0; k < kCopies; ++k) {
+      const int g = kCopies * cw + k;
+      if (g < 32)
+        dma16s(lat + (g >> 1) * a.lat_rs + (g & 1) * 1024, 16 * lane,
+               lat_lds + (uint32_t)(((t % kBufN) * kT * 512) * 4 + g * 1024));
+      else
+        dma16s(rope + 4 * (g - 32) * a.rope_rs, rope_off,
+               rope_lds + (uint32_t)(((t % kBufN) * kT * 64) * 4 + (g - 32) * 1024));
     }
   };
   // zero this wave's copied pieces of tile t that lie past the range
@@ -1227,122 +1238,138 @@ __global__ void __launch_bounds__(512) decode_f32(const DecodeArgs a) {
     if (t < ntiles && t0 + kT > tok1) {
 #pragma unroll
       for (int k = 0; k < kCopies; ++k) {
-        const int idx = (kCopies * cw + k) * 64 + lane, tr = idx / 144;
-        if (t0 + tr >= tok1) *(MLA_LDS f32x4*)(MLA_LDS float*)&tile[t % kBufN][idx * 4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int g = kCopies * cw + k;
+        const int tr = g < 32 ? g >> 1 : 4 * (g - 32) + (lane >> 4);
+        MLA_LDS float* dst = g < 32 ? (MLA_LDS float*)&tlat[t % kBufN][g * 256 + 4 * lane]
+                                    : (MLA_LDS float*)&trope[t % kBufN][(g - 32) * 256 + 4 * lane];
+        if (t0 + tr >= tok1) *(MLA_LDS f32x4*)dst = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
+  // The value waves' copy duties.  Barrier A0 needs tile 0, B_t tile t+1;
+  // after B_t the buffer of tile t-1 (read for the last time before B_t)
+  // takes tile t+3.
+  auto copy_start = [&]() __attribute__((always_inline)) {
+    blk = tile_block(0);
+    issue(0);
+    if (ntiles > 1) {
+      blk = tile_block(1);
+      issue(1);
+    }
+    wait_groups<kCopies, 1>(ntiles > 1 ? 1 : 0);  // tile 0 (tile 1 may still be in flight)
+    fix_tile(0);
+  };
+  auto copy_first = [&]() __attribute__((always_inline)) {
+    if (ntiles > 2) {
+      blk = tile_block(2);
+      issue(2);
+    }
+    blk = tile_block(3);
+  };
+  auto copy_land_first = [&]() __attribute__((always_inline)) {
+    wait_groups<kCopies, 1>(ntiles > 2 ? 1 : 0);  // tile 1 (tile 2 may still be in flight)
+    fix_tile(1);
+  };
+  auto copy_issue = [&](int t) __attribute__((always_inline)) {
+    if (t + 3 < ntiles) {
+      issue(t + 3);
+      blk = tile_block(t + 4);
+    }
+  };
+  auto copy_land = [&](int t) __attribute__((always_inline)) {
+    wait_groups<kCopies, 1>(t + 3 < ntiles ? 1 : 0);  // tile t+2 (tile t+3 may still be in flight)
+    fix_tile(t + 2);
+  };
 
-  if (copyw) {
-    // ================= copy waves =================
-    // Barrier A0 needs tile 0, barrier B_j tile j+1.  Tiles 0 and 1 go out
-    // first and A0 follows as soon as tile 0 has landed (the copies of a
-    // compute unit are issued at a limited rate: a chunk's first tiles are
-    // not held up behind its later ones); tiles 2 and 3 go out after A0, and
-    // after B_j (j >= 2) the buffer of tile j-2, read for the last time
-    // before B_{j-1}, takes tile j+2.
+  if (!valw) {
+    // ================= score waves =================
+    const int64_t qoff = (int64_t)b * a.rows + row;
+    const float* ql = (const float*)a.q_lat + qoff * 512;
+    const f32x4 qa = *(const f32x4*)(ql + 4 * lane);
+    const f32x4 qb = *(const f32x4*)(ql + 256 + 4 * lane);
+    const float qr = ((const float*)a.q_rope + qoff * 64)[lane];
+    // scores of tile t: wave w takes tokens 4w .. 4w+3; sp[t & 1][4 u + r]
+    // receives row r's share of token u
+    auto scores = [&](int t) __attribute__((always_inline)) {
+      float part[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const MLA_LDS float* tr = (const MLA_LDS float*)&tlat[t % kBufN][(4 * cw + u) * 512];
+        const f32x4 x = *(const MLA_LDS f32x4*)(tr + 4 * lane);
+        const f32x4 y = *(const MLA_LDS f32x4*)(tr + 256 + 4 * lane);
+        const float kr = trope[t % kBufN][(4 * cw + u) * 64 + lane];
+        const float ax = fmaf(x[0], qa[0], fmaf(x[1], qa[1], fmaf(x[2], qa[2], x[3] * qa[3])));
+        const float ay = fmaf(y[0], qb[0], fmaf(y[1], qb[1], fmaf(y[2], qb[2], fmaf(y[3], qb[3], kr * qr))));
+        part[u] = ax + ay;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) part[u] = row_sum(part[u]);
+      const int u = lane & 15;
+      if (u < 4) {
+        const float v = u == 0 ? part[0] : u == 1 ? part[1] : u == 2 ? part[2] : part[3];
+        sp[t & 1][4 * (4 * cw + u) + (lane >> 4)] = v;
+      }
+    };
     if (ntiles > 0) {
-      for (int t = 0; t < 2; ++t) {
-        blk = tile_block(t);
-        issue(t, 0, kCopies);
-      }
-      wait_vmcnt<kCopies>();  // tile 0 (tile 1 may still be in flight)
-      fix_tile(0);
-      __syncthreads();  // A0
-      for (int t = 2; t < 4; ++t) {
-        blk = tile_block(t);
-        issue(t, 0, kCopies);
-      }
-      blk = tile_block(4);
-      wait_vmcnt<2 * kCopies>();  // tile 1 (tiles 2, 3 may still be in flight)
-      fix_tile(1);
-      __syncthreads();  // B_0
-      for (int j = 1; j < ntiles; ++j) {
-        if (j >= 2) {
-          issue(j + 2, 0, kCopies);  // into the buffer of tile j-2
-          blk = tile_block(j + 3);
-        }
-        wait_vmcnt<kCopies>();  // tile j+1 (tile j+2 may still be in flight)
-        fix_tile(j + 1);
-        __syncthreads();  // B_j
+      __syncthreads();  // A0: tile 0 has landed
+      scores(0);
+      __syncthreads();  // B_0: the scores of tile 0 are complete, tile 1 has landed
+      for (int t = 0; t + 1 < ntiles; ++t) {
+        scores(t + 1);
+        __syncthreads();  // B_{t+1}
       }
     }
-    wait_vmcnt<0>();  // copies issued for tiles past the range have landed
     return;
   }
 
-  // ================= arithmetic waves =================
-  const int64_t qoff = (int64_t)b * a.rows + row;
-  const float* ql = (const float*)a.q_lat + qoff * 512;
-  const f32x4 qa = *(const f32x4*)(ql + 4 * lane);
-  const f32x4 qb = *(const f32x4*)(ql + 256 + 4 * lane);
-  const float qr = ((const float*)a.q_rope + qoff * 64)[lane];
+  // ================= value waves =================
   const int c2 = 2 * (cw * 64 + lane);  // this thread's latent columns c2, c2 + 1
   float m = -__builtin_inff(), l = 0.f, o0 = 0.f, o1 = 0.f;
-  // scores of tile t: wave w takes tokens 4w .. 4w+3, written to sc[t & 1]
-  auto scores = [&](int t) __attribute__((always_inline)) {
-    const MLA_LDS float* tl = (const MLA_LDS float*)&tile[t % kBufN][0];
-    float part[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const MLA_LDS float* tr = tl + (4 * cw + u) * kRowF;
-      const f32x4 x = *(const MLA_LDS f32x4*)(tr + 4 * lane);
-      const f32x4 y = *(const MLA_LDS f32x4*)(tr + 256 + 4 * lane);
-      float acc = tr[512 + lane] * qr;
-      acc = fmaf(x[0], qa[0], fmaf(x[1], qa[1], fmaf(x[2], qa[2], fmaf(x[3], qa[3], acc))));
-      acc = fmaf(y[0], qb[0], fmaf(y[1], qb[1], fmaf(y[2], qb[2], fmaf(y[3], qb[3], acc))));
-      part[u] = acc;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float sdot = wave_sum_rows(part[u]);
-      const int tok = tok0 + t * kT + 4 * cw + u;
-      if (lane == u) sc[t & 1][4 * cw + u] = tok < tok1 ? sdot * a.scale_log2 : -__builtin_inff();
-    }
-  };
-  // online softmax and values of tile t (its scores complete in sc[t & 1])
+  // online softmax and values of tile t (its scores complete in sp[t & 1])
   auto values = [&](int t) __attribute__((always_inline)) {
-    const MLA_LDS float* tl = (const MLA_LDS float*)&tile[t % kBufN][0];
-    float x[kT];
-    float mt = m;
-#pragma unroll
-    for (int u = 0; u < kT; ++u) {
-      x[u] = sc[t & 1][u];
-      mt = fmaxf(mt, x[u]);
-    }
+    const MLA_LDS float* tl = (const MLA_LDS float*)&tlat[t % kBufN][0];
+    const int u = lane & 15;
+    const f32x4 pr = *(const MLA_LDS f32x4*)&sp[t & 1][4 * u];
+    const float s = tok0 + t * kT + u < tok1 ? ((pr[0] + pr[1]) + (pr[2] + pr[3])) * a.scale_log2
+                                             : -__builtin_inff();
     // every tile holds at least one token of the range, so mt is finite
+    const float mt = fmaxf(m, row_max(s));
     const float alpha = __builtin_amdgcn_exp2f(m - mt);  // 0 on the first tile (m = -inf)
-    l *= alpha;
+    const float p = __builtin_amdgcn_exp2f(s - mt);      // lane u: token u's weight
+    l = l * alpha + row_sum(p);
     o0 *= alpha;
     o1 *= alpha;
 #pragma unroll
-    for (int u = 0; u < kT; ++u) {
-      const float pu = __builtin_amdgcn_exp2f(x[u] - mt);
-      const float c0 = tl[u * kRowF + c2], c1 = tl[u * kRowF + c2 + 1];  // one 8-byte read
-      l += pu;
-      o0 = fmaf(pu, c0, o0);
-      o1 = fmaf(pu, c1, o1);
+    for (int v = 0; v < kT; ++v) {
+      const float pv = lane_f(p, v);
+      const float c0 = tl[v * 512 + c2], c1 = tl[v * 512 + c2 + 1];  // one 8-byte read
+      o0 = fmaf(pv, c0, o0);
+      o1 = fmaf(pv, c1, o1);
     }
     m = mt;
   };
-  // one barrier per tile: after B_t the scores of tile t+1 and the values of
-  // tile t (sc is double-buffered: B_t orders the values of tile t-1, which
-  // read sc[(t+1) & 1], before the scores of tile t+1 rewrite it)
   if (ntiles > 0) {
-    __syncthreads();  // A0: tile 0 has landed
-    scores(0);
+    copy_start();
+    __syncthreads();  // A0
+    copy_first();
+    copy_land_first();
+    __syncthreads();  // B_0
+    for (int t = 0; t < ntiles; ++t) {
+      copy_issue(t);
+      values(t);
+      if (t + 1 < ntiles) {
+        copy_land(t);
+        __syncthreads();  // B_{t+1}
+      }
+    }
   }
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // B_t: the scores of tile t are complete, tile t+1 has landed
-    if (t + 1 < ntiles) scores(t + 1);
-    values(t);
-  }
+  wait_vmcnt<0>();
   const int64_t slot = (int64_t)b * a.num_splits + split;
   float* orow = (float*)a.o + (slot * a.rows + row) * 512;  // fp32 only (the launcher refuses fp16 here)
   const float inv = l > 0.f ? 1.f / l : 0.f;
   orow[c2] = o0 * inv;
   orow[c2 + 1] = o1 * inv;
-  if (tid == 0) a.lse[slot * a.rows + row] = l > 0.f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
+  if (wave == 4 && lane == 0) a.lse[slot * a.rows + row] = l > 0.f ? (m + log2f(l)) * kLn2 : -__builtin_inff();
 }
 
 template __global__ void decode_mfma_bf16<64>(const DecodeArgs a);
