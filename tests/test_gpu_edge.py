@@ -66,6 +66,17 @@ def test_empty_and_single_token_sequences(dtype, sq):
         compare(inp, ns)
 
 
+def test_fp32_tile_boundaries():
+    """fp32 cache: visible ranges ending on both sides of the kernel's 16-token
+    tile edges (queries 0 and 1 of a sequence see len - 1 and len tokens), and
+    chunks of one to thirteen tiles, so the four-slot tile ring is refilled."""
+    wl = BASE.scaled(name="edge_f32_tiles", batch=12, q_per_seq=2, heads=16, cache_dtype="f32", len_range=None,
+                     lens=(15, 16, 17, 31, 32, 33, 47, 48, 49, 80, 129, 200), spare_blocks=2, seed=4100)
+    inp = MI.generate(wl)
+    for ns in (1, 2, 4):
+        compare(inp, ns)
+
+
 @pytest.mark.parametrize("heads,sq", [(16, 1), (100, 1), (100, 2), (128, 2)])
 def test_partial_row_blocks(heads, sq):
     wl = BASE.scaled(name=f"edge_rows_h{heads}_sq{sq}", batch=3, q_per_seq=sq, heads=heads,
