@@ -31,6 +31,7 @@
 //    rank the lower expert index first.  Cross-lane steps are DPP moves
 //    within rows of 16 lanes, plus one lane read per row for 64 lanes.
 #include "mla_device.h"
+#include "mla_copy.h"
 #include "gate_kernels.h"
 #include "proj_chunk.h"
 
@@ -51,93 +52,84 @@ __global__ void __launch_bounds__(256) gate_proj_mfma(const GateArgs a) {
 // Many tokens: workgroup (slice x, token tile y) computes the affinities of
 // tokens 128y .. 128y+127 with every expert over d_model slice x.  Per
 // 64-wide stage the 128 token rows and the 32 * kNT centroid rows (rows past
-// the last token or expert repeat it; their results are never stored) are
-// loaded as 128-byte rows, 8 rows per wave load, into one of two LDS
-// buffers (rows padded to 144 bytes so that the operand reads, 8 rows per
-// pass at one column, hit distinct banks); the loads of the next two stages
-// are in flight while one is multiplied.  Wave w owns token tile w (32
-// tokens) against all kNT expert tiles, so each staged centroid row serves
-// 128 tokens.  The results leave through LDS: each wave writes its tile
-// there and stores rows of 16-byte pieces.
+// the last token or expert repeat it; their results are never stored) go
+// HBM -> LDS by DMA as 128-byte rows, 1 KB (eight rows) per copy, into a
+// ring of kS stage slots, kS - 1 stages in flight while one is multiplied
+// (one barrier per stage).  The copies are contiguous in LDS, so the row's
+// 16-byte pieces are permuted at the source instead of padding the rows:
+// piece p of row r sits at slot p ^ ((r >> 1) & 7), and the operand reads (16
+// rows per pass at one piece) hit 16 distinct bank groups.  Wave w owns
+// token tile w (32 tokens) against all kNT expert tiles, so each staged
+// centroid row serves 128 tokens.  The results leave through LDS: each wave
+// writes its tile there and stores rows of 16-byte pieces.
 template <int kNT>
 __global__ void __launch_bounds__(256) gate_proj_tall(const GateArgs a) {
-  constexpr int kRow = 144;
-  constexpr int kER = 32 * kNT;                            // staged centroid rows
-  constexpr int kLoads = (kGateTallM + kER) / 32;          // wave loads per lane per stage
-  constexpr int kBuf = (kGateTallM + kER) * kRow;          // one stage buffer
+  constexpr int kRows = kGateTallM + 32 * kNT;             // staged rows per stage
+  constexpr int kStage = kRows * 128;                      // bytes of a stage slot
+  constexpr int kS = 147456 / kStage < 4 ? 147456 / kStage : 4;  // ring slots
+  constexpr int kPer = kRows / 8 / 4;                      // 1 KB copies per wave per stage
+  static_assert(kS >= 3 && kPer * 4 * 8 == kRows && kPer * (kS - 2) < 64, "ring shape");
   constexpr int kOutRow = 128 * 4 + 16;                    // output staging row: 128 fp32 + pad
   constexpr int kOutWave = 32 * kOutRow;                   // one wave's output staging
-  constexpr int kLds = 2 * kBuf > 4 * kOutWave ? 2 * kBuf : 4 * kOutWave;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 5, n32 = lane & 31, sub = lane >> 3, piece = lane & 7;
+  constexpr int kLds = kS * kStage > 4 * kOutWave ? kS * kStage : 4 * kOutWave;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 5, n32 = lane & 31;
   const int T = a.tokens, N = a.n_experts;
   const int m0 = blockIdx.y * kGateTallM;
   const int k_lo = blockIdx.x * a.kslice;
   const int stages = (min(a.d_model, k_lo + a.kslice) - k_lo) / 64;
-  const uint16_t* u = (const uint16_t*)a.u;
-  const uint16_t* e = (const uint16_t*)a.e;
   const int64_t dm = a.d_model;
-  // two register sets hold the next two stages' rows while one is multiplied
-  u32x4 va[kLoads], vb[kLoads];
-  auto load = [&](u32x4 (&v)[kLoads], int st) __attribute__((always_inline)) {
-    const int k0 = k_lo + 64 * st;
+  const uint32_t lds0 = (uint32_t)(size_t)(MLA_LDS uint8_t*)lds;
+  // copy c = kPer wave + k brings rows 8c .. 8c+7: lane i reads source piece
+  // (i & 7) ^ swz(row) of row 8c + i / 8 (a fixed address per copy, plus the
+  // stage's column offset)
+  const uint8_t* src[kPer];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int r = 32 * i + 8 * wave + sub;
-      const uint16_t* src = i < kGateTallM / 32 ? u + min(m0 + r, T - 1) * dm : e + min(r - kGateTallM, N - 1) * dm;
-      v[i] = *(const u32x4*)(src + k0 + 8 * piece);
-    }
-  };
-  auto store = [&](const u32x4 (&v)[kLoads], int b) __attribute__((always_inline)) {
+  for (int k = 0; k < kPer; ++k) {
+    const int r = 8 * (kPer * wave + k) + (lane >> 3);
+    const uint16_t* row = r < kGateTallM ? (const uint16_t*)a.u + min(m0 + r, T - 1) * dm
+                                         : (const uint16_t*)a.e + min(r - kGateTallM, N - 1) * dm;
+    src[k] = (const uint8_t*)(row + k_lo) + 16 * ((lane & 7) ^ ((r >> 1) & 7));
+  }
+  auto issue = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int r = 32 * i + 8 * wave + sub;  // u rows, then e rows: one row index space
-      *(MLA_LDS u32x4*)&lds[b * kBuf + r * kRow + 16 * piece] = v[i];
-    }
+    for (int k = 0; k < kPer; ++k)
+      dma16(src[k] + 128 * st, lds0 + (uint32_t)((st % kS) * kStage + (kPer * wave + k) * 1024));
   };
   f32x16 acc[kNT];
 #pragma unroll
   for (int j = 0; j < kNT; ++j) acc[j] = f32x16{};
-  auto compute = [&](int b) __attribute__((always_inline)) {
-    const uint8_t* buf = &lds[b * kBuf];
+  // operand rows: 32 wave + n32 (tokens), kGateTallM + 32 j + n32 (experts);
+  // k-step ks reads piece 2 ks + g
+  const int ra = 32 * wave + n32;
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const MLA_LDS uint8_t* buf = (const MLA_LDS uint8_t*)lds + (st % kS) * kStage;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int kb = 32 * ks + 16 * g;
-      const bf16x8 av = *(const MLA_LDS bf16x8*)&buf[(32 * wave + n32) * kRow + kb];
+      const int p = 2 * ks + g;
+      const bf16x8 av = *(const MLA_LDS bf16x8*)(buf + ra * 128 + 16 * (p ^ ((ra >> 1) & 7)));
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        const bf16x8 bv = *(const MLA_LDS bf16x8*)&buf[(kGateTallM + 32 * j + n32) * kRow + kb];
+        const int rb = kGateTallM + 32 * j + n32;
+        const bf16x8 bv = *(const MLA_LDS bf16x8*)(buf + rb * 128 + 16 * (p ^ ((rb >> 1) & 7)));
         acc[j] = mfma32x32x16(av, bv, acc[j]);
       }
     }
   };
-  // stage s sits in LDS buffer s & 1 while it is multiplied; stage s + 1 is
-  // stored into the other buffer after that (its readers, stage s - 1, are
-  // past the barrier), and the freed register set starts loading stage
-  // s + 3.  Loads and stores are unconditional (stage numbers clamped to the
-  // last; a store past the last stage lands in a buffer nobody reads again),
-  // so the loop body is straight-line and each store waits only for its own
-  // register set.
+  // stages 0 .. kS-2 go out first; before barrier B_st each wave waits for
+  // its copies of stage st (the ones issued after it may stay in flight);
+  // after B_st every wave is done with stage st-1, whose slot takes stage
+  // st+kS-1
   const int last = stages - 1;
-  load(va, 0);
-  store(va, 0);
-  load(va, min(1, last));
-  load(vb, min(2, last));
-  __syncthreads();
-  int st = 0;
-  for (; st + 1 < stages; st += 2) {
-    compute(0);
-    store(va, 1);
-    load(va, min(st + 3, last));
-    __syncthreads();
-    compute(1);
-    store(vb, 0);
-    load(vb, min(st + 4, last));
-    __syncthreads();
+  for (int st = 0; st <= min(kS - 2, last); ++st) issue(st);
+  for (int st = 0; st < stages; ++st) {
+    wait_groups<kPer, kS - 2>(min(kS - 2, last - st));
+    __syncthreads();  // B_st
+    if (st + kS - 1 <= last) issue(st + kS - 1);
+    compute(st);
   }
-  if (st < stages) compute(0);  // an odd stage count: the last stage is in buffer 0
-  __syncthreads();              // every wave is done with the stage buffers
+  __syncthreads();  // every wave is done with the stage slots
   // out: up to four expert tiles (128 columns) at a time through the wave's
   // own LDS area.  D lane l, register i: token (i/4)*8 + 4g + i%4 of the
   // wave's tile, expert n32 of the tile
