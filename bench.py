@@ -145,6 +145,8 @@ def cpu_baseline(inp, budget_s: float):
     return {"value": kv_equiv / el, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(done)} (sequence, head) rows of {wl.name} ({wl.batch * wl.heads} in a step), "
                       f"explicit fp64 K/V reconstruction, {el:.1f} s",
+            "method": "measured in this run on the sample; value = the sample's KV-token equivalents / its time "
+                      "(a whole step is not run on the host)",
             "cpu_model": cpu_model(), "blas": blas_vendor()}
 
 
@@ -486,6 +488,9 @@ def main():
         "roofline": {**roof, "frac_of_measured": frac_measured, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                                      "calibrated on a 256 MiB copy)",
+                     "traffic_source": "not measured in this run: read from profiles/decode_bf16_b32_h128_t4k_counters.json "
+                                       "(rocprofv3 counter runs), reported only while the decode sources hash to the "
+                                       "value recorded there; null otherwise",
                      "kernel": DECODE_KERNEL[wl.cache_dtype], "launch_ms": dec_avg,
                      "launch_timing": f"{K} back-to-back launches over {n_rot} cache copies, HIP events",
                      "algorithmic_bytes": cache_bytes},
