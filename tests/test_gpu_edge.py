@@ -77,9 +77,10 @@ def test_fp32_tile_boundaries():
         compare(inp, ns)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
 @pytest.mark.parametrize("heads,sq", [(16, 1), (100, 1), (100, 2), (128, 2)])
-def test_partial_row_blocks(heads, sq):
-    wl = BASE.scaled(name=f"edge_rows_h{heads}_sq{sq}", batch=3, q_per_seq=sq, heads=heads,
+def test_partial_row_blocks(heads, sq, dtype):
+    wl = BASE.scaled(name=f"edge_rows_h{heads}_sq{sq}_{dtype}", batch=3, q_per_seq=sq, heads=heads, cache_dtype=dtype,
                      len_range=(100, 400), spare_blocks=2, seed=4100 + heads + sq)
     inp = MI.generate(wl)
     compare(inp, 2)
