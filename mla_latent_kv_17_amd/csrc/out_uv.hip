@@ -319,6 +319,55 @@ __global__ void __launch_bounds__(256) merge_out_uv16(const OutUvArgs a) {
 // wave (DPP).  o_lat comes from memory, or (kMerge) is merged from the chunk
 // partials into LDS first (weights exp(lse_s - max) over their sum, as in
 // split_combine).
+
+// Columns 4c .. 4c+3 of one row merged from its chunk partials (element
+// index op of chunk 0, chunk s at op + s * cs; log-sum-exps at lp[s * ls]):
+// rounds of 16 chunks with every load of a round issued before any is used
+// (indices past the last chunk read the last one and are not counted); the
+// running maximum rescales the sums between rounds.  A chunk with lse = -inf
+// takes no part, whatever its partial holds.  Returns the normalised row
+// piece and, through lse_out, ln of the weight sum plus the maximum.
+template <typename PT>
+__device__ __forceinline__ f32x4 merge_row4(const PT* part, int64_t op, int64_t cs, const float* lp, int64_t ls,
+                                            int ns, float& lse_out) {
+  constexpr int kR = 16;
+  float m = -__builtin_inff(), z = 0.f;
+  f32x4 x = f32x4{};
+  for (int s0 = 0; s0 < ns; s0 += kR) {
+    float l[kR];
+    f32x4 pv[kR];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int sc = min(s0 + k, ns - 1);
+      l[k] = lp[sc * ls];
+      pv[k] = load4(part + op + sc * cs);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any result is used
+#pragma unroll
+    for (int k = 0; k < kR; ++k)
+      if (s0 + k >= ns) l[k] = -__builtin_inff();
+    float mr = m;
+#pragma unroll
+    for (int k = 0; k < kR; ++k) mr = fmaxf(mr, l[k]);
+    // branch-free, so that the round's loads issue together: while no chunk
+    // holds a token, m and mr are -inf and every weight below is 0
+    const float c = m == -__builtin_inff() ? 0.f : expf(m - mr);
+    z *= c;
+    x *= c;
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const bool live = l[k] != -__builtin_inff();
+      const float e = live ? expf(l[k] - mr) : 0.f;
+      z += e;
+      const f32x4 y = x + e * pv[k];
+      x = live ? y : x;
+    }
+    m = mr;
+  }
+  lse_out = z > 0.f ? m + logf(z) : -__builtin_inff();
+  return x * (z > 0.f ? 1.f / z : 0.f);
+}
+
 template <bool kMerge>
 __global__ void __launch_bounds__(256) out_uv_f32(const OutUvArgs a) {
   __shared__ __attribute__((aligned(16))) float xs[512];
@@ -339,25 +388,13 @@ __global__ void __launch_bounds__(256) out_uv_f32(const OutUvArgs a) {
         const int b = r / a.sq, q = r - b * a.sq;
         const int64_t rs = (int64_t)a.sq * a.heads;
         const int64_t base = (int64_t)b * a.num_splits * rs + (int64_t)q * a.heads + h;
-        const float* lp = a.lse_part + base;
         const int64_t op = base * 512 + 4 * tid;  // element index of the chunk-0 partial
-        float m = -__builtin_inff();
-        for (int s = 0; s < a.num_splits; ++s) m = fmaxf(m, lp[s * rs]);
-        f32x4 x = f32x4{};
-        float z = 0.f;
-        if (m != -__builtin_inff()) {
-          for (int s = 0; s < a.num_splits; ++s) {
-            const float ls = lp[s * rs];
-            if (ls == -__builtin_inff()) continue;
-            const float e = expf(ls - m);
-            z += e;
-            const int64_t i = op + s * rs * 512;
-            x += e * (a.part_f16 ? load4((const _Float16*)a.o_part + i) : load4((const float*)a.o_part + i));
-          }
-        }
-        *(f32x4*)&xs[4 * tid] = x * (z > 0.f ? 1.f / z : 0.f);
-        if (a.lse && tid == 0 && (blockIdx.x & 7) == 0)
-          a.lse[(int64_t)r * a.heads + h] = z > 0.f ? m + logf(z) : -__builtin_inff();
+        float lse_r;
+        const f32x4 x = a.part_f16
+                            ? merge_row4((const _Float16*)a.o_part, op, rs * 512, a.lse_part + base, rs, a.num_splits, lse_r)
+                            : merge_row4((const float*)a.o_part, op, rs * 512, a.lse_part + base, rs, a.num_splits, lse_r);
+        *(f32x4*)&xs[4 * tid] = x;
+        if (a.lse && tid == 0 && (blockIdx.x & 7) == 0) a.lse[(int64_t)r * a.heads + h] = lse_r;
       }
     } else {
       if (tid < 128) *(f32x4*)&xs[4 * tid] = *(const f32x4*)(a.o_lat + ((int64_t)r * a.heads + h) * 512 + 4 * tid);

@@ -113,16 +113,18 @@ class DecodeStep:
     def project(self, stream=None):
         mla_out_uv(self.dev.dims, self.o_lat, self.dev.w_uv, self.out, stream)
 
-    # the fused merge walks the chunks a few at a time per 16-row tile, so it
-    # pays one memory latency per round: with many chunks and few query rows
-    # the separate merge, which spreads rows over workgroups, is faster
+    # the fused merge of bf16 weights walks the chunks a few at a time per
+    # 16-row tile, so it pays one memory latency per round: with many chunks
+    # and few query rows the separate merge, which spreads rows over
+    # workgroups, is faster.  The fp32 form issues 16 chunks' loads at once
+    # and is fused at every chunk count.
     FUSED_MERGE_MAX_SPLITS = 8
 
     def merge_project(self, stream=None):
-        """out and lse; with 1 < num_splits <= FUSED_MERGE_MAX_SPLITS the merge is
-        fused into the projection (mla_combine_out_uv), otherwise mla_split_combine
-        then mla_out_uv."""
-        if self.num_splits > self.FUSED_MERGE_MAX_SPLITS:
+        """out and lse; with 1 < num_splits (at most FUSED_MERGE_MAX_SPLITS for
+        bf16 weights) the merge is fused into the projection
+        (mla_combine_out_uv), otherwise mla_split_combine then mla_out_uv."""
+        if self.num_splits > self.FUSED_MERGE_MAX_SPLITS and self.dev.w_uv.dtype != torch.float32:
             self.combine(stream)
             self.project(stream)
         elif self.num_splits > 1:

@@ -147,7 +147,10 @@ def test_split_combine(B, ns, Sq, heads, part):
 @pytest.mark.parametrize("B,ns,Sq,heads,wdt", [(3, 5, 2, 128, "bf16"), (37, 3, 1, 100, "bf16"),
                                                (2, 64, 1, 128, "bf16"), (5, 7, 2, 16, "f32"),
                                                # several 16-row tiles per workgroup; chunks past the first 64
-                                               (40, 4, 2, 128, "bf16"), (2, 130, 1, 128, "bf16")])
+                                               (40, 4, 2, 128, "bf16"), (2, 130, 1, 128, "bf16"),
+                                               # fp32 weights: one full round of 16 chunks, and three
+                                               # rounds with a partial last one
+                                               (1, 16, 1, 16, "f32"), (2, 40, 2, 16, "f32")])
 def test_combine_out_uv(B, ns, Sq, heads, wdt, part):
     """The merge fused into the projection against the fp64 merge followed by
     the fp64 projection, and against mla_split_combine + mla_out_uv."""
