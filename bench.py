@@ -484,8 +484,8 @@ def main():
                    "q_per_seq": wl.q_per_seq, "heads": wl.heads, "d_latent": 512, "d_rope": 64, "d_head": 128,
                    "block_size": 64, "cache_dtype": wl.cache_dtype, "num_splits": step.num_splits,
                    "steps_timed": "absorb_q + decode + the split merge fused into out_uv (combine_out_uv; split_combine "
-                                  "+ out_uv above 8 chunks with bf16 weights, out_uv alone for one chunk), caches "
-                                  "evicted before each"},
+                                  "+ out_uv above 8 chunks with bf16 weights and more than 8 query rows, out_uv alone "
+                                  "for one chunk), caches evicted before each"},
         "roofline": {**roof, "frac_of_measured": frac_measured, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                                      "calibrated on a 256 MiB copy)",

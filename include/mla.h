@@ -219,8 +219,9 @@ int mla_out_uv(const mla_dims* dims, const float* o_lat, const void* w_uv, int32
  * (layouts and partial dtypes as for mla_split_combine);
  * w_uv, w_dtype, out, out_dtype: as for mla_out_uv; lse: [batch*q_per_seq][heads]
  * fp32, or NULL.
- * Chunks with lse_s = -inf carry weight 0 (their o_s is not read); a row whose
- * chunks all do gets out = 0 and lse = -inf.  Same accuracy as the two calls. */
+ * Chunks with lse_s = -inf carry weight 0 (their o_s may hold anything, NaN
+ * included, and never reaches the result); a row whose chunks all do gets
+ * out = 0 and lse = -inf.  Same accuracy as the two calls. */
 int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_part, int32_t part_dtype,
                        const float* lse_part, const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype,
                        float* lse, void* stream);

@@ -321,7 +321,13 @@ int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_p
   mla::OutUvArgs a{nullptr, w_uv, out, rows, dims->heads, o_part, lse_part, lse, num_splits, dims->q_per_seq,
                    out_dtype == MLA_BF16, part_dtype == MLA_F16};
   hipStream_t s = (hipStream_t)stream;
-  if (w_dtype == MLA_BF16) {
+  if (w_dtype == MLA_BF16 && num_splits > 8 && rows <= mla::kMergeFewRows) {
+    // few query rows, many chunks: the chunks of a row spread over a workgroup
+    const int64_t grid = (int64_t)dims->heads * 2;
+    const void* k = part_dtype == MLA_F16 ? (const void*)mla::merge_out_uv_few<_Float16>
+                                           : (const void*)mla::merge_out_uv_few<float>;
+    st = launch("mla::merge_out_uv_few", k, dim3((unsigned)grid), dim3(256), a, s);
+  } else if (w_dtype == MLA_BF16) {
     // workgroups per head: enough to fill the compute units, at most one per
     // 16-row tile
     const int tiles = (rows + 15) / 16;

@@ -68,6 +68,9 @@ struct OutUvArgs {
 __global__ void out_uv_mfma(const OutUvArgs a);        // bf16 weights, hi/lo split of o_lat
 template <typename PT>  // partial type: float or _Float16
 __global__ void merge_out_uv16(const OutUvArgs a);  // the same with the chunk merge on the way (16-row tiles)
+template <typename PT>
+__global__ void merge_out_uv_few(const OutUvArgs a);  // the same for few query rows and many chunks
+constexpr int kMergeFewRows = 8;  // query rows up to which merge_out_uv_few is used beyond 8 chunks
 template <bool kMerge>
 __global__ void out_uv_f32(const OutUvArgs a);   // fp32 weights
 

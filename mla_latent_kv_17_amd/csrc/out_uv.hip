@@ -312,6 +312,119 @@ __global__ void __launch_bounds__(256) merge_out_uv16(const OutUvArgs a) {
   }
 }
 
+// Merged form, bf16 weights, for few query rows and many chunks (the fused
+// kernel above spreads rows, not chunks, over its threads).  Workgroup =
+// (head, half of d_head); per query row:
+//  * the 256 threads merge the row: thread t takes columns 8 (t % 64) .. +7
+//    of chunks g, g + 4, g + 8, ... (g = t / 64) in rounds of kR chunks,
+//    every load of a round issued before any is used, each chunk group with
+//    its own running maximum (a chunk with lse = -inf takes no part,
+//    whatever its partial holds); the four groups are combined through LDS;
+//  * wave w computes output dims d0 + 16 w .. + 15: lane l holds columns
+//    8 l .. 8 l + 7 of those 16 weight rows in registers for every row, the
+//    products (exact, bf16 x fp32) and sums are fp32, then summed across the
+//    wave.
+template <typename PT>
+__global__ void __launch_bounds__(256) merge_out_uv_few(const OutUvArgs a) {
+  constexpr int kR = sizeof(PT) == 2 ? 16 : 8;  // chunks per round and group
+  __shared__ __attribute__((aligned(16))) float gx[4][512];
+  __shared__ float gm[4], gz[4];
+  __shared__ __attribute__((aligned(16))) float xs[512];
+  const int h = blockIdx.x >> 1, d0 = (blockIdx.x & 1) * 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  u32x4 wr[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    wr[k] = *(const u32x4*)((const uint16_t*)a.w + ((int64_t)h * 128 + d0 + 16 * wave + k) * 512 + 8 * lane);
+  const int ns = a.num_splits;
+  const int64_t rs = (int64_t)a.sq * a.heads, cs = rs * 512;
+  const int g = tid >> 6, c8 = tid & 63;
+  for (int r = 0; r < a.rows; ++r) {
+    const int b = r / a.sq, q = r - b * a.sq;
+    const int64_t pr = (int64_t)b * ns * rs + (int64_t)q * a.heads + h;
+    const float* lp = a.lse_part + pr;
+    const PT* vp = (const PT*)a.o_part + pr * 512 + 8 * c8;
+    float m = -__builtin_inff(), z = 0.f, x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    for (int s0 = g; s0 < ns; s0 += 4 * kR) {
+      float l[kR];
+      Piece8<PT> pv[kR];
+#pragma unroll
+      for (int k = 0; k < kR; ++k) {
+        const int sc = min(s0 + 4 * k, ns - 1);  // past the last chunk: read it again, not counted
+        l[k] = lp[sc * rs];
+        pv[k].load(vp + sc * cs);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any result is used
+#pragma unroll
+      for (int k = 0; k < kR; ++k)
+        if (s0 + 4 * k >= ns) l[k] = -__builtin_inff();
+      float mr = m;
+#pragma unroll
+      for (int k = 0; k < kR; ++k) mr = fmaxf(mr, l[k]);
+      // branch-free: while no chunk holds a token, m and mr are -inf and every weight is 0
+      const float c = m == -__builtin_inff() ? 0.f : expf(m - mr);
+      z *= c;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] *= c;
+#pragma unroll
+      for (int k = 0; k < kR; ++k) {
+        const bool live = l[k] != -__builtin_inff();
+        const float e = live ? expf(l[k] - mr) : 0.f;
+        z += e;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = live ? fmaf(e, pv[k][j], x[j]) : x[j];
+      }
+      m = mr;
+    }
+    __syncthreads();  // xs of the previous row is read
+    if (c8 == 0) {
+      gm[g] = m;
+      gz[g] = z;
+    }
+    *(f32x4*)&gx[g][8 * c8] = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)&gx[g][8 * c8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
+    __syncthreads();
+    {
+      const float mm = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+      float wg[4], zz = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        wg[k] = gm[k] == -__builtin_inff() ? 0.f : expf(gm[k] - mm);
+        zz += wg[k] * gz[k];
+      }
+      const float inv = zz > 0.f ? 1.f / zz : 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int col = tid + 256 * u;
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v = fmaf(wg[k], gx[k][col], v);
+        xs[col] = v * inv;
+      }
+      if (a.lse && tid == 0 && (blockIdx.x & 1) == 0)
+        a.lse[(int64_t)r * a.heads + h] = zz > 0.f ? mm + logf(zz) : -__builtin_inff();
+    }
+    __syncthreads();
+    const f32x4 x0 = *(const f32x4*)&xs[8 * lane], x1 = *(const f32x4*)&xs[8 * lane + 4];
+    float mine = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w2 = wr[k][e];  // columns 8 lane + 2e, + 2e + 1
+        v = fmaf(__uint_as_float(w2 << 16), e < 2 ? x0[2 * e] : x1[2 * e - 4], v);
+        v = fmaf(__uint_as_float(w2 & 0xFFFF0000u), e < 2 ? x0[2 * e + 1] : x1[2 * e - 3], v);
+      }
+      v = wave_sum_rows(v);
+      mine = lane == k ? v : mine;
+    }
+    if (lane < 16) store_out(a.out, ((int64_t)r * a.heads + h) * 128 + d0 + 16 * wave + lane, mine, a.out_bf16);
+  }
+}
+
 // fp32 weights: workgroup = (head, block of 16 output dims d); wave w holds
 // the weight rows d0 + 4w .. d0 + 4w + 3 in registers (lane l: columns
 // 8l .. 8l+7 of each, a row read as 2 KB per wave) and reuses them for every
@@ -416,6 +529,8 @@ __global__ void __launch_bounds__(256) out_uv_f32(const OutUvArgs a) {
   }
 }
 
+template __global__ void merge_out_uv_few<float>(const OutUvArgs);
+template __global__ void merge_out_uv_few<_Float16>(const OutUvArgs);
 template __global__ void merge_out_uv16<float>(const OutUvArgs);
 template __global__ void merge_out_uv16<_Float16>(const OutUvArgs);
 template __global__ void out_uv_f32<false>(const OutUvArgs);

@@ -113,18 +113,24 @@ class DecodeStep:
     def project(self, stream=None):
         mla_out_uv(self.dev.dims, self.o_lat, self.dev.w_uv, self.out, stream)
 
-    # the fused merge of bf16 weights walks the chunks a few at a time per
-    # 16-row tile, so it pays one memory latency per round: with many chunks
-    # and few query rows the separate merge, which spreads rows over
-    # workgroups, is faster.  The fp32 form issues 16 chunks' loads at once
-    # and is fused at every chunk count.
+    # With bf16 weights the fused merge for many query rows walks the chunks
+    # a few at a time per 16-row tile, paying one memory latency per round:
+    # beyond FUSED_MERGE_MAX_SPLITS chunks the separate merge, which spreads
+    # rows over workgroups, is faster, unless there are at most
+    # FUSED_FEW_ROWS query rows (the library then spreads each row's chunks
+    # over a workgroup).  The fp32 form issues 16 chunks' loads at once and
+    # is fused at every chunk count.
     FUSED_MERGE_MAX_SPLITS = 8
+    FUSED_FEW_ROWS = 8
 
     def merge_project(self, stream=None):
-        """out and lse; with 1 < num_splits (at most FUSED_MERGE_MAX_SPLITS for
-        bf16 weights) the merge is fused into the projection
-        (mla_combine_out_uv), otherwise mla_split_combine then mla_out_uv."""
-        if self.num_splits > self.FUSED_MERGE_MAX_SPLITS and self.dev.w_uv.dtype != torch.float32:
+        """out and lse; with 1 < num_splits the merge is fused into the
+        projection (mla_combine_out_uv), except with bf16 weights beyond
+        FUSED_MERGE_MAX_SPLITS chunks and FUSED_FEW_ROWS query rows, where
+        mla_split_combine then mla_out_uv run."""
+        rows = self.dev.batch * self.dev.q_per_seq
+        if (self.num_splits > self.FUSED_MERGE_MAX_SPLITS and self.dev.w_uv.dtype != torch.float32
+                and rows > self.FUSED_FEW_ROWS):
             self.combine(stream)
             self.project(stream)
         elif self.num_splits > 1:

@@ -150,7 +150,12 @@ def test_split_combine(B, ns, Sq, heads, part):
                                                (40, 4, 2, 128, "bf16"), (2, 130, 1, 128, "bf16"),
                                                # fp32 weights: one full round of 16 chunks, and three
                                                # rounds with a partial last one
-                                               (1, 16, 1, 16, "f32"), (2, 40, 2, 16, "f32")])
+                                               (1, 16, 1, 16, "f32"), (2, 40, 2, 16, "f32"),
+                                               # bf16 beyond 8 chunks: at most 8 query rows (chunks spread
+                                               # over the workgroup; the 64- and 130-chunk cases above too),
+                                               # and more rows (16-row tiles, rounds of two chunks)
+                                               (1, 64, 1, 128, "bf16"), (4, 12, 2, 64, "bf16"),
+                                               (3, 9, 1, 16, "bf16"), (5, 20, 2, 128, "bf16")])
 def test_combine_out_uv(B, ns, Sq, heads, wdt, part):
     """The merge fused into the projection against the fp64 merge followed by
     the fp64 projection, and against mla_split_combine + mla_out_uv."""
