@@ -73,7 +73,8 @@ def test_out_uv_bf16_weights(rows):
     check(f"out_uv rows={rows}", out.cpu().numpy(), ref, "f32")
 
 
-@pytest.mark.parametrize("rows,wdt,ns", [(37, "bf16", 1), (5, "f32", 1), (6, "bf16", 3), (3, "f32", 3)])
+@pytest.mark.parametrize("rows,wdt,ns", [(37, "bf16", 1), (5, "f32", 1), (6, "bf16", 3), (3, "f32", 3),
+                                         (2, "bf16", 12), (3, "f32", 20)])
 def test_projection_bf16_output(rows, wdt, ns):
     """A bf16 output is the round-to-nearest-even of the same call's fp32
     output, bit for bit (the sums are the same; only the store differs)."""

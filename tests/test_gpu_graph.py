@@ -9,7 +9,9 @@ import mla_inputs as MI
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,ns", [("bf16_small_split", 7), ("bf16_small_paged", 1), ("fp8_small_sq2", 2)])
+@pytest.mark.parametrize("name,ns", [("bf16_small_split", 7), ("bf16_small_paged", 1), ("fp8_small_sq2", 2),
+                                     # merges fused beyond 8 chunks: one query row (bf16), fp32 weights
+                                     ("bf16_small_split", 12), ("fp32_b1_h16_t1k", 16)])
 def test_graph_replays_match_eager(name, ns):
     import torch
     from mla_latent_kv_17_amd.runner import DecodeStep, DeviceInputs
