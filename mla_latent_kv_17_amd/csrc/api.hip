@@ -335,8 +335,10 @@ int mla_combine_out_uv(const mla_dims* dims, int32_t num_splits, const void* o_p
     a.groups = std::min(tiles, std::max(1, (cus + dims->heads - 1) / dims->heads));
     const int64_t grid = (int64_t)(dims->heads + 7) / 8 * 8 * a.groups;
     if (grid > 0x7fffffff) return MLA_ERR_SHAPE;
-    const void* k = part_dtype == MLA_F16 ? (const void*)mla::merge_out_uv16<_Float16>
-                                           : (const void*)mla::merge_out_uv16<float>;
+    const bool one = num_splits == 1;  // the single chunk: no first-round loads of absent chunks
+    const void* k = part_dtype == MLA_F16
+                        ? (one ? (const void*)mla::merge_out_uv16<_Float16, 1> : (const void*)mla::merge_out_uv16<_Float16, 4>)
+                        : (one ? (const void*)mla::merge_out_uv16<float, 1> : (const void*)mla::merge_out_uv16<float, 4>);
     st = launch("mla::merge_out_uv16", k, dim3((unsigned)grid), dim3(256), a, s);
   } else {
     if (rows > 65535) return MLA_ERR_SHAPE;

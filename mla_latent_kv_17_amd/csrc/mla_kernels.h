@@ -66,7 +66,7 @@ struct OutUvArgs {
   int groups;             // merge_out_uv16: workgroups per head (each takes every groups-th 16-row tile)
 };
 __global__ void out_uv_mfma(const OutUvArgs a);        // bf16 weights, hi/lo split of o_lat
-template <typename PT>  // partial type: float or _Float16
+template <typename PT, int kF>  // partial type: float or _Float16; chunks of the first round: 4, or 1 for one chunk
 __global__ void merge_out_uv16(const OutUvArgs a);  // the same with the chunk merge on the way (16-row tiles)
 template <typename PT>
 __global__ void merge_out_uv_few(const OutUvArgs a);  // the same for few query rows and many chunks

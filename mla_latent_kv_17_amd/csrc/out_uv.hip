@@ -142,12 +142,14 @@ struct Piece8<float> {
 //  * out^T[32 w + 16 db + 0..15][16 rows] with v_mfma_f32_16x16x32_bf16,
 //    A = the weights (registers), B = the merged rows (LDS), hi then lo.
 // More than four chunks take further rounds of two; more than 64 recompute
-// their weights from the row's max and sum.
-template <typename PT>
+// their weights from the row's max and sum.  kF is the number of chunks the
+// first round loads: 4, or 1 for a single chunk (num_splits == 1 only: the
+// rounds after the first assume kF even).
+template <typename PT, int kF>
 __global__ void __launch_bounds__(256) merge_out_uv16(const OutUvArgs a) {
+  static_assert(kF == 4 || kF == 1, "first round of four chunks, or the single chunk");
   const int groups = a.groups;
   constexpr int kW = 64;  // chunk weights held in LDS per round
-  constexpr int kF = 4;   // chunks loaded with the first round
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * 1024];  // merged tile: hi, lo bf16
   __shared__ float wt[16][kW];
   __shared__ float rowm[16], rowinv[16];
@@ -531,8 +533,10 @@ __global__ void __launch_bounds__(256) out_uv_f32(const OutUvArgs a) {
 
 template __global__ void merge_out_uv_few<float>(const OutUvArgs);
 template __global__ void merge_out_uv_few<_Float16>(const OutUvArgs);
-template __global__ void merge_out_uv16<float>(const OutUvArgs);
-template __global__ void merge_out_uv16<_Float16>(const OutUvArgs);
+template __global__ void merge_out_uv16<float, 4>(const OutUvArgs);
+template __global__ void merge_out_uv16<_Float16, 4>(const OutUvArgs);
+template __global__ void merge_out_uv16<float, 1>(const OutUvArgs);
+template __global__ void merge_out_uv16<_Float16, 1>(const OutUvArgs);
 template __global__ void out_uv_f32<false>(const OutUvArgs);
 template __global__ void out_uv_f32<true>(const OutUvArgs);
 

@@ -122,12 +122,18 @@ class DecodeStep:
     # is fused at every chunk count.
     FUSED_MERGE_MAX_SPLITS = 8
     FUSED_FEW_ROWS = 8
+    # one chunk: from this many query rows the merged kernel (one chunk of
+    # weight 1) projects faster than mla_out_uv (256 rows of 128 heads: 33.0
+    # against 37.1 us; 32 rows: 11.8 against 10.7 us)
+    FUSED_ONE_CHUNK_ROWS = 64
 
     def merge_project(self, stream=None):
         """out and lse; with 1 < num_splits the merge is fused into the
         projection (mla_combine_out_uv), except with bf16 weights beyond
         FUSED_MERGE_MAX_SPLITS chunks and FUSED_FEW_ROWS query rows, where
-        mla_split_combine then mla_out_uv run."""
+        mla_split_combine then mla_out_uv run.  With one chunk, mla_out_uv,
+        or from FUSED_ONE_CHUNK_ROWS query rows with bf16 weights
+        mla_combine_out_uv on the single chunk."""
         rows = self.dev.batch * self.dev.q_per_seq
         if (self.num_splits > self.FUSED_MERGE_MAX_SPLITS and self.dev.w_uv.dtype != torch.float32
                 and rows > self.FUSED_FEW_ROWS):
@@ -136,6 +142,11 @@ class DecodeStep:
         elif self.num_splits > 1:
             mla_combine_out_uv(self.dev.dims, self.num_splits, self.o_part, self.lse_part, self.dev.w_uv, self.out,
                                self.lse, stream)
+        elif rows >= self.FUSED_ONE_CHUNK_ROWS and self.dev.w_uv.dtype != torch.float32:
+            # one chunk, many query rows: o_lat and lse as a single chunk's
+            # result (the layouts coincide); the merged kernel projects them
+            # faster than mla_out_uv (lse is already written)
+            mla_combine_out_uv(self.dev.dims, 1, self.o_lat, self.lse, self.dev.w_uv, self.out, None, stream)
         else:
             self.project(stream)
 

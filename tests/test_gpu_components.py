@@ -156,7 +156,9 @@ def test_split_combine(B, ns, Sq, heads, part):
                                                # over the workgroup; the 64- and 130-chunk cases above too),
                                                # and more rows (16-row tiles, rounds of two chunks)
                                                (1, 64, 1, 128, "bf16"), (4, 12, 2, 64, "bf16"),
-                                               (3, 9, 1, 16, "bf16"), (5, 20, 2, 128, "bf16")])
+                                               (3, 9, 1, 16, "bf16"), (5, 20, 2, 128, "bf16"),
+                                               # a single chunk (the one-chunk instance; rows with no token)
+                                               (40, 1, 2, 128, "bf16"), (3, 1, 1, 16, "f32")])
 def test_combine_out_uv(B, ns, Sq, heads, wdt, part):
     """The merge fused into the projection against the fp64 merge followed by
     the fp64 projection, and against mla_split_combine + mla_out_uv."""
