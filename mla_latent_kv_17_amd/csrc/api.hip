@@ -432,7 +432,7 @@ int cache_append_impl(const mla_dims* dims, int32_t d_model, const void* h, cons
     st = launch("mla::append_proj_f32", (const void*)mla::append_proj_f32, dim3(mla::kAppendCols / 4, tokens),
                 dim3(256), a, s);
   } else {
-    const dim3 grid(mla::kAppendCols / 64, chunks, (tokens + 31) / 32);
+    const dim3 grid(mla::kAppendCols / 32, chunks, (tokens + 31) / 32);
     if (grid.z > 65535) return MLA_ERR_SHAPE;
     st = launch("mla::append_proj_mfma", (const void*)mla::append_proj_mfma, grid, dim3(256), a, s);
   }

@@ -11,7 +11,9 @@
 // Two launches:
 //  * append_proj_mfma (bf16 inputs): X = h W^T with W = [W_DKV; W_KR]
 //    (576 x d_model), a [tokens x 576] product over K = d_model, one
-//    workgroup per (64 output columns, 512-wide chunk of d_model, 32 tokens)
+//    workgroup per (32 output columns, 512-wide chunk of d_model, 32 tokens:
+//    180 workgroups at d_model 5120, so the weight stream spreads over most
+//    compute units)
 //    (proj_chunk_bf16: LDS-staged coalesced rows, matrix cores, fp32 chunk
 //    partials into the caller's workspace).  The weights are the traffic
 //    (576 x d_model x 2 bytes) and are read once; the small h is read once
@@ -34,7 +36,7 @@ __global__ void __launch_bounds__(256) append_proj_mfma(const AppendArgs a) {
   auto wrow = [&](int n) __attribute__((always_inline)) -> const uint16_t* {
     return n < 512 ? w_dkv + n * dm : w_kr + (n - 512) * dm;  // W_DKV rows, then W_KR rows
   };
-  proj_chunk_bf16((const uint16_t*)a.h, a.tokens, a.d_model, kAppendCols, wrow, blockIdx.x * 64, blockIdx.y,
+  proj_chunk_bf16<32>((const uint16_t*)a.h, a.tokens, a.d_model, kAppendCols, wrow, blockIdx.x * 32, blockIdx.y,
                   blockIdx.z * 32, a.part, kAppendCols);
 }
 
