@@ -88,23 +88,25 @@ __global__ void __launch_bounds__(256) append_finish(const AppendArgs a) {
   const int64_t blk = a.block_table[(int64_t)b * a.max_blocks + (max(p, 0) >> 6)];
   const int row = p & 63;
   // the chunk sums (they do not depend on the token's position), chunk
-  // order fixed, the loads of eight chunks for all of a thread's columns in
-  // flight at a time with no branch between them
+  // order fixed, the loads of sixteen chunks (d_model up to 8192 in one
+  // round) for all of a thread's columns in flight at a time with no branch
+  // between them
+  constexpr int kRound = 16;
   const int64_t cstride = (int64_t)a.tokens * kAppendCols;
   const float* pp = a.part + (int64_t)r * kAppendCols;
   float sum[3] = {0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < a.chunks; c0 += 8) {
-    float v[3][8];
+  for (int c0 = 0; c0 < a.chunks; c0 += kRound) {
+    float v[3][kRound];
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int n = min(tid + 256 * u, kAppendCols - 1);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[u][k] = pp[min(c0 + k, a.chunks - 1) * cstride + n];
+      for (int k = 0; k < kRound; ++k) v[u][k] = pp[min(c0 + k, a.chunks - 1) * cstride + n];
     }
 #pragma unroll
     for (int u = 0; u < 3; ++u)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sum[u] += c0 + k < a.chunks ? v[u][k] : 0.f;
+      for (int k = 0; k < kRound; ++k) sum[u] += c0 + k < a.chunks ? v[u][k] : 0.f;
   }
 #pragma unroll
   for (int u = 0; u < 3; ++u)
