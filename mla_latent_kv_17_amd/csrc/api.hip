@@ -585,7 +585,7 @@ int mla_moe_gate(int32_t tokens, int32_t d_model, int32_t n_experts, int32_t top
     const void* k = tall[(n_experts + 31) / 32 - 1];
     st = launch("mla::gate_proj_tall", k, grid, dim3(256), a, s);
   } else {
-    const dim3 grid((n_experts + 63) / 64, chunks, (tokens + 31) / 32);
+    const dim3 grid((n_experts + 31) / 32, chunks, (tokens + 31) / 32);  // 32-expert tiles
     st = launch("mla::gate_proj_mfma", (const void*)mla::gate_proj_mfma, grid, dim3(256), a, s);
   }
   if (st) return st;

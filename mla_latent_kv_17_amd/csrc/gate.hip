@@ -11,7 +11,7 @@
 // Two launches:
 //  * the affinities U E^T as fp32 partial sums over slices of d_model in the
 //    caller's workspace, on the matrix cores (exact products, fp32 sums):
-//    - gate_proj_mfma (few tokens): one workgroup per (64 experts, 512-wide
+//    - gate_proj_mfma (few tokens): one workgroup per (32 experts, 512-wide
 //      slice, 32 tokens) through proj_chunk_bf16, so that even one token
 //      tile spreads the centroid read (the traffic) over many CUs;
 //    - gate_proj_tall (many tokens): one workgroup per (128 tokens, slice of
@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256) gate_proj_mfma(const GateArgs a) {
   const uint16_t* e = (const uint16_t*)a.e;
   const int64_t dm = a.d_model;
   auto wrow = [&](int n) __attribute__((always_inline)) -> const uint16_t* { return e + n * dm; };
-  proj_chunk_bf16((const uint16_t*)a.u, a.tokens, a.d_model, a.n_experts, wrow, blockIdx.x * 64, blockIdx.y,
+  proj_chunk_bf16<32>((const uint16_t*)a.u, a.tokens, a.d_model, a.n_experts, wrow, blockIdx.x * 32, blockIdx.y,
                   blockIdx.z * 32, a.part, a.part_stride);
 }
 
