@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(256) append_proj_mfma(const AppendArgs a) {
   auto wrow = [&](int n) __attribute__((always_inline)) -> const uint16_t* {
     return n < 512 ? w_dkv + n * dm : w_kr + (n - 512) * dm;  // W_DKV rows, then W_KR rows
   };
-  proj_chunk_bf16<32>((const uint16_t*)a.h, a.tokens, a.d_model, kAppendCols, wrow, blockIdx.x * 32, blockIdx.y,
+  proj_chunk_bf16((const uint16_t*)a.h, a.tokens, a.d_model, kAppendCols, wrow, blockIdx.x * 32, blockIdx.y,
                   blockIdx.z * 32, a.part, kAppendCols);
 }
 

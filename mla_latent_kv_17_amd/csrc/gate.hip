@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256) gate_proj_mfma(const GateArgs a) {
   const uint16_t* e = (const uint16_t*)a.e;
   const int64_t dm = a.d_model;
   auto wrow = [&](int n) __attribute__((always_inline)) -> const uint16_t* { return e + n * dm; };
-  proj_chunk_bf16<32>((const uint16_t*)a.u, a.tokens, a.d_model, a.n_experts, wrow, blockIdx.x * 32, blockIdx.y,
+  proj_chunk_bf16((const uint16_t*)a.u, a.tokens, a.d_model, a.n_experts, wrow, blockIdx.x * 32, blockIdx.y,
                   blockIdx.z * 32, a.part, a.part_stride);
 }
 

@@ -1,8 +1,9 @@
 // One workgroup's share of a skinny product X = H W^T with bf16 rows of
 // length d_model on both sides (the tokens' hidden states H, a weight W of
 // n_cols rows), used by the cache append and the MoE gate: the fp32 partial
-// sums over one 512-wide chunk of d_model for 32 tokens and kCols (64 or
-// 32) output columns, on the matrix cores (v_mfma_f32_32x32x16_bf16, exact products,
+// sums over one 512-wide chunk of d_model for 32 tokens and 32 output
+// columns (small tiles, so that even one token tile spreads the weight
+// stream over many compute units), on the matrix cores (v_mfma_f32_32x32x16_bf16, exact products,
 // fp32 sums).  The row slices are staged in LDS with fully coalesced loads (a
 // wave's load is 1 KB of one row; the operands' own lane layout would touch
 // 32 rows per load); each of the four waves multiplies a quarter of the
@@ -15,16 +16,16 @@ namespace mla {
 
 constexpr int kProjChunk = 512;
 
-// Workgroup (256 threads) for columns n0 .. n0+kCols-1, chunk `chunk`,
+// Workgroup (256 threads) for columns n0 .. n0+31, chunk `chunk`,
 // tokens m0 .. m0+31.  wrow(n) is W's row n for n < n_cols; columns at or past
 // n_cols, tokens at or past `tokens` and bytes past d_model stage zeros.
 // Writes part[(chunk * tokens + r) * part_stride + n] for the valid r, n.
-template <int kCols = 64, typename WRow>
+template <typename WRow>
 __device__ __forceinline__ void proj_chunk_bf16(const uint16_t* h, int tokens, int d_model, int n_cols, WRow wrow,
                                                 int n0, int chunk, int m0, float* part, int part_stride) {
   constexpr int kPad = 33;          // LDS row stride (floats) of the partial tiles
   constexpr int kRow = 1024 + 16;   // LDS row stride (bytes) of the staged operands
-  static_assert(kCols == 64 || kCols == 32, "64 or 32 output columns");
+  constexpr int kCols = 32;         // output columns per workgroup
   constexpr int kNT = kCols / 32;   // 32-column blocks
   __shared__ __attribute__((aligned(16))) uint8_t ws[kCols * kRow];  // W rows n0 .., this chunk
   __shared__ __attribute__((aligned(16))) uint8_t hs[32 * kRow];  // H rows m0 .. m0+31, this chunk
